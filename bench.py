@@ -1,0 +1,220 @@
+#!/usr/bin/env python
+"""Benchmark: chunkwise GLA forward + backward with ZeCO's segment decomposition on one GPU.
+
+One step = the whole path on one batch: gla_chunk_fwd -> gla_segment_scan -> gla_segment_correct
+(forward), then gla_chunk_bwd -> gla_segment_scan(reverse) -> gla_segment_correct (backward).
+Inputs are drawn once (seeded, synthetic) and stay resident in HBM; every output and intermediate
+buffer is allocated before the timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--gate VARIANT]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GLA fwd+bwd tokens/sec at 16k-token segments on 1 MI355X; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(w, part):
+    """Algorithmic HBM bytes: every input read once, every output written once (element size e
+    for q/k/v/o/do/dq/dk/dv, 4 bytes for g/dg), plus the per-segment float32 states."""
+    e = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    units = w.B * w.H * w.P
+    st = 4 * w.dk * w.dv
+    if part == "fwd":          # q, k, v, g in; o out; segment states out/in/out
+        return th * (e * (2 * w.dk + w.dv) + 4 * w.dk + e * w.dv) + units * st * 3
+    if part == "chunk_bwd":    # q, k, v, g, do in; dq, dk, dv, dg out; seg_in in, D out
+        return th * (e * (2 * w.dk + 2 * w.dv) + 4 * w.dk + e * (2 * w.dk + w.dv) + 4 * w.dk) + units * st * 2
+    if part == "bwd":          # the whole backward: chunk_bwd plus the reverse scan's states
+        return alg_bytes(w, "chunk_bwd") + units * st * 2
+    raise ValueError(part)
+
+
+def alg_flops(w, part):
+    """Algorithmic flops per token-head (the causal half of the intra-chunk products counted)."""
+    th = w.B * w.H * w.T
+    C, dk, dv = w.chunk, w.dk, w.dv
+    fwd = (C + 1) * (dk + dv) + 4 * dk * dv + (2 * dk * dv if w.P > 1 else 0)
+    bwd = (C + 1) * (3 * dk + 2 * dv) + 8 * dk * dv + (4 * dk * dv if w.P > 1 else 0)
+    return th * (fwd if part == "fwd" else bwd)
+
+
+def cpu_baseline(w, gate, budget_s=12.0):
+    """The oracle (plain float64 recurrence, fwd+bwd) on a bounded sample of the workload: head 0,
+    the first n segments, n grown until the run takes about budget_s."""
+    import numpy as np
+    import oracle
+    from sequence_state_scan_amd import inputs
+    from sequence_state_scan_amd.inputs import as_f64
+
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, 0, w.dtype, 0, True, gate)
+    a = {n: as_f64(t) for n, t in h.items()}
+    n, spent, tokens = 1, 0.0, 0
+    while True:
+        t1 = min(n * w.L, w.T)
+        sl = {k: v[:, :, :t1] for k, v in a.items()}
+        t0 = time.perf_counter()
+        oracle.gla_fwd(sl["q"], sl["k"], sl["v"], sl["g"])
+        oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["do"])
+        dt = time.perf_counter() - t0
+        spent, tokens = dt, t1
+        if dt >= budget_s / 4 or t1 >= w.T or n >= 64:
+            break
+        n = max(n + 1, int(n * math.ceil(budget_s / 4 / max(dt, 1e-3))))
+    # tokens of the workload per second: one head of `tokens` tokens is tokens / H workload tokens
+    value = (tokens / (w.B * w.H)) / spent
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "head 0 of %d, first %d tokens (%d segments), fwd+bwd float64 token recurrence, %.2fs; "
+                      "value = tokens/(B*H)/time" % (w.B * w.H, tokens, tokens // w.L, spent)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--gate", default="logsigmoid16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs every segment on a single MI355X and has no "
+              "multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sequence_state_scan_amd import gla, inputs
+
+    w = inputs.WORKLOADS[args.workload or inputs.HEADLINE]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gla.load_library()
+
+    t = time.time()
+    d = inputs.generate_workload(w, gate=args.gate, bwd=True)
+    x = {n: v.to(dev) for n, v in d.items()}
+    del d
+    log("inputs %s drawn and uploaded in %.1fs" % (w.name, time.time() - t))
+
+    B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
+    f32, edt = torch.float32, x["q"].dtype
+    buf = {
+        "o": torch.empty_like(x["v"]),
+        "cs": torch.empty((B, H, T // C, dk, dv), device=dev, dtype=edt),
+        "S_loc": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
+        "ld": torch.empty((B, H, P, dk), device=dev, dtype=f32),
+        "S_in": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
+        "h_fin": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
+        "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+        "dg": torch.empty_like(x["g"]),
+        "D": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
+        "G": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
+        "dh0": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
+    }
+    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
+
+    calls = [
+        ("gla_chunk_fwd", lambda: gla.gla_chunk_fwd(q, k, v, g, C, P, o=buf["o"], chunk_states=buf["cs"],
+                                                     seg_state=buf["S_loc"], seg_logdecay=buf["ld"])),
+        ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
+                                                           h_out=buf["h_fin"])),
+        ("gla_segment_correct(FWD)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, P, q=q, g=g, seg_in=buf["S_in"],
+                                                                      o=buf["o"], chunk_states=buf["cs"])),
+        ("gla_chunk_bwd", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], buf["S_in"], C, P, dq=buf["dq"],
+                                                     dk=buf["dk"], dv=buf["dv"], dg=buf["dg"], seg_dstate=buf["D"])),
+        ("gla_segment_scan(reverse)", lambda: gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True,
+                                                                    seg_carry=buf["G"], h_out=buf["dh0"])),
+        ("gla_segment_correct(BWD)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, P, k=k, v=v, g=g,
+                                                                      seg_in=buf["S_in"], seg_grad=buf["G"],
+                                                                      chunk_states=buf["cs"], dk=buf["dk"],
+                                                                      dv=buf["dv"], dg=buf["dg"])),
+    ]
+
+    stream = torch.cuda.current_stream(dev)  # the stream every call launches on
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        for i, (_, fn) in enumerate(calls):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_call = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+                for i, (name, _) in enumerate(calls)}
+    tokens = B * T
+    value = tokens / (ms_step / 1e3)
+
+    # the dominant call and its roofline (algorithmic bytes of that call / its mean duration)
+    dom = max(per_call, key=per_call.get)
+    if dom == "gla_chunk_bwd":
+        dom_bytes, dom_flops = alg_bytes(w, "chunk_bwd"), alg_flops(w, "bwd")
+    elif dom == "gla_chunk_fwd":
+        dom_bytes, dom_flops = alg_bytes(w, "fwd"), alg_flops(w, "fwd")
+    else:
+        dom_bytes, dom_flops = None, None
+    roof = None
+    if dom_bytes:
+        ach = dom_bytes / (per_call[dom] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "alg_bytes_per_launch": dom_bytes,
+                "mfma_frac": round(dom_flops / (per_call[dom] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    step_bytes = alg_bytes(w, "fwd") + alg_bytes(w, "bwd")
+    step_flops = alg_flops(w, "fwd") + alg_flops(w, "bwd")
+    step_roof = {"alg_bytes": step_bytes, "hbm_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "alg_flops": step_flops,
+                 "mfma_frac": round(step_flops / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.time()
+        cpu = cpu_baseline(w, args.gate)
+        log("cpu baseline in %.1fs" % (time.time() - t))
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C, "P": P, "K": K,
+                   "segment_tokens": w.L, "gate": args.gate},
+        "roofline": roof, "cpu_baseline": cpu,
+        "step_roofline": step_roof,
+        "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * gla.h -- C ABI of libgla.so: chunkwise gated linear attention with a per-key-channel
+ * (diagonal) decay, forward and backward, and ZeCO's segment decomposition, on one
+ * MI355X (gfx950).
+ *
+ * The method (ZeCO, arXiv 2507.01004, as summarised on the atlas.scime.ai and
+ * pith.science pages):
+ *   - a sequence of T tokens is cut into P segments of L = T/P tokens;
+ *   - every segment runs the gated-linear-attention recurrence from a ZERO state and
+ *     produces local outputs and local states (the local pass of the paper's Algorithm 1,
+ *     as the pith.science referee report describes it in major comment 1);
+ *   - a decay-and-add scan over segments, split into K blocks of d_k rows, gives every
+ *     segment its true incoming state: S_in[p+1] = exp(logdecay[p]) * S_in[p] + S_local[p]
+ *     (the All-Scan update, pith.science "What carries the argument");
+ *   - every segment's outputs are corrected with the cumulative decay (the second pass over
+ *     Q, K, V of the same comment), using the linear-decomposition identity
+ *     (pith.science "Assumptions", Appendix A.1);
+ *   - the backward reuses the forward's global incoming states (pith.science
+ *     "Assumptions", Appendix A.4).  How the state gradient crosses segments is not
+ *     written on the pages; this library runs the same decay-and-add scan in reverse.
+ *
+ * The recurrence, per (batch b, head h), tokens t = 0..T-1, state S in R^{dk x dv}:
+ *     S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,   S_{-1} = h0 (zero)
+ * g is the log of the decay ("log-gate"), one value per token and per d_k channel.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers owned by the caller (for example torch tensors).
+ *     The library never allocates, frees or keeps device memory, and never writes inputs.
+ *   - All tensors are contiguous, row-major:
+ *       q, k, dq, dk, g, dg:   [B][H][T][dk]
+ *       v, o, do, dv:          [B][H][T][dv]
+ *       per-segment states:    [B][H][P][dk][dv]      (float32)
+ *       per-chunk states:      [B][H][T/chunk][dk][dv] (dtype)
+ *       seg_logdecay:          [B][H][P][dk]          (float32)
+ *       single states (h0...): [B][H][dk][dv]         (float32)
+ *   - dtype selects the element type of q, k, v, o, do, dq, dk, dv: GLA_BF16 (bfloat16)
+ *     or GLA_F32 (float32).  g, dg and every state are always float32.  bf16 products
+ *     run on MFMA with float32 accumulation; f32 products on the f32 MFMA.
+ *   - g must be <= 0 everywhere (a decay in (0, 1]).  gla_segment_correct relies on it to
+ *     stop a segment's correction once every channel's cumulative decay has underflowed to
+ *     exactly zero in float32.  Inside one chunk the kernels factor exp(b_t - b_s) as
+ *     exp(b_t) * exp(-b_s) with b the in-chunk running sum of g, so each channel's decay
+ *     over one chunk must stay above -87 (exp(87) is near the float32 limit); use a
+ *     smaller chunk for stronger gates.
+ *   - stream is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
+ *     it: no host synchronisation, no device-wide barrier.  The caller orders the calls.
+ *   - Shapes, dtype, pointers and the supported-shape table are all checked on the host
+ *     BEFORE any HIP call; a rejected call enqueues nothing.  A failed launch returns
+ *     GLA_ERR_HIP.  gla_last_error() describes the last failure of the calling thread.
+ *
+ * Supported shapes (gla_supported() answers for a given combination):
+ *   GLA_BF16: chunk in {32, 64}; dk in {32, 64, 128}; dv in {32, 64, 128, 256}
+ *   GLA_F32:  chunk in {16, 32, 64}; dk in {16, 32}; dv in {16, 32}
+ *   always:   B, H, P >= 1; T % P == 0; (T / P) % chunk == 0
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARG = 1, /* bad shape, null pointer, bad enum value */
+  GLA_ERR_UNSUPPORTED = 2, /* valid arguments, but no kernel is built for this shape */
+  GLA_ERR_HIP = 3          /* a HIP launch failed */
+} gla_status;
+
+enum { GLA_F32 = 0, GLA_BF16 = 1 };
+enum { GLA_FWD = 0, GLA_BWD = 1 };
+
+/* Returns 1 if the kernels exist for (dtype, dk, dv, chunk), else 0. */
+int gla_supported(int dtype, int dk, int dv, int chunk);
+
+/* Static description of a status code. */
+const char* gla_status_string(gla_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* gla_last_error(void);
+
+/*
+ * gla_chunk_fwd -- local pass (the first pass of ZeCO's Algorithm 1 as the pith.science referee
+ * report describes it, including the HBM state store it makes, major comment 1; chunkwise
+ * form: intra-chunk decay-masked attention plus the chunk state recurrence, with K/Lambda for
+ * the intra part and K*Gamma for the state update, the two forms minor comment 4 compares).
+ *
+ * For every segment p, starting from a ZERO state, computes
+ *   o[t]                    = local output of token t (its segment's history only), dtype
+ *   chunk_states[b,h,n]     = local state after chunk n (n = 0 .. T/chunk - 1 counts chunks
+ *                             over the whole sequence), dtype, [B][H][T/chunk][dk][dv]
+ *   seg_state[b,h,p]        = the segment's end state from a zero start, float32 [dk][dv]
+ *   seg_logdecay[b,h,p,c]   = sum of g over the segment's tokens, float32
+ * Inputs q, k, v (dtype), g (float32).  chunk is the tile length C of the chunkwise form.
+ * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
+ */
+gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         void* o, void* chunk_states, float* seg_state, float* seg_logdecay,
+                         int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                         void* stream);
+
+/*
+ * gla_segment_scan -- decay-and-add scan over the P segments (All-Scan update,
+ * pith.science "What carries the argument"), on each of K blocks of dk/K state rows
+ * independently (the results do not depend on K, bit for bit).
+ *
+ * reverse == 0 (forward):
+ *   seg_carry[p] = state ENTERING segment p:  seg_carry[0] = h_boundary (h0; NULL = 0),
+ *   seg_carry[p+1] = exp(seg_logdecay[p]) * seg_carry[p] + seg_state[p]   (row-wise)
+ *   h_out (nullable) = exp(seg_logdecay[P-1]) * seg_carry[P-1] + seg_state[P-1] = S_T
+ * reverse == 1 (backward; seg_state holds each segment's local state-gradient D_p):
+ *   seg_carry[p] = gradient w.r.t. the state LEAVING segment p:
+ *   seg_carry[P-1] = h_boundary (dL/dS_T; NULL = 0),
+ *   seg_carry[p-1] = exp(seg_logdecay[p]) * seg_carry[p] + seg_state[p]
+ *   h_out (nullable) = dL/dh0 = exp(seg_logdecay[0]) * seg_carry[0] + seg_state[0]
+ * All float32: seg_state, seg_carry [B][H][P][dk][dv]; seg_logdecay [B][H][P][dk];
+ * h_boundary, h_out [B][H][dk][dv].  seg_carry must not alias seg_state.
+ * Requires 1 <= K <= dk and dk % K == 0.  Any dk, dv >= 1 are accepted.
+ */
+gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay,
+                            const float* h_boundary, float* seg_carry, float* h_out,
+                            int B, int H, int P, int dk, int dv, int K, int reverse,
+                            void* stream);
+
+/*
+ * gla_segment_correct -- cumulative-decay correction of every segment's local results
+ * (ZeCO's second pass over Q, K, V, pith.science referee report, major comment 1; the
+ * atlas.scime.ai summary describes it as correcting local chunk states to global
+ * states with a cumulative decay; the identity is the linear decomposition of "Assumptions").
+ *
+ * mode == GLA_FWD: for t in segment p, with a_t = exp(sum of g from the segment's first
+ *   token through t) and S_in[p] = seg_in[p] (seg_carry of the forward scan):
+ *     o[t]            += (q[t] * a_t) . S_in[p]
+ *     chunk_states[n] += diag(a at the last token of chunk n) S_in[p]     (n in segment p)
+ *   Uses q, g, seg_in; o and chunk_states (dtype) are in/out.  k, v, seg_grad, dk_, dv_, dg
+ *   may be NULL.  Afterwards chunk_states holds the GLOBAL state after every chunk.
+ * mode == GLA_BWD: with G_p = seg_grad[p] (seg_carry of the reverse scan) and r_t = sum of g
+ *   over the tokens after t up to the segment's end:
+ *     dk_[t] += exp(r_t) * (G_p v[t])
+ *     dv_[t] += G_p^T (exp(r_t) * k[t])
+ *     dg[t]  += exp(g[t] + r_t) * rowsum(S_{t-1} * G_p)     (S_{t-1}: global state before t)
+ *   S_{t-1} is rebuilt per chunk from chunk_states (global, after the GLA_FWD correction) and
+ *   seg_in.  Uses k, v, g, seg_in, seg_grad, chunk_states; dk_, dv_ (dtype) and dg (float32)
+ *   are in/out.  q and o may be NULL.
+ */
+gla_status gla_segment_correct(int mode, const void* q, const void* k, const void* v,
+                               const float* g, const float* seg_in, const float* seg_grad,
+                               void* o, void* chunk_states, void* dk_, void* dv_, float* dg,
+                               int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                               void* stream);
+
+/*
+ * gla_chunk_bwd -- backward of every segment given the GLOBAL states (the forward's states are
+ * reused, pith.science "Assumptions", Appendix A.4; Alg. 3 loads the state from HBM and walks
+ * the chunks, minor comment 5).  chunk_states must hold the global state after every chunk
+ * (gla_chunk_fwd followed by gla_segment_correct(GLA_FWD)); seg_in is the forward scan's
+ * seg_carry.  With do the output gradient:
+ *   dq[t]          = S_t do[t] with S_t the GLOBAL state (complete, needs no correction)
+ *   dk_[t], dv_[t] = gradients from segment p's own outputs (state gradient U starting at
+ *                    zero at the segment's end): dk_[t] = U_t v[t], dv_[t] = U_t^T k[t]
+ *   dg[t]          = sum_{t' >= t in segment} (q[t'] dq[t'] - k[t'] dk_[t'])  (float32; formed
+ *                    chunk by chunk with the exact carry rowsum(S * U) at chunk boundaries)
+ *   seg_dstate[b,h,p] = D_p = gradient w.r.t. the state entering segment p from segment p's
+ *                    own outputs, float32 [dk][dv]
+ * q, k, v, do, chunk_states and the outputs dq, dk_, dv_ share dtype.  Outputs are fully
+ * overwritten and must not alias inputs.
+ */
+gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const void* do_, const void* chunk_states, const float* seg_in,
+                         void* dq, void* dk_, void* dv_, float* dg, float* seg_dstate,
+                         int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -70,7 +70,7 @@ def load_library(path: str):
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     i = ctypes.c_int
-    lib.oracle_gla_fwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_gla_fwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, i, i]
     lib.oracle_gla_fwd.restype = None
     lib.oracle_gla_bwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, i]
     lib.oracle_gla_bwd.restype = None
@@ -106,8 +106,9 @@ def _dims(q, v):
 # Token recurrence (C)
 # ----------------------------------------------------------------------------------------------
 
-def gla_fwd(q, k, v, g, h0=None, threads: int = 0):
-    """Token-by-token forward.  Returns (o [B,H,T,dv], hT [B,H,dk,dv]), float64.
+def gla_fwd(q, k, v, g, h0=None, threads: int = 0, states_every: int = 0):
+    """Token-by-token forward.  Returns (o [B,H,T,dv], hT [B,H,dk,dv]), float64, and with
+    states_every = C > 0 also the state after every C tokens, [B,H,T//C,dk,dv].
 
     S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, S_{-1} = h0 (zeros if None).
     """
@@ -116,8 +117,11 @@ def gla_fwd(q, k, v, g, h0=None, threads: int = 0):
     h0 = None if h0 is None else _f64(h0)
     o = np.empty((B, H, T, dv), dtype=np.float64)
     hT = np.empty((B, H, dk, dv), dtype=np.float64)
+    hs = np.empty((B, H, T // states_every, dk, dv), dtype=np.float64) if states_every > 0 else None
     _load().oracle_gla_fwd(B * H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0),
-                           _ptr(o), _ptr(hT), int(threads))
+                           _ptr(o), _ptr(hT), _ptr(hs), int(states_every), int(threads))
+    if hs is not None:
+        return o, hT, hs
     return o, hT
 
 
@@ -195,23 +199,28 @@ def _merge(x):
     return x.reshape(B, H, P * L, *x.shape[4:])
 
 
-def segment_local_fwd(q, k, v, g, P: int, threads: int = 0):
+def segment_local_fwd(q, k, v, g, P: int, threads: int = 0, chunk: int = 0):
     """Local pass: every segment from a zero state.
 
     Returns (o_local [B,H,T,dv], S_local [B,H,P,dk,dv], logdecay [B,H,P,dk]) where S_local is the
     segment's end state when it starts from zero and logdecay is the sum of g over the segment
-    (the log of the cumulative decay the All-Scan update applies).
+    (the log of the cumulative decay the All-Scan update applies).  With chunk = C > 0 it also
+    returns the local state after every C tokens, [B,H,T//C,dk,dv] (the chunk states the local
+    pass stores).
     """
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
     B, H, T, dk, dv = _dims(q, v)
     qs, ks, vs, gs = (_split(x, P) for x in (q, k, v, g))
     L = T // P
     # Treat (B, H, P) as the batch of independent zero-state sequences.
-    o, hT = gla_fwd(qs.reshape(B * H * P, 1, L, dk), ks.reshape(B * H * P, 1, L, dk),
-                    vs.reshape(B * H * P, 1, L, dv), gs.reshape(B * H * P, 1, L, dk), None, threads)
-    o_local = o.reshape(B, H, T, dv)
-    S_local = hT.reshape(B, H, P, dk, dv)
+    res = gla_fwd(qs.reshape(B * H * P, 1, L, dk), ks.reshape(B * H * P, 1, L, dk),
+                  vs.reshape(B * H * P, 1, L, dv), gs.reshape(B * H * P, 1, L, dk), None, threads,
+                  states_every=chunk)
+    o_local = res[0].reshape(B, H, T, dv)
+    S_local = res[1].reshape(B, H, P, dk, dv)
     logdecay = gs.sum(axis=3)
+    if chunk > 0:
+        return o_local, S_local, logdecay, res[2].reshape(B, H, T // chunk, dk, dv)
     return o_local, S_local, logdecay
 
 
@@ -240,12 +249,24 @@ def segment_scan(seg_state, logdecay, h_boundary=None, reverse: bool = False):
     return carry, acc
 
 
-def segment_correct_fwd(o_local, q, g, seg_in, P: int):
-    """o_t = o_local_t + (q_t * a_t) . S_in[p],  a_t = exp(sum of g from the segment start to t)."""
+def segment_correct_fwd(o_local, q, g, seg_in, P: int, chunk_states_local=None, chunk: int = 0):
+    """o_t = o_local_t + (q_t * a_t) . S_in[p],  a_t = exp(sum of g from the segment start to t).
+
+    With the local chunk states (and their chunk length) it also returns the global ones:
+    state after chunk n = local state after chunk n + diag(a at the chunk's last token) S_in[p].
+    """
     o_local, q, g, S_in = _f64(o_local), _f64(q), _f64(g), _f64(seg_in)
     a = np.exp(np.cumsum(_split(g, P), axis=3))  # inclusive, within each segment
-    corr = np.einsum("bhplc,bhpcj->bhplj", _split(q, P) * a, S_in)
-    return o_local + _merge(corr)
+    corr = np.matmul(_split(q, P) * a, S_in)        # [..., L, dk] @ [..., dk, dv]
+    o = o_local + _merge(corr)
+    if chunk_states_local is None:
+        return o
+    B, H, Pn, L, dk = a.shape
+    n_per = L // chunk
+    a_end = a[:, :, :, chunk - 1::chunk, :]  # [B,H,P,n_per,dk]
+    cs = _f64(chunk_states_local).reshape(B, H, Pn, n_per, dk, -1)
+    cs = cs + a_end[..., None] * S_in[:, :, :, None, :, :]
+    return o, cs.reshape(B, H, Pn * n_per, dk, -1)
 
 
 def segment_local_bwd(q, k, v, g, do, seg_in, P: int, threads: int = 0):
@@ -291,8 +312,8 @@ def segment_correct_bwd(k, v, g, dk_local, dv_local, dg_local, seg_in, seg_grad,
     r[:, :, :, :-1, :] = rev_incl[:, :, :, 1:, :]  # sum_{s>t}
     e = np.exp(r)
     ks, vs = _split(k, P), _split(v, P)
-    ddk = e * np.einsum("bhplj,bhpcj->bhplc", vs, G)
-    ddv = np.einsum("bhplc,bhpcj->bhplj", e * ks, G)
+    ddk = e * np.matmul(vs, np.swapaxes(G, -1, -2))  # (G v_t)[c]
+    ddv = np.matmul(e * ks, G)                       # G^T (e_t k_t)
     X_next = np.zeros_like(S_in)
     X_next[:, :, :-1] = S_in[:, :, 1:]
     if h_final is not None:
@@ -308,13 +329,19 @@ def segment_correct_bwd(k, v, g, dk_local, dv_local, dg_local, seg_in, seg_grad,
     }
 
 
-def zeco_fwd(q, k, v, g, P: int, h0=None, threads: int = 0):
-    """Forward through the decomposition: local pass, scan, correction.  Returns a dict."""
-    o_local, S_local, ld = segment_local_fwd(q, k, v, g, P, threads)
+def zeco_fwd(q, k, v, g, P: int, h0=None, threads: int = 0, chunk: int = 0):
+    """Forward through the decomposition: local pass, scan, correction.  Returns a dict; with
+    chunk = C > 0 it holds the local and the corrected (global) state after every C tokens."""
+    res = segment_local_fwd(q, k, v, g, P, threads, chunk)
+    o_local, S_local, ld = res[:3]
     S_in, h_final = segment_scan(S_local, ld, h0, reverse=False)
-    o = segment_correct_fwd(o_local, q, g, S_in, P)
-    return {"o": o, "o_local": o_local, "S_local": S_local, "logdecay": ld, "S_in": S_in,
-            "h_final": h_final}
+    out = {"o_local": o_local, "S_local": S_local, "logdecay": ld, "S_in": S_in, "h_final": h_final}
+    if chunk > 0:
+        out["chunk_states_local"] = res[3]
+        out["o"], out["chunk_states"] = segment_correct_fwd(o_local, q, g, S_in, P, res[3], chunk)
+    else:
+        out["o"] = segment_correct_fwd(o_local, q, g, S_in, P)
+    return out
 
 
 def zeco_bwd(q, k, v, g, do, P: int, S_in, logdecay, h_final=None, dhT=None, threads: int = 0):

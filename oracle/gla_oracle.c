@@ -58,36 +58,56 @@ int oracle_max_threads(void) {
 #endif
 }
 
-/* Forward recurrence.  hT may be NULL. */
+/* Forward recurrence.  hT may be NULL.  If hs is not NULL, the state after tokens
+ * every-1, 2*every-1, ... is stored in hs [BH][T/every][dk][dv].  Work unit: one sequence and a
+ * block of up to JB columns of S (columns never interact); exp(g) is taken once per (t, c) for
+ * the block. */
+#define JB 16
 void oracle_gla_fwd(int BH, int T, int dk, int dv,
                     const double* q, const double* k, const double* v, const double* g,
-                    const double* h0, double* o, double* hT, int nthreads) {
+                    const double* h0, double* o, double* hT, double* hs, int every, int nthreads) {
   set_threads(nthreads);
-  const long n_units = (long)BH * dv; /* one unit = one column j of one sequence */
+  const int nblk = (dv + JB - 1) / JB;
+  const int nrec = (hs && every > 0) ? T / every : 0;
+  const long n_units = (long)BH * nblk;
 #pragma omp parallel
   {
-    double* S = (double*)malloc(sizeof(double) * (size_t)dk); /* column j of S */
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * JB); /* S[c][jj], columns j0.. */
 #pragma omp for schedule(dynamic, 1)
     for (long u = 0; u < n_units; ++u) {
-      const long bh = u / dv;
-      const int j = (int)(u % dv);
+      const long bh = u / nblk;
+      const int j0 = (int)(u % nblk) * JB;
+      const int nj = dv - j0 < JB ? dv - j0 : JB;
       const double* qb = q + bh * (long)T * dk;
       const double* kb = k + bh * (long)T * dk;
       const double* vb = v + bh * (long)T * dv;
       const double* gb = g + bh * (long)T * dk;
       double* ob = o + bh * (long)T * dv;
-      for (int c = 0; c < dk; ++c) S[c] = h0 ? h0[bh * (long)dk * dv + (long)c * dv + j] : 0.0;
+      for (int c = 0; c < dk; ++c)
+        for (int jj = 0; jj < nj; ++jj)
+          S[c * JB + jj] = h0 ? h0[bh * (long)dk * dv + (long)c * dv + j0 + jj] : 0.0;
       for (int t = 0; t < T; ++t) {
-        const double vtj = vb[(long)t * dv + j];
-        double acc = 0.0;
+        double acc[JB];
+        for (int jj = 0; jj < nj; ++jj) acc[jj] = 0.0;
         for (int c = 0; c < dk; ++c) {
-          S[c] = exp(gb[(long)t * dk + c]) * S[c] + kb[(long)t * dk + c] * vtj;
-          acc += qb[(long)t * dk + c] * S[c];
+          const double a = exp(gb[(long)t * dk + c]);
+          const double ktc = kb[(long)t * dk + c];
+          const double qtc = qb[(long)t * dk + c];
+          for (int jj = 0; jj < nj; ++jj) {
+            S[c * JB + jj] = a * S[c * JB + jj] + ktc * vb[(long)t * dv + j0 + jj];
+            acc[jj] += qtc * S[c * JB + jj];
+          }
         }
-        ob[(long)t * dv + j] = acc;
+        for (int jj = 0; jj < nj; ++jj) ob[(long)t * dv + j0 + jj] = acc[jj];
+        if (nrec && (t + 1) % every == 0) {
+          double* hb = hs + (bh * (long)nrec + (t + 1) / every - 1) * dk * dv;
+          for (int c = 0; c < dk; ++c)
+            for (int jj = 0; jj < nj; ++jj) hb[(long)c * dv + j0 + jj] = S[c * JB + jj];
+        }
       }
       if (hT)
-        for (int c = 0; c < dk; ++c) hT[bh * (long)dk * dv + (long)c * dv + j] = S[c];
+        for (int c = 0; c < dk; ++c)
+          for (int jj = 0; jj < nj; ++jj) hT[bh * (long)dk * dv + (long)c * dv + j0 + jj] = S[c * JB + jj];
     }
     free(S);
   }
@@ -104,7 +124,6 @@ void oracle_gla_bwd(int BH, int T, int dk, int dv,
                     int nthreads) {
   set_threads(nthreads);
   const long n_rows = (long)BH * dk;
-  const long n_cols = (long)BH * dv;
   double* dg_const = (double*)calloc((size_t)n_rows, sizeof(double)); /* rowsum(S_{T-1} * dhT) */
 
   /* Sweep 1: rows of S, forward in t.  dq_t[c] = sum_j S_t[c][j] do_t[j]. */
@@ -171,31 +190,46 @@ void oracle_gla_bwd(int BH, int T, int dk, int dv,
     free(U);
   }
 
-  /* Sweep 3: columns of U, reverse in t.  dv_t[j] = sum_c U_t[c][j] k_t[c]. */
-#pragma omp parallel
+  /* Sweep 3: columns of U, reverse in t, in blocks of up to JB columns.
+   * dv_t[j] = sum_c U_t[c][j] k_t[c]. */
   {
-    double* U = (double*)malloc(sizeof(double) * (size_t)dk);
+    const int nblk = (dv + JB - 1) / JB;
+    const long n_units = (long)BH * nblk;
+#pragma omp parallel
+    {
+      double* U = (double*)malloc(sizeof(double) * (size_t)dk * JB);
 #pragma omp for schedule(dynamic, 1)
-    for (long u = 0; u < n_cols; ++u) {
-      const long bh = u / dv;
-      const int j = (int)(u % dv);
-      const double* qb = q + bh * (long)T * dk;
-      const double* kb = k + bh * (long)T * dk;
-      const double* gb = g + bh * (long)T * dk;
-      const double* db = dout + bh * (long)T * dv;
-      for (int c = 0; c < dk; ++c) U[c] = dhT ? dhT[bh * (long)dk * dv + (long)c * dv + j] : 0.0;
-      for (int t = T - 1; t >= 0; --t) {
-        const double dtj = db[(long)t * dv + j];
-        double acc = 0.0;
-        for (int c = 0; c < dk; ++c) {
-          U[c] += qb[(long)t * dk + c] * dtj;
-          acc += U[c] * kb[(long)t * dk + c];
+      for (long u = 0; u < n_units; ++u) {
+        const long bh = u / nblk;
+        const int j0 = (int)(u % nblk) * JB;
+        const int nj = dv - j0 < JB ? dv - j0 : JB;
+        const double* qb = q + bh * (long)T * dk;
+        const double* kb = k + bh * (long)T * dk;
+        const double* gb = g + bh * (long)T * dk;
+        const double* db = dout + bh * (long)T * dv;
+        for (int c = 0; c < dk; ++c)
+          for (int jj = 0; jj < nj; ++jj)
+            U[c * JB + jj] = dhT ? dhT[bh * (long)dk * dv + (long)c * dv + j0 + jj] : 0.0;
+        for (int t = T - 1; t >= 0; --t) {
+          double acc[JB];
+          for (int jj = 0; jj < nj; ++jj) acc[jj] = 0.0;
+          for (int c = 0; c < dk; ++c) {
+            const double qtc = qb[(long)t * dk + c];
+            const double ktc = kb[(long)t * dk + c];
+            for (int jj = 0; jj < nj; ++jj) {
+              U[c * JB + jj] += qtc * db[(long)t * dv + j0 + jj];
+              acc[jj] += U[c * JB + jj] * ktc;
+            }
+          }
+          for (int jj = 0; jj < nj; ++jj) dvv[bh * (long)T * dv + (long)t * dv + j0 + jj] = acc[jj];
+          for (int c = 0; c < dk; ++c) {
+            const double a = exp(gb[(long)t * dk + c]);
+            for (int jj = 0; jj < nj; ++jj) U[c * JB + jj] *= a;
+          }
         }
-        dvv[bh * (long)T * dv + (long)t * dv + j] = acc;
-        for (int c = 0; c < dk; ++c) U[c] *= exp(gb[(long)t * dk + c]);
       }
+      free(U);
     }
-    free(U);
   }
 
   /* dg, closed form: reverse running sum of q*dq - k*dk, plus rowsum(S_{T-1} * dhT). */

@@ -1,0 +1,183 @@
+// C ABI of libgla.so (declared in include/gla.h): host-side argument checks, then kernel
+// launches on the caller's stream.  Every check runs before the first HIP call, so a rejected
+// call enqueues nothing and touches no device.
+#include "gla.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gla_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gla_status fail(gla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gla_status ok() {
+  g_last_error.clear();
+  return GLA_OK;
+}
+
+bool in_list(int v, std::initializer_list<int> l) {
+  for (int x : l)
+    if (x == v) return true;
+  return false;
+}
+
+bool shape_listed(int dtype, int dk, int dv, int chunk) {
+  if (dtype == GLA_BF16)
+    return in_list(chunk, {32, 64}) && in_list(dk, {32, 64, 128}) && in_list(dv, {32, 64, 128, 256});
+  if (dtype == GLA_F32)
+    return in_list(chunk, {16, 32, 64}) && in_list(dk, {16, 32}) && in_list(dv, {16, 32});
+  return false;
+}
+
+struct Kernels {
+  gla::launch_fn fwd, corr_fwd, dqk, dv, corr_dk, corr_dv;
+};
+
+bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
+  if (!shape_listed(dtype, dk, dv, chunk)) return false;
+  k->fwd = gla::lookup_fwd_local(dtype, chunk, dk, dv);
+  k->corr_fwd = gla::lookup_correct_fwd(dtype, chunk, dk, dv);
+  k->dqk = gla::lookup_bwd_dqk(dtype, chunk, dk, dv);
+  k->dv = gla::lookup_bwd_dv(dtype, chunk, dk, dv);
+  k->corr_dk = gla::lookup_correct_bwd_dk(dtype, chunk, dk, dv);
+  k->corr_dv = gla::lookup_correct_bwd_dv(dtype, chunk, dk, dv);
+  return k->fwd && k->corr_fwd && k->dqk && k->dv && k->corr_dk && k->corr_dv;
+}
+
+// Shape checks shared by the chunked entry points.
+gla_status check_shape(const char* fn, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                       Kernels* kern) {
+  if (B < 1 || H < 1 || T < 1 || P < 1 || dk < 1 || dv < 1 || chunk < 1)
+    return fail(GLA_ERR_INVALID_ARG, "%s: B, H, T, dk, dv, chunk and P must be >= 1", fn);
+  if (dtype != GLA_F32 && dtype != GLA_BF16) return fail(GLA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (T % P != 0) return fail(GLA_ERR_INVALID_ARG, "%s: T=%d is not a multiple of P=%d", fn, T, P);
+  if ((T / P) % chunk != 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: segment length %d is not a multiple of chunk=%d", fn, T / P, chunk);
+  const long long units = (long long)B * H * P;
+  if (units * 4 > (1LL << 30)) return fail(GLA_ERR_INVALID_ARG, "%s: B*H*P=%lld is too large", fn, units);
+  if (!find_kernels(dtype, dk, dv, chunk, kern))
+    return fail(GLA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%s dk=%d dv=%d chunk=%d", fn,
+                dtype == GLA_BF16 ? "bf16" : "f32", dk, dv, chunk);
+  return GLA_OK;
+}
+
+gla_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(GLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_supported(int dtype, int dk, int dv, int chunk) {
+  Kernels k;
+  return find_kernels(dtype, dk, dv, chunk, &k) ? 1 : 0;
+}
+
+const char* gla_status_string(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_ERR_INVALID_ARG: return "GLA_ERR_INVALID_ARG";
+    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED";
+    case GLA_ERR_HIP: return "GLA_ERR_HIP";
+  }
+  return "unknown gla_status";
+}
+
+const char* gla_last_error(void) { return g_last_error.c_str(); }
+
+gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g, void* o,
+                         void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
+                         int dk, int dv, int chunk, int P, int dtype, void* stream) {
+  const char* fn = "gla_chunk_fwd";
+  Kernels kern;
+  gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
+  if (st != GLA_OK) return st;
+  if (!q || !k || !v || !g || !o || !chunk_states || !seg_state || !seg_logdecay)
+    return fail(GLA_ERR_INVALID_ARG,
+                "%s: q, k, v, g, o, chunk_states, seg_state and seg_logdecay must be non-null", fn);
+  const void* ins[] = {q, k, v, g};
+  for (const void* p : ins)
+    if (p == o || p == chunk_states) return fail(GLA_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
+  gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B * H, T, dk, dv, P};
+  return launched(fn, kern.fwd(&a, static_cast<hipStream_t>(stream)));
+}
+
+gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
+                            float* seg_carry, float* h_out, int B, int H, int P, int dk, int dv, int K,
+                            int reverse, void* stream) {
+  const char* fn = "gla_segment_scan";
+  if (B < 1 || H < 1 || P < 1 || dk < 1 || dv < 1)
+    return fail(GLA_ERR_INVALID_ARG, "%s: B, H, P, dk and dv must be >= 1", fn);
+  if (K < 1 || K > dk || dk % K != 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: K=%d must divide dk=%d", fn, K, dk);
+  if (reverse != 0 && reverse != 1) return fail(GLA_ERR_INVALID_ARG, "%s: reverse must be 0 or 1", fn);
+  if (!seg_state || !seg_logdecay || !seg_carry)
+    return fail(GLA_ERR_INVALID_ARG, "%s: seg_state, seg_logdecay and seg_carry must be non-null", fn);
+  if (seg_carry == seg_state) return fail(GLA_ERR_INVALID_ARG, "%s: seg_carry must not alias seg_state", fn);
+  const long long blocks = (long long)B * H * K * (((long long)(dk / K) * dv + 255) / 256);
+  if (blocks > 0x7fffffffLL) return fail(GLA_ERR_INVALID_ARG, "%s: problem too large", fn);
+  return launched(fn, gla::launch_segment_scan(seg_state, seg_logdecay, h_boundary, seg_carry, h_out, B * H, P,
+                                               dk, dv, K, reverse, static_cast<hipStream_t>(stream)));
+}
+
+gla_status gla_segment_correct(int mode, const void* q, const void* k, const void* v, const float* g,
+                               const float* seg_in, const float* seg_grad, void* o, void* chunk_states, void* dk_,
+                               void* dv_, float* dg, int B, int H, int T, int dk, int dv, int chunk, int P,
+                               int dtype, void* stream) {
+  const char* fn = "gla_segment_correct";
+  if (mode != GLA_FWD && mode != GLA_BWD) return fail(GLA_ERR_INVALID_ARG, "%s: unknown mode %d", fn, mode);
+  Kernels kern;
+  gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
+  if (st != GLA_OK) return st;
+  gla::CorrArgs a{q, k, v, g, seg_in, seg_grad, o, chunk_states, dk_, dv_, dg, B * H, T, dk, dv, P};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == GLA_FWD) {
+    if (!q || !g || !seg_in || !o || !chunk_states)
+      return fail(GLA_ERR_INVALID_ARG, "%s(GLA_FWD): q, g, seg_in, o and chunk_states must be non-null", fn);
+    return launched(fn, kern.corr_fwd(&a, s));
+  }
+  if (!k || !v || !g || !seg_in || !seg_grad || !chunk_states || !dk_ || !dv_ || !dg)
+    return fail(GLA_ERR_INVALID_ARG,
+                "%s(GLA_BWD): k, v, g, seg_in, seg_grad, chunk_states, dk, dv and dg must be non-null", fn);
+  hipError_t e = kern.corr_dk(&a, s);
+  if (e == hipSuccess) e = kern.corr_dv(&a, s);
+  return launched(fn, e);
+}
+
+gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* do_,
+                         const void* chunk_states, const float* seg_in, void* dq, void* dk_, void* dv_, float* dg,
+                         float* seg_dstate, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                         void* stream) {
+  const char* fn = "gla_chunk_bwd";
+  Kernels kern;
+  gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
+  if (st != GLA_OK) return st;
+  if (!q || !k || !v || !g || !do_ || !chunk_states || !seg_in || !dq || !dk_ || !dv_ || !dg || !seg_dstate)
+    return fail(GLA_ERR_INVALID_ARG, "%s: every pointer argument must be non-null", fn);
+  const void* ins[] = {q, k, v, g, do_, chunk_states, seg_in};
+  for (const void* p : ins)
+    if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate)
+      return fail(GLA_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
+  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate, B * H, T, dk, dv, P};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kern.dqk(&a, s);
+  if (e == hipSuccess) e = kern.dv(&a, s);
+  return launched(fn, e);
+}
+
+}  // extern "C"

@@ -1,0 +1,281 @@
+// Device-side building blocks shared by the GLA kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix products use the 16x16 MFMA family on 64-lane waves.  For a 16x16 output tile the
+// lane l (n16 = l % 16, g4 = l / 16) supplies
+//   A operand: A[m = n16][KPL consecutive k-slots owned by group g4]
+//   B operand: B[k-slots of group g4][n = n16]
+// and receives C[m = 4*g4 + i][n = n16], i = 0..3.  bf16 uses v_mfma_f32_16x16x32_bf16
+// (KPL = 8, 32 k per instruction), f32 uses v_mfma_f32_16x16x4_f32 (KPL = 1, 4 k).
+// Every product here is written as C[m][n] = sum_k X[m][k] * Y[n][k] with X and Y stored
+// k-contiguous ("NT" form), so each lane's fragment is one contiguous LDS read.
+//
+// Which physical k a slot holds only has to agree between A and B, so a state tile kept in
+// accumulator registers (lane holds S[4*g4 + i][n16] of each 16x16 block) can feed the A
+// operand directly: the lane's k-slots are taken as {16*kb + 4*g4 + i}, and the B operand
+// reads the same k from LDS (mma_regX below).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kWaves = 4;
+constexpr int kPad = 8;        // LDS row padding in elements (keeps 16-byte alignment)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <typename E> struct ElemPad { static constexpr int v = kPad; };
+
+// --------------------------------------------------------------------------------------------
+// Element loads and stores (4 or 8 consecutive elements <-> float registers)
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (bf16)x[e];
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  f32x4 r;
+  r[0] = (float)a[0]; r[1] = (float)a[1]; r[2] = (float)a[2]; r[3] = (float)a[3];
+  return r;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ void store4(bf16* p, f32x4 x) {
+  bf16x4 a;
+  a[0] = (bf16)x[0]; a[1] = (bf16)x[1]; a[2] = (bf16)x[2]; a[3] = (bf16)x[3];
+  *reinterpret_cast<bf16x4*>(p) = a;
+}
+
+// 8 rows x 8 columns of a row-major tensor with leading dimension ld -> v[row][col]
+template <typename E>
+__device__ __forceinline__ void load_blk(float (&v)[8][8], const E* p, long ld) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) load8(p + r * ld, v[r]);
+}
+// v[row][col] -> dst rows (row-major, leading dimension ld)
+template <typename E>
+__device__ __forceinline__ void store_blk_rows(E* dst, int ld, const float (&v)[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) store8(dst + r * ld, v[r]);
+}
+// v[row][col] -> dst[col][row] (the transposed block, leading dimension ld)
+template <typename E>
+__device__ __forceinline__ void store_blk_cols(E* dst, int ld, const float (&v)[8][8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float col[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) col[r] = v[r][c];
+    store8(dst + c * ld, col);
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// MFMA
+// --------------------------------------------------------------------------------------------
+template <typename E> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KSTEP = 32, KPL = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static frag ld(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KSTEP = 4, KPL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static frag ld(const float* p) { return *p; }
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// acc[m][n] += sum_{k in [kb, ke)} X[m][k] * Y[n][k] for the 16x16 tile whose X rows start at X
+// and Y rows start at Y (row strides ldx, ldy).  kb, ke multiples of Mma<E>::KSTEP.
+template <typename E>
+__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const E* X, int ldx, const E* Y, int ldy,
+                                        int kb, int ke) {
+  const int l = lane_id();
+  const E* xp = X + (l & 15) * ldx + Mma<E>::KPL * (l >> 4);
+  const E* yp = Y + (l & 15) * ldy + Mma<E>::KPL * (l >> 4);
+#pragma unroll 4
+  for (int kk = kb; kk < ke; kk += Mma<E>::KSTEP) acc = Mma<E>::mma(Mma<E>::ld(xp + kk), Mma<E>::ld(yp + kk), acc);
+  return acc;
+}
+
+// Fragment of an operand Z[m][k] for the 16 rows m0..m0+15 at k-step kk, read from LDS.
+//   TR == false: Z stored k-contiguous, row m at P + m * ld (P points at row m0).
+//   TR == true:  Z stored transposed, ZT[k][m] at P + k * ld + m (P points at column m0).
+// bf16 TR uses ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i % 4) of
+// the 8-byte chunks addressed by lanes 4e + i/4 (e = 0..3).  Lane s of group g4 therefore
+// addresses ZT[kk + 8*g4 + s/4 (+4)][4*(s%4)] and receives Z[m0 + s][kk + 8*g4 + 0..3 (4..7)].
+template <typename E, bool TR>
+__device__ __forceinline__ typename Mma<E>::frag frag_ld(const E* P, int ld, int kk) {
+  const int l = lane_id(), s = l & 15, g4 = l >> 4;
+  if constexpr (sizeof(E) == 2) {
+    if constexpr (!TR) {
+      return *reinterpret_cast<const bf16x8*>(P + s * ld + kk + 8 * g4);
+    } else {
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lbf16x4;
+      const E* p0 = P + (kk + 8 * g4 + (s >> 2)) * ld + 4 * (s & 3);
+      const lbf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) lbf16x4*)(p0));
+      const lbf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) lbf16x4*)(p0 + 4 * ld));
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { r[e] = lo[e]; r[4 + e] = hi[e]; }
+      return r;
+    }
+  } else {
+    if constexpr (!TR) return P[s * ld + kk + g4];
+    else return P[(kk + g4) * ld + s];
+  }
+}
+
+// acc[m][n] += sum_{k in [kb, ke)} X[m][k] Y[n][k]; XTR / YTR select the storage of X and Y
+// as in frag_ld.  kb, ke multiples of Mma<E>::KSTEP.
+template <typename E, bool XTR, bool YTR>
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const E* X, int ldx, const E* Y, int ldy, int kb, int ke) {
+#pragma unroll 4
+  for (int kk = kb; kk < ke; kk += Mma<E>::KSTEP)
+    acc = Mma<E>::mma(frag_ld<E, XTR>(X, ldx, kk), frag_ld<E, YTR>(Y, ldy, kk), acc);
+  return acc;
+}
+
+// acc[m][n] += sum_k X[m][k] * Y[n][k] where X comes from NKB accumulator-layout register tiles:
+// R[kb][i] holds X[m = n16][k = 16*kb + 4*g4 + i].  Yrow points at Y's row n = n16 of this tile
+// (so the lane reads Y[n16][16*kb + 4*g4 + i]).
+template <typename E, int NKB>
+__device__ __forceinline__ f32x4 mma_regX(f32x4 acc, const f32x4 (&R)[NKB], const E* Yrow) {
+  const int g4 = lane_id() >> 4;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int p = 0; p < NKB / 2; ++p) {
+      bf16x8 x, y;
+      const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 4 * g4);
+      const bf16x4 yhi = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 16 + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (bf16)R[2 * p][i];
+        x[4 + i] = (bf16)R[2 * p + 1][i];
+        y[i] = ylo[i];
+        y[4 + i] = yhi[i];
+      }
+      acc = Mma<bf16>::mma(x, y, acc);
+    }
+    if constexpr (NKB % 2 == 1) {
+      bf16x8 x, y;
+      const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 16 * (NKB - 1) + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (bf16)R[NKB - 1][i];
+        x[4 + i] = (bf16)0.f;
+        y[i] = ylo[i];
+        y[4 + i] = (bf16)0.f;
+      }
+      acc = Mma<bf16>::mma(x, y, acc);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = Mma<float>::mma(R[kb][i], Yrow[16 * kb + 4 * g4 + i], acc);
+  }
+  return acc;
+}
+
+// Same as mma_regX, with X given as pieces already in the element type: R[kb] holds
+// X[m = n16][k = 16*kb + 4*g4 + 0..3] (bf16x4 for bf16, f32x4 for float).
+template <typename E> struct Piece4 { typedef f32x4 type; };
+template <> struct Piece4<bf16> { typedef bf16x4 type; };
+
+template <typename E>
+__device__ __forceinline__ typename Piece4<E>::type load_piece(const E* p) {
+  return *reinterpret_cast<const typename Piece4<E>::type*>(p);
+}
+
+template <typename E, int NKB>
+__device__ __forceinline__ f32x4 mma_regX_e(f32x4 acc, const typename Piece4<E>::type (&R)[NKB], const E* Yrow) {
+  const int g4 = lane_id() >> 4;
+  if constexpr (sizeof(E) == 2) {
+    static_assert(NKB % 2 == 0, "bf16 pieces come in pairs");
+#pragma unroll
+    for (int p = 0; p < NKB / 2; ++p) {
+      bf16x8 x, y;
+      const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 4 * g4);
+      const bf16x4 yhi = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 16 + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = R[2 * p][i];
+        x[4 + i] = R[2 * p + 1][i];
+        y[i] = ylo[i];
+        y[4 + i] = yhi[i];
+      }
+      acc = Mma<bf16>::mma(x, y, acc);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = Mma<float>::mma(R[kb][i], Yrow[16 * kb + 4 * g4 + i], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float piece_dot(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+__device__ __forceinline__ float piece_dot(bf16x4 a, f32x4 b) {
+  return (float)a[0] * b[0] + (float)a[1] * b[1] + (float)a[2] * b[2] + (float)a[3] * b[3];
+}
+
+// Sum over the four lanes that share n16 (lanes n16, n16+16, n16+32, n16+48).
+__device__ __forceinline__ float sum_over_g4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// --------------------------------------------------------------------------------------------
+// Workgroup -> (unit, tile) mapping.  The dispatcher deals consecutive workgroup ids to the 8
+// XCDs in turn; this keeps all NT tiles of one unit (they read the same q/k/g chunk) on the
+// same XCD and therefore the same L2.  Grid size: round_up(n_units, 8) * NT.
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ void xcd_map(int bid, int NT, int& unit, int& tile) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  unit = (slot / NT) * 8 + xcd;
+  tile = slot - (slot / NT) * NT;
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int round_up(int a, int b) { return ceil_div(a, b) * b; }
+
+}  // namespace gla

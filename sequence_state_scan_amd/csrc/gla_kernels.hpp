@@ -1,0 +1,93 @@
+// Host-visible declarations shared by the HIP translation units of libgla.so: argument blocks,
+// the launcher table and the list of shapes kernels are built for.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace gla {
+
+struct FwdArgs {  // gla_chunk_fwd
+  const void *q, *k, *v;
+  const float* g;
+  void* o;
+  void* chunk_states;  // [B][H][T/C][dk][dv], element type = dtype
+  float *seg_state, *seg_logdecay;
+  int BH, T, Dk, Dv, P;
+};
+
+struct BwdArgs {  // gla_chunk_bwd
+  const void *q, *k, *v;
+  const float* g;
+  const void* dO;
+  const void* chunk_states;  // global states after every chunk
+  const float* seg_in;
+  void *dq, *dk, *dv;
+  float *dg, *seg_dstate;
+  int BH, T, Dk, Dv, P;
+};
+
+struct CorrArgs {  // gla_segment_correct
+  const void *q, *k, *v;
+  const float *g, *seg_in, *seg_grad;
+  void *o, *chunk_states, *dk, *dv;
+  float* dg;
+  int BH, T, Dk, Dv, P;
+};
+
+typedef hipError_t (*launch_fn)(const void* args, hipStream_t stream);
+
+// Compile-time shape lists.  bf16: the MFMA K step is 32, so every contracted length
+// (chunk, d_k, d_v) is a multiple of 32.  f32 kernels exist for small heads only.
+template <int... Vs> struct IntList {};
+using Bf16Chunks = IntList<32, 64>;
+using Bf16Dk = IntList<32, 64, 128>;
+using Bf16Dv = IntList<32, 64, 128, 256>;
+using Bf16Tiles = IntList<32, 64>;
+using F32Chunks = IntList<16, 32, 64>;
+using F32Dk = IntList<16, 32>;
+using F32Dv = IntList<16, 32>;
+using F32Tiles = IntList<16, 32>;
+
+template <typename F, int... Vs>
+inline bool dispatch_int(int v, IntList<Vs...>, F&& f) {
+  return ((v == Vs ? (f(std::integral_constant<int, Vs>{}), true) : false) || ...);
+}
+
+inline int tile_of(int d) { return d < 64 ? d : 64; }
+
+// Per translation unit lookups; nullptr when no kernel exists for the shape.
+// dtype: 0 = f32, 1 = bf16.
+launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_bwd_dqk(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_bwd_dv(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_correct_bwd_dk(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_correct_bwd_dv(int dtype, int chunk, int dk, int dv);
+
+hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
+                               float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
+                               int reverse, hipStream_t stream);
+
+// Generic lookup over (dtype, chunk, D, tile): Launcher<E, C, D, TILE>::run.
+template <template <typename, int, int, int> class Launcher, class DL16, class DL32>
+inline launch_fn lookup3(int dtype, int chunk, int d, int tile) {
+  launch_fn r = nullptr;
+  if (dtype == 1) {
+    dispatch_int(chunk, Bf16Chunks{}, [&](auto c) {
+      dispatch_int(d, DL16{}, [&](auto dd) {
+        dispatch_int(tile, Bf16Tiles{}, [&](auto t) { r = &Launcher<__bf16, c.value, dd.value, t.value>::run; });
+      });
+    });
+  } else if (dtype == 0) {
+    dispatch_int(chunk, F32Chunks{}, [&](auto c) {
+      dispatch_int(d, DL32{}, [&](auto dd) {
+        dispatch_int(tile, F32Tiles{}, [&](auto t) { r = &Launcher<float, c.value, dd.value, t.value>::run; });
+      });
+    });
+  }
+  return r;
+}
+
+}  // namespace gla

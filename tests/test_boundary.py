@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: libgla.so loads, exports every function include/gla.h declares, and
+rejects bad arguments on the host before any HIP call (so these tests never launch anything).
+"""
+import ctypes
+
+import pytest
+import torch
+
+from sequence_state_scan_amd import gla
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gla.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = gla.declared_functions()
+    assert {"gla_chunk_fwd", "gla_chunk_bwd", "gla_segment_scan", "gla_segment_correct"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.gla_status_string(0) == b"GLA_OK"
+    assert lib.gla_status_string(1) == b"GLA_ERR_INVALID_ARG"
+    assert lib.gla_status_string(2) == b"GLA_ERR_UNSUPPORTED"
+    assert lib.gla_status_string(3) == b"GLA_ERR_HIP"
+
+
+def test_supported_shape_table(lib):
+    for dk, dv, c in [(128, 256, 64), (128, 128, 64), (64, 64, 32), (32, 32, 32), (128, 256, 32)]:
+        assert lib.gla_supported(gla.GLA_BF16, dk, dv, c) == 1, (dk, dv, c)
+    for dk, dv, c in [(16, 16, 16), (32, 32, 64), (16, 32, 32)]:
+        assert lib.gla_supported(gla.GLA_F32, dk, dv, c) == 1, (dk, dv, c)
+    for dt, dk, dv, c in [(gla.GLA_BF16, 48, 64, 64), (gla.GLA_BF16, 128, 256, 16), (gla.GLA_BF16, 256, 256, 64),
+                          (gla.GLA_F32, 128, 128, 64), (gla.GLA_F32, 16, 16, 8), (7, 64, 64, 64)]:
+        assert lib.gla_supported(dt, dk, dv, c) == 0, (dt, dk, dv, c)
+
+
+def _fwd(lib, B=1, H=1, T=256, dk=64, dv=64, chunk=64, P=1, dtype=gla.GLA_BF16, q=FAKE, o=ctypes.c_void_p(0x2000),
+         ss=FAKE):
+    return lib.gla_chunk_fwd(q, FAKE, FAKE, FAKE, o, ctypes.c_void_p(0x4000), ss, FAKE, B, H, T, dk, dv, chunk, P,
+                             dtype, NUL)
+
+
+def test_chunk_fwd_host_checks(lib):
+    E, U = gla.GLA_ERR_INVALID_ARG, gla.GLA_ERR_UNSUPPORTED
+    assert _fwd(lib, T=250, P=4) == E          # T % P != 0
+    assert _fwd(lib, T=256, P=8) == E          # segment 32 not a multiple of chunk 64
+    assert _fwd(lib, B=0) == E
+    assert _fwd(lib, dtype=9) == E
+    assert _fwd(lib, q=NUL) == E               # null input
+    assert _fwd(lib, ss=NUL) == E              # null output
+    assert _fwd(lib, o=FAKE) == E              # o aliases q
+    assert _fwd(lib, dk=48) == U               # valid but no kernel built
+    assert _fwd(lib, chunk=16) == U            # bf16 needs chunk >= 32
+    assert b"multiple" in lib.gla_last_error() or len(lib.gla_last_error()) > 0
+
+
+def test_segment_scan_host_checks(lib):
+    E = gla.GLA_ERR_INVALID_ARG
+    other = ctypes.c_void_p(0x3000)
+    args = lambda K=2, rev=0, carry=other, st=FAKE: (st, FAKE, NUL, carry, NUL, 1, 1, 4, 16, 16, K, rev, NUL)  # noqa
+    assert lib.gla_segment_scan(*args(K=3)) == E      # K does not divide dk
+    assert lib.gla_segment_scan(*args(K=0)) == E
+    assert lib.gla_segment_scan(*args(K=32)) == E     # K > dk
+    assert lib.gla_segment_scan(*args(rev=2)) == E
+    assert lib.gla_segment_scan(*args(carry=NUL)) == E
+    assert lib.gla_segment_scan(*args(carry=FAKE)) == E  # carry aliases state
+
+
+def test_segment_correct_host_checks(lib):
+    E = gla.GLA_ERR_INVALID_ARG
+    def call(mode, q=FAKE, k=FAKE, o=FAKE, dk=FAKE, T=256, P=4):
+        return lib.gla_segment_correct(mode, q, k, FAKE, FAKE, FAKE, FAKE, o, FAKE, dk, FAKE, FAKE,
+                                       1, 1, T, 32, 32, 32, P, gla.GLA_BF16, NUL)
+    assert call(5) == E
+    assert call(gla.GLA_FWD, q=NUL) == E
+    assert call(gla.GLA_FWD, o=NUL) == E
+    assert call(gla.GLA_BWD, k=NUL) == E
+    assert call(gla.GLA_BWD, dk=NUL) == E
+    assert call(gla.GLA_FWD, T=100, P=4) == E
+
+
+def test_chunk_bwd_host_checks(lib):
+    E = gla.GLA_ERR_INVALID_ARG
+    def call(dq=ctypes.c_void_p(0x5000), dg=ctypes.c_void_p(0x6000), P=2):
+        return lib.gla_chunk_bwd(FAKE, ctypes.c_void_p(0x1100), ctypes.c_void_p(0x1200), ctypes.c_void_p(0x1300),
+                                 ctypes.c_void_p(0x1400), ctypes.c_void_p(0x1480), ctypes.c_void_p(0x1500), dq,
+                                 ctypes.c_void_p(0x7000),
+                                 ctypes.c_void_p(0x8000), dg, ctypes.c_void_p(0x9000),
+                                 1, 1, 256, 64, 64, 64, P, gla.GLA_BF16, NUL)
+    assert call(dq=FAKE) == E      # dq aliases q
+    assert call(dg=NUL) == E
+    assert call(P=3) == E
+
+
+def test_binding_has_no_cpu_fallback():
+    q = torch.zeros(1, 1, 64, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gla.gla_chunk_fwd(q, q, q, torch.zeros(1, 1, 64, 32), chunk=32, P=1)

@@ -1,0 +1,241 @@
+"""GPU parity: every entry point of libgla.so, called through the C ABI (ctypes binding), against
+the float64 oracle on the same seeded inputs.
+
+Tolerance (per tensor): max|gpu - oracle| / max|oracle| <= 2e-2 for bf16 inputs, 1e-4 for fp32.
+Intermediates (local outputs and states, segment carries, local gradients) are checked as well
+as the final results, so a wrong step cannot hide behind a later one.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_state_scan_amd import gla, inputs
+from sequence_state_scan_amd.inputs import as_f64
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+FWD_KEYS = ("o_local", "cs_local", "S_local", "logdecay", "S_in", "h_final", "o", "cs")
+BWD_KEYS = ("dq", "dk_local", "dv_local", "dg_local", "D_local", "G", "dh0", "dk", "dv", "dg")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def maxrel(x, r):
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    den = np.max(np.abs(r)) if r.size else 0.0
+    num = np.max(np.abs(x - r)) if r.size else 0.0
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+def dev(d):
+    return {k: v.to("cuda") for k, v in d.items()}
+
+
+def gpu_pipeline(d, chunk, P, K, bwd, h0=None, dhT=None):
+    """Every step through the C ABI, keeping the intermediates.  Returns float64 numpy arrays."""
+    q, k, v, g = d["q"], d["k"], d["v"], d["g"]
+    o, cs, S_loc, ld = gla.gla_chunk_fwd(q, k, v, g, chunk, P)
+    res = {"o_local": o.clone(), "cs_local": cs.clone(), "S_local": S_loc, "logdecay": ld}
+    S_in, h_final = gla.gla_segment_scan(S_loc, ld, K, h_boundary=h0)
+    gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=q, g=g, seg_in=S_in, o=o, chunk_states=cs)
+    res.update(S_in=S_in, h_final=h_final, o=o, cs=cs)
+    if bwd:
+        dq, dk, dv, dg, D = gla.gla_chunk_bwd(q, k, v, g, d["do"], cs, S_in, chunk, P)
+        res.update(dq=dq, dk_local=dk.clone(), dv_local=dv.clone(), dg_local=dg.clone(), D_local=D)
+        G, dh0 = gla.gla_segment_scan(D, ld, K, h_boundary=dhT, reverse=True)
+        gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=S_in, seg_grad=G,
+                                chunk_states=cs, dk=dk, dv=dv, dg=dg)
+        res.update(G=G, dh0=dh0, dk=dk, dv=dv, dg=dg)
+    torch.cuda.synchronize()
+    return {n: as_f64(t) for n, t in res.items()}
+
+
+def oracle_pipeline(d, chunk, P, bwd, h0=None, dhT=None):
+    a = {n: as_f64(t) for n, t in d.items()}
+    z = oracle.zeco_fwd(a["q"], a["k"], a["v"], a["g"], P, h0, chunk=chunk)
+    res = {"o_local": z["o_local"], "cs_local": z["chunk_states_local"], "S_local": z["S_local"],
+           "logdecay": z["logdecay"], "S_in": z["S_in"], "h_final": z["h_final"], "o": z["o"],
+           "cs": z["chunk_states"]}
+    if bwd:
+        b = oracle.zeco_bwd(a["q"], a["k"], a["v"], a["g"], a["do"], P, z["S_in"], z["logdecay"], z["h_final"], dhT)
+        for n in BWD_KEYS:
+            res[n] = b[n]
+    return res
+
+
+def check(gpu, ref, keys, tol, label):
+    errs = {n: maxrel(gpu[n], ref[n]) for n in keys}
+    say(label, " ".join("%s=%.2e" % (n, e) for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, "%s: max relative error above %.0e: %s" % (label, tol, bad)
+
+
+def run_case(B, H, T, dk, dv, chunk, P, K, dtype, bwd, gate="logsigmoid16", seed=0, carry=False):
+    d = inputs.generate(B, H, T, dk, dv, dtype, seed, bwd, gate)
+    h0 = dhT = None
+    if carry:
+        rng = np.random.default_rng(seed + 100)
+        h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+        dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    gpu = gpu_pipeline(dev(d), chunk, P, K, bwd, None if h0 is None else h0.cuda(),
+                       None if dhT is None else dhT.cuda())
+    ref = oracle_pipeline(d, chunk, P, bwd, None if h0 is None else h0.numpy(), None if dhT is None else dhT.numpy())
+    label = "B%d H%d T%d dk%d dv%d C%d P%d K%d %s %s" % (B, H, T, dk, dv, chunk, P, K, dtype, gate)
+    check(gpu, ref, FWD_KEYS + (BWD_KEYS if bwd else ()), TOL[dtype], label)
+    # and the end result against the plain recurrence, without any segmentation
+    a = {n: as_f64(t) for n, t in d.items()}
+    o, hT = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"], None if h0 is None else h0.numpy())
+    plain = {"o": o, "h_final": hT}
+    keys = ("o", "h_final")
+    if bwd:
+        plain.update(oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"], None if h0 is None else h0.numpy(),
+                                    None if dhT is None else dhT.numpy()))
+        keys += ("dq", "dk", "dv", "dg", "dh0")
+    check(gpu, plain, keys, TOL[dtype], label + " vs plain recurrence")
+    return gpu
+
+
+# ------------------------------------------------------------------------------- the workloads
+
+def test_tiny_fp32_workload():
+    w = inputs.WORKLOADS["tiny_fp32_t256_p4"]
+    run_case(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K, w.dtype, bwd=False)
+    # the same shape through the backward as well
+    run_case(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K, w.dtype, bwd=True)
+
+
+@pytest.mark.parametrize("name", ["fwd_b2h4_t16k_p1", "fwd_h4_t32k_p8"])
+def test_forward_workloads(name):
+    w = inputs.WORKLOADS[name]
+    t = time.time()
+    run_case(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K, w.dtype, bwd=False)
+    say("%s: %.1fs" % (name, time.time() - t))
+
+
+def test_fwdbwd_workload_h16():
+    w = inputs.WORKLOADS["fwdbwd_h16_t16k_p4"]
+    t = time.time()
+    gpu = run_case(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K, w.dtype, bwd=True)
+    say("%s: %.1fs" % (w.name, time.time() - t))
+
+
+# ------------------------------------------------------------------------- stress and edge cases
+
+@pytest.mark.parametrize("gate", ["weak", "zero", "strong", "mixed"])
+@pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 64, 128, 32), ("f32", 32, 16, 16)])
+def test_gate_variants_with_boundary_states(gate, dtype, dk, dv, chunk):
+    # B*H = 3 units per segment (not a multiple of the 8-way XCD grouping), h0 and dL/dS_T given
+    run_case(1, 3, 1024, dk, dv, chunk, 4, 2, dtype, bwd=True, gate=gate, seed=5, carry=True)
+
+
+@pytest.mark.parametrize("dtype,dk,dv,chunk,P", [("bf16", 32, 32, 32, 8), ("bf16", 128, 256, 64, 3),
+                                                  ("f32", 16, 32, 32, 5), ("f32", 32, 32, 64, 1)])
+def test_one_chunk_per_segment_and_odd_counts(dtype, dk, dv, chunk, P):
+    run_case(2, 1, chunk * P, dk, dv, chunk, P, 1, dtype, bwd=True, gate="weak", seed=6)
+
+
+def test_chunk_size_invariance():
+    d = dev(inputs.generate(1, 2, 2048, 128, 128, "bf16", 3, True, "weak"))
+    a = gpu_pipeline(d, 32, 4, 4, True)
+    b = gpu_pipeline(d, 64, 4, 4, True)
+    for n in ("o", "dq", "dk", "dv", "dg", "h_final"):
+        assert maxrel(a[n], b[n]) <= TOL["bf16"], n
+
+
+def test_run_to_run_determinism():
+    d = dev(inputs.generate(1, 4, 4096, 128, 256, "bf16", 4, True))
+    a = gpu_pipeline(d, 64, 4, 2, True)
+    b = gpu_pipeline(d, 64, 4, 2, True)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_scan_is_bitwise_independent_of_K():
+    rng = np.random.default_rng(9)
+    B, H, P, dk, dv = 2, 3, 7, 64, 48
+    S = torch.from_numpy(rng.standard_normal((B, H, P, dk, dv)).astype(np.float32)).cuda()
+    ld = torch.from_numpy((-np.abs(rng.standard_normal((B, H, P, dk))) * 0.5).astype(np.float32)).cuda()
+    h = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32)).cuda()
+    for rev in (False, True):
+        outs = [gla.gla_segment_scan(S, ld, K, h_boundary=h, reverse=rev) for K in (1, 2, 4, 8, 16, 64)]
+        torch.cuda.synchronize()
+        for c, o in outs[1:]:
+            assert torch.equal(c, outs[0][0]) and torch.equal(o, outs[0][1])
+        ref_c, ref_h = oracle.segment_scan(as_f64(S), as_f64(ld), as_f64(h), reverse=rev)
+        assert maxrel(as_f64(outs[0][0]), ref_c) < 1e-5
+        assert maxrel(as_f64(outs[0][1]), ref_h) < 1e-5
+
+
+def test_state_carry_across_calls():
+    # running the second half with h0 = the first half's final state equals one call
+    d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 8, False, "weak")
+    full = gla.zeco_forward(*(d[n].cuda() for n in ("q", "k", "v", "g")), 64, 2, 2)
+    first = gla.zeco_forward(*(d[n][:, :, :1024].contiguous().cuda() for n in ("q", "k", "v", "g")), 64, 1, 1)
+    second = gla.zeco_forward(*(d[n][:, :, 1024:].contiguous().cuda() for n in ("q", "k", "v", "g")), 64, 1, 1,
+                              h0=first["h_final"])
+    torch.cuda.synchronize()
+    o = torch.cat([first["o"], second["o"]], dim=2)
+    assert maxrel(as_f64(o), as_f64(full["o"])) <= TOL["bf16"]
+    assert maxrel(as_f64(second["h_final"]), as_f64(full["h_final"])) <= TOL["bf16"]
+
+
+def test_headline_workload_at_full_size():
+    """64 segments of 16384 tokens, 4 heads, fwd+bwd, in the launch configuration the benchmark
+    times.  The oracle runs head 0 in full (forward over all 1M tokens; exact backward over the last
+    two segments, started from the oracle's own state at that point), and the homogeneity identity
+    sum<dq,q> = sum<dk,k> = sum<dv,v> = sum<do,o> is checked on every head."""
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    t = time.time()
+    d = inputs.generate_workload(w)
+    say("generated %s in %.1fs" % (w.name, time.time() - t))
+    x = dev(d)
+    del d
+    f = gla.zeco_forward(x["q"], x["k"], x["v"], x["g"], w.chunk, w.P, w.K)
+    b = gla.zeco_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, w.chunk, w.P, w.K)
+    torch.cuda.synchronize()
+    say("gpu fwd+bwd done")
+    # homogeneity on every (b, h)
+    def dot(a, c):
+        return (a.double() * c.double()).sum(dim=(2, 3))
+    ref = dot(x["do"], f["o"])
+    for xn, dn in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        rel = float(((dot(x[xn], b[dn]) - ref).abs() / ref.abs()).max())
+        say("homogeneity %s: %.2e" % (xn, rel))
+        assert rel <= TOL["bf16"], xn
+    # oracle on head 0
+    h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, 0, w.dtype, 0, True)
+    a = {n: as_f64(t) for n, t in h.items()}
+    L = w.L
+    t62 = (w.P - 2) * L
+    t = time.time()
+    o_head, S62 = oracle.gla_fwd(a["q"][:, :, :t62], a["k"][:, :, :t62], a["v"][:, :, :t62], a["g"][:, :, :t62])
+    o_tail, hT = oracle.gla_fwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:], S62)
+    say("oracle forward over %d tokens: %.1fs" % (w.T, time.time() - t))
+    o_ref = np.concatenate([o_head, o_tail], axis=2)
+    del o_head, o_tail
+    errs = {
+        "o": maxrel(as_f64(f["o"][:1, :1]), o_ref),
+        "h_final": maxrel(as_f64(f["h_final"][:1, :1]), hT),
+        "S_in[62]": maxrel(as_f64(f["seg_in"][:1, :1, w.P - 2]), S62),
+    }
+    del o_ref
+    t = time.time()
+    gb = oracle.gla_bwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:],
+                        a["do"][:, :, t62:], S62)
+    say("oracle backward over the last two segments: %.1fs" % (time.time() - t))
+    for n in ("dq", "dk", "dv", "dg"):
+        errs[n] = maxrel(as_f64(b[n][:1, :1, t62:]), gb[n])
+    errs["G[61]"] = maxrel(as_f64(b["seg_grad"][:1, :1, w.P - 3]), gb["dh0"])
+    say("headline workload, head 0: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad

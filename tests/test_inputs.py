@@ -59,3 +59,18 @@ def test_workloads_are_consistent():
     for w in inputs.WORKLOADS.values():
         assert w.T % w.P == 0 and w.L % w.chunk == 0 and w.dk % w.K == 0, w.name
     assert inputs.HEADLINE in inputs.WORKLOADS
+
+
+def test_bf16_path_equals_torch_cast_of_f32_draw():
+    a = inputs.generate(2, 3, 9000, 16, 32, "bf16", seed=2, bwd=True)
+    b = inputs.generate(2, 3, 9000, 16, 32, "f32", seed=2, bwd=True)
+    for n in ("q", "k", "v", "do"):
+        assert torch.equal(a[n], b[n].to(torch.bfloat16)), n
+    assert torch.equal(a["g"], b["g"])
+
+
+def test_head_slice_regenerates_alone():
+    full = inputs.generate(2, 3, 9000, 16, 16, "bf16", seed=7, bwd=True)
+    one = inputs.generate_head(2, 3, 9000, 16, 16, 1, 2, "bf16", seed=7, bwd=True)
+    for n in full:
+        assert torch.equal(full[n][1:2, 2:3], one[n]), n

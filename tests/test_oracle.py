@@ -264,3 +264,19 @@ def test_scan_rows_are_independent():
     full, _ = oracle.segment_scan(S, ld, None)
     part, _ = oracle.segment_scan(S[:, :, :, 2:6], ld[:, :, :, 2:6], None)
     assert np.array_equal(full[:, :, :, 2:6], part)
+
+
+@pytest.mark.parametrize("P,C", [(1, 4), (2, 8), (4, 4)])
+def test_chunk_states_local_and_corrected(P, C):
+    # the recorded states are the plain recurrence's state after every C tokens (prefix runs),
+    # locally per segment and, after the correction step, globally
+    c = _case(1, 2, 32, 4, 3, seed=50 + P, gscale=0.05, with_h0=True)
+    z = oracle.zeco_fwd(c["q"], c["k"], c["v"], c["g"], P, c["h0"], chunk=C)
+    L = 32 // P
+    for n in range(32 // C):
+        t1 = (n + 1) * C
+        _, ref = oracle.gla_fwd(c["q"][:, :, :t1], c["k"][:, :, :t1], c["v"][:, :, :t1], c["g"][:, :, :t1], c["h0"])
+        assert _rel(z["chunk_states"][:, :, n], ref) < 1e-12
+        p0 = (t1 - 1) // L * L  # first token of this chunk's segment
+        _, loc = oracle.gla_fwd(c["q"][:, :, p0:t1], c["k"][:, :, p0:t1], c["v"][:, :, p0:t1], c["g"][:, :, p0:t1])
+        assert _rel(z["chunk_states_local"][:, :, n], loc) < 1e-12

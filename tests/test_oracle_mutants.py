@@ -19,22 +19,24 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gla_oracle.c")
 
 FWD_MUTANTS = {
     "gate_applied_after_adding_kv": (
-        "S[c] = exp(gb[(long)t * dk + c]) * S[c] + kb[(long)t * dk + c] * vtj;",
-        "S[c] = exp(gb[(long)t * dk + c]) * (S[c] + kb[(long)t * dk + c] * vtj);"),
+        "S[c * JB + jj] = a * S[c * JB + jj] + ktc * vb[(long)t * dv + j0 + jj];",
+        "S[c * JB + jj] = a * (S[c * JB + jj] + ktc * vb[(long)t * dv + j0 + jj]);"),
     "output_reads_state_before_update": (
-        "          S[c] = exp(gb[(long)t * dk + c]) * S[c] + kb[(long)t * dk + c] * vtj;\n"
-        "          acc += qb[(long)t * dk + c] * S[c];",
-        "          acc += qb[(long)t * dk + c] * S[c];\n"
-        "          S[c] = exp(gb[(long)t * dk + c]) * S[c] + kb[(long)t * dk + c] * vtj;"),
+        "            S[c * JB + jj] = a * S[c * JB + jj] + ktc * vb[(long)t * dv + j0 + jj];\n"
+        "            acc[jj] += qtc * S[c * JB + jj];",
+        "            acc[jj] += qtc * S[c * JB + jj];\n"
+        "            S[c * JB + jj] = a * S[c * JB + jj] + ktc * vb[(long)t * dv + j0 + jj];"),
     "gate_sign_flipped": (
-        "S[c] = exp(gb[(long)t * dk + c]) * S[c]",
-        "S[c] = exp(-gb[(long)t * dk + c]) * S[c]"),
+        "          const double a = exp(gb[(long)t * dk + c]);\n          const double ktc",
+        "          const double a = exp(-gb[(long)t * dk + c]);\n          const double ktc"),
     "initial_state_dropped": (
-        "for (int c = 0; c < dk; ++c) S[c] = h0 ? h0[bh * (long)dk * dv + (long)c * dv + j] : 0.0;",
-        "for (int c = 0; c < dk; ++c) S[c] = 0.0;"),
+        "S[c * JB + jj] = h0 ? h0[bh * (long)dk * dv + (long)c * dv + j0 + jj] : 0.0;",
+        "S[c * JB + jj] = 0.0;"),
     "query_of_previous_token": (
-        "acc += qb[(long)t * dk + c] * S[c];",
-        "acc += qb[(long)(t > 0 ? t - 1 : 0) * dk + c] * S[c];"),
+        "          const double qtc = qb[(long)t * dk + c];\n          for (int jj = 0; jj < nj; ++jj) {\n"
+        "            S[c * JB",
+        "          const double qtc = qb[(long)(t > 0 ? t - 1 : 0) * dk + c];\n"
+        "          for (int jj = 0; jj < nj; ++jj) {\n            S[c * JB"),
 }
 
 BWD_MUTANTS = {
@@ -48,8 +50,8 @@ BWD_MUTANTS = {
         "          U[j] = exp(gb[(long)t * dk + c]) * U[j] + qtc * db[(long)t * dv + j];\n"
         "          acc += U[j] * vb[(long)t * dv + j];"),
     "dv_query_term_sign": (
-        "U[c] += qb[(long)t * dk + c] * dtj;",
-        "U[c] -= qb[(long)t * dk + c] * dtj;"),
+        "U[c * JB + jj] += qtc * db[(long)t * dv + j0 + jj];",
+        "U[c * JB + jj] -= qtc * db[(long)t * dv + j0 + jj];"),
     "dg_final_state_term_dropped": (
         "double run = dg_const[u];",
         "double run = 0.0 * dg_const[u];"),
