@@ -29,7 +29,14 @@ constexpr int kWaves = 4;
 constexpr int kPad = 8;        // LDS row padding in elements (keeps 16-byte alignment)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// threadIdx.x hidden from loop-invariant code motion: the per-lane addresses a long loop body
+// derives from it are then recomputed where they are used, not held (or spilled) across the loop.
+__device__ __forceinline__ int fresh_tid() {
+  int x = threadIdx.x;
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 template <typename E> struct ElemPad { static constexpr int v = kPad; };
 
@@ -263,6 +270,120 @@ __device__ __forceinline__ float sum_over_g4(float x) {
   x += __shfl_xor(x, 32);
   return x;
 }
+
+// --------------------------------------------------------------------------------------------
+// 4x4 transpose inside each quad of lanes (lanes 4m..4m+3), with DPP quad permutes.  On entry
+// lane 4m+r holds column r of a 4x4 block (x[i] = M[i][r]); on exit it holds row r
+// (x[c] = M[r][c]).  Used to turn an accumulator tile (4 consecutive rows per lane) into
+// 4 consecutive columns per lane for 8-byte stores.
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ float dpp_quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+  const int r = lane_id() & 3;
+  const bool hi2 = r & 2, hi1 = r & 1;
+  // exchange the off-diagonal 2x2 blocks with lane r^2
+  float s0 = hi2 ? x[0] : x[2], s1 = hi2 ? x[1] : x[3];
+  float r0 = dpp_quad_xor2(s0), r1 = dpp_quad_xor2(s1);
+  if (hi2) { x[0] = r0; x[1] = r1; } else { x[2] = r0; x[3] = r1; }
+  // exchange inside each 2x2 block with lane r^1
+  s0 = hi1 ? x[0] : x[1];
+  s1 = hi1 ? x[2] : x[3];
+  r0 = dpp_quad_xor1(s0);
+  r1 = dpp_quad_xor1(s1);
+  if (hi1) { x[0] = r0; x[2] = r1; } else { x[1] = r0; x[3] = r1; }
+  return x;
+}
+
+// --------------------------------------------------------------------------------------------
+// Segmented scans across lanes: segments of W consecutive lanes (W a power of two dividing 64).
+// --------------------------------------------------------------------------------------------
+// Inclusive prefix sum of x over the lanes of the segment (lane order).
+template <int W>
+__device__ __forceinline__ float seg_scan_incl(float x) {
+  const int i = lane_id() & (W - 1);
+#pragma unroll
+  for (int d = 1; d < W; d <<= 1) {
+    const float y = __shfl_up(x, d, W);
+    if (i >= d) x += y;
+  }
+  return x;
+}
+// Inclusive suffix sum of x over the lanes of the segment (from the segment's last lane down).
+template <int W>
+__device__ __forceinline__ float seg_scan_rev_incl(float x) {
+  const int i = lane_id() & (W - 1);
+#pragma unroll
+  for (int d = 1; d < W; d <<= 1) {
+    const float y = __shfl_down(x, d, W);
+    if (i + d < W) x += y;
+  }
+  return x;
+}
+// Value of x at the next lane of the segment (0 on the segment's last lane).
+template <int W>
+__device__ __forceinline__ float seg_next(float x) {
+  const float y = __shfl_down(x, 1, W);
+  return ((lane_id() & (W - 1)) != W - 1) ? y : 0.f;
+}
+// Value of x at the segment's last lane, on every lane of the segment.
+template <int W>
+__device__ __forceinline__ float seg_last(float x) { return __shfl(x, W - 1, W); }
+// Value of x at the previous lane of the segment (0 on the segment's first lane).
+template <int W>
+__device__ __forceinline__ float seg_prev(float x) {
+  const float y = __shfl_up(x, 1, W);
+  return (lane_id() & (W - 1)) ? y : 0.f;
+}
+
+// Raw 4-row x 8-column tile piece of a row-major tensor, held in registers for prefetching.
+template <typename E> struct Rows4x8;
+template <> struct Rows4x8<bf16> {
+  bf16x8 r[4];
+  __device__ __forceinline__ void load(const bf16* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const bf16x8*>(p + i * ld);
+  }
+  __device__ __forceinline__ float at(int i, int e) const { return (float)r[i][e]; }
+};
+template <> struct Rows4x8<float> {
+  float4 r[4][2];
+  __device__ __forceinline__ void load(const float* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i][0] = *reinterpret_cast<const float4*>(p + i * ld);
+      r[i][1] = *reinterpret_cast<const float4*>(p + i * ld + 4);
+    }
+  }
+  __device__ __forceinline__ float at(int i, int e) const {
+    const float4 v = r[i][e >> 2];
+    const int k = e & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+
+// 8 consecutive elements (16 bytes for bf16, 32 for float) copied global -> registers -> LDS.
+template <typename E> struct Vec8;
+template <> struct Vec8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+};
+template <> struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<float4*>(p) = a;
+    *reinterpret_cast<float4*>(p + 4) = b;
+  }
+};
 
 // --------------------------------------------------------------------------------------------
 // Workgroup -> (unit, tile) mapping.  The dispatcher deals consecutive workgroup ids to the 8

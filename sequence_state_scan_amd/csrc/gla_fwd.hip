@@ -16,31 +16,35 @@
 
 namespace gla {
 
-// One workgroup = one (batch*head, segment) unit and one DVT-wide slice of d_v.  The state
-// slice S[:, slice] (float32) lives in accumulator registers for the whole segment: wave w owns
-// the 16-column blocks jb = w, w+4, ...  After every chunk the state is also written out
-// (chunk_states, element type E): the local chunk states the correction turns into global
-// ones and the backward reads.
-template <typename E, int C, int DK, int DVT>
-__global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_units) {
-  constexpr int NTB = C / 8, NCB8 = DK / 8, NQB = NTB * NCB8, NVB = NTB * (DVT / 8);
-  constexpr int LDQ = DK + kPad, LDV = DVT + kPad, LDT = C + kPad;
-  constexpr int NJB = DVT / 16, NKB = DK / 16, NTT = C / 16;
-  constexpr int JPW = ceil_div(NJB, kWaves);
+// One workgroup of NW waves = one (batch*head, segment) unit, all of d_v.  The state S (float32,
+// dk x dv) lives in accumulator registers for the whole segment: wave w owns the 16-column
+// blocks jb = w, w+NW, ...  After every chunk the state is also written out (chunk_states,
+// element type E): the local chunk states the correction turns into global ones and the
+// backward reads.
+//
+// Per chunk: (1) the gate's running sum is taken with a shuffle scan across the lanes that hold
+// one 8-channel column (4 tokens per lane), q/k are scaled and every tile is staged in LDS, and
+// the next chunk's q, k, g, v are requested into registers; (2) the intra-chunk scores;
+// (3) outputs and the state update on MFMA.  The requests of (1) are in flight during (2)-(3).
+template <typename E, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_units) {
+  constexpr int NT = NW * 64;
+  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG, RT = NT / 2;
+  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
+  constexpr int LDQ = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
+  constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
+  constexpr int JPW = ceil_div(NJB, NW);
   constexpr int KS = Mma<E>::KSTEP;
-  static_assert(NQB <= 128, "one 8x8 block of q and one of k per loader thread");
+  static_assert(NI <= RT, "one 4x8 item of q (and one of k) per loader thread");
 
   __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
   __shared__ __attribute__((aligned(16))) E sK[C * LDQ];   // Kbar [s][c]
   __shared__ __attribute__((aligned(16))) E sKt[C * LDQ];  // Ktil [s][c]
   __shared__ __attribute__((aligned(16))) E sV[C * LDV];   // V    [s][j]
   __shared__ __attribute__((aligned(16))) E sA[C * LDT];   // A    [t][s], masked
-  __shared__ float sGtot[NTB * DK];                        // per 8-token block gate sums
   __shared__ float sLamE[DK];                              // exp(lam) per channel
 
-  const int NT = a.Dv / DVT;
-  int unit, tile;
-  xcd_map(blockIdx.x, NT, unit, tile);
+  const int unit = blockIdx.x;
   if (unit >= n_units) return;
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
@@ -48,19 +52,34 @@ __global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_un
   const float* __restrict__ g = a.g;
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
-  const int Dv = a.Dv;
   const int L = a.T / a.P;
   const int nchunks = L / C;
   const int bh = unit / a.P, p = unit - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;  // index of this segment's first chunk state
-  const int j0 = tile * DVT;
+  const long chunk0 = (long)unit * nchunks;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool krole = tid >= 128;
-  const int bi = krole ? tid - 128 : tid;
-  const bool has_blk = bi < NQB;
-  const int tb = bi / NCB8, cb = bi - (bi / NCB8) * NCB8;
+  const bool krole = tid >= RT;
+  const int rt = krole ? tid - RT : tid;
+  const bool has_item = rt < NI;
+  const int tg = rt % NTG, cg = rt / NTG;
+  const E* __restrict__ xsrc = krole ? k : q;
+
+  Rows4x8<float> pg;
+  Rows4x8<E> px;
+  Vec8<E> pv[VPT];
+  auto prefetch = [&](int n) {
+    const long t0 = tok0 + (long)n * C;
+    if (has_item) {
+      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
+      px.load(xsrc + (t0 + tg * 4) * DK + cg * 8, DK);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pv[i].load(v + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+    }
+  };
 
   f32x4 S[JPW][NKB];
 #pragma unroll
@@ -71,74 +90,70 @@ __global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_un
 #pragma unroll
   for (int e = 0; e < 8; ++e) ldsum[e] = 0.f;
 
+  prefetch(0);
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
-    // ---- stage the chunk: gate prefix sums, scaled q/k, V ----
-    float gv[8][8], xv[8][8];
-    if (has_blk) {
-      load_blk<float>(gv, g + (t0 + tb * 8) * DK + cb * 8, DK);
-      load_blk<E>(xv, (krole ? k : q) + (t0 + tb * 8) * DK + cb * 8, DK);
+    // ---- (1) gate prefix sums, scaled q / k, V -> LDS; request the next chunk ----
+    {
+      float b[4][8], lam[8];
 #pragma unroll
-      for (int r = 1; r < 8; ++r)
+      for (int e = 0; e < 8; ++e) {
+        float run = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gv[r][e] += gv[r - 1][e];
-      if (!krole)
+        for (int r = 0; r < 4; ++r) {
+          run += has_item ? pg.at(r, e) : 0.f;
+          b[r][e] = run;
+        }
+        const float incl = seg_scan_incl<NTG>(run);
+        const float excl = seg_prev<NTG>(incl);
+        lam[e] = seg_last<NTG>(incl);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sGtot[tb * DK + cb * 8 + e] = gv[7][e];
-    }
-    for (int vb = tid; vb < NVB; vb += kThreads) {
-      const int vtb = vb / (DVT / 8), vjb = vb - (vb / (DVT / 8)) * (DVT / 8);
-      float vv[8][8];
-      load_blk<E>(vv, v + (t0 + vtb * 8) * Dv + j0 + vjb * 8, Dv);
-      store_blk_rows<E>(sV + (vtb * 8) * LDV + vjb * 8, LDV, vv);
-    }
-    __syncthreads();
-    if (has_blk) {
-      float pre[8], tot[8];
+        for (int r = 0; r < 4; ++r) b[r][e] += excl;
+      }
+      if (has_item) {
+        if (!krole) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { pre[e] = 0.f; tot[e] = 0.f; }
-      for (int u = 0; u < NTB; ++u) {
+          for (int r = 0; r < 4; ++r) {
+            float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = sGtot[u * DK + cb * 8 + e];
-          if (u < tb) pre[e] += s;
-          tot[e] += s;
+            for (int e = 0; e < 8; ++e) x[e] = px.at(r, e) * __expf(b[r][e]);
+            store8(sQ + (tg * 4 + r) * LDQ + cg * 8, x);
+          }
+          if (tg == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              sLamE[cg * 8 + e] = __expf(lam[e]);
+              ldsum[e] += lam[e];
+            }
+          }
+        } else {
+          float el[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float xb[8], xt[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              xb[e] = px.at(r, e) * __expf(-b[r][e]);
+              xt[e] = xb[e] * el[e];
+            }
+            store8(sK + (tg * 4 + r) * LDQ + cg * 8, xb);
+            store8(sKt + (tg * 4 + r) * LDQ + cg * 8, xt);
+          }
         }
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[r][e] += pre[e];  // gv = b (in-chunk inclusive running sum)
-      if (!krole) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xv[r][e] *= __expf(gv[r][e]);
-        store_blk_rows<E>(sQ + (tb * 8) * LDQ + cb * 8, LDQ, xv);
-        if (tb == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            sLamE[cb * 8 + e] = __expf(tot[e]);
-            ldsum[e] += tot[e];
-          }
-        }
-      } else {
-        float kt[8][8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float kk = xv[r][e];
-            kt[r][e] = kk * __expf(tot[e] - gv[r][e]);
-            xv[r][e] = kk * __expf(-gv[r][e]);
-          }
-        store_blk_rows<E>(sK + (tb * 8) * LDQ + cb * 8, LDQ, xv);
-        store_blk_rows<E>(sKt + (tb * 8) * LDQ + cb * 8, LDQ, kt);
+      for (int i = 0; i < VPT; ++i) {
+        const int pc = tid + NT * i;
+        if (NVP % NT == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next chunk's loads after this chunk's staging
+    if (n + 1 < nchunks) prefetch(n + 1);
     __syncthreads();
-    // ---- intra-chunk scores: A^T[s][t] = Kbar[s] . Qbar[t], kept for s <= t, stored as A[t][s] ----
-    for (int idx = w; idx < NTT * NTT; idx += kWaves) {
+    // ---- (2) intra-chunk scores: A^T[s][t] = Kbar[s] . Qbar[t], kept for s <= t, stored as A[t][s] ----
+    for (int idx = w; idx < NTT * NTT; idx += NW) {
       const int sT = idx / NTT, tT = idx - (idx / NTT) * NTT;
       f32x4 acc = zero4();
       if (sT <= tT) acc = mma<E, false, false>(acc, sK + sT * 16 * LDQ, LDQ, sQ + tT * 16 * LDQ, LDQ, 0, DK);
@@ -149,11 +164,11 @@ __global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_un
       store4(sA + t * LDT + sT * 16 + 4 * g4, acc);
     }
     __syncthreads();
-    // ---- outputs O^T[j][t] = V^T A^T + S_prev^T Qbar^T, then the state update ----
-    E* cs = cst + (chunk0 + n) * (long)DK * Dv;
+    // ---- (3) outputs O^T[j][t] = V^T A^T + S_prev^T Qbar^T, then the state update ----
+    E* cs = cst + (chunk0 + n) * (long)DK * DV;
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * kWaves;
+      const int jb = w + jj * NW;
       if (jb < NJB) {
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
@@ -161,15 +176,15 @@ __global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_un
           const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
           acc = mma<E, true, false>(acc, sV + jb * 16, LDV, sA + tT * 16 * LDT, LDT, 0, ke);
           acc = mma_regX<E, NKB>(acc, S[jj], sQ + (tT * 16 + n16) * LDQ);
-          store4(o + (t0 + tT * 16 + n16) * Dv + j0 + jb * 16 + 4 * g4, acc);
+          store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) S[jj][kb][i] *= sLamE[kb * 16 + 4 * g4 + i];
           S[jj][kb] = mma<E, true, true>(S[jj][kb], sKt + kb * 16, LDQ, sV + jb * 16, LDV, 0, C);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) cs[(long)(kb * 16 + 4 * g4 + i) * Dv + j0 + jb * 16 + n16] = (E)S[jj][kb][i];
+          // lane (n16 = 4m + r) stores row 16kb + 4g4 + r, columns 16jb + 4m .. +3
+          store4(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
         }
       }
     }
@@ -177,19 +192,18 @@ __global__ __launch_bounds__(kThreads) void fwd_local_kernel(FwdArgs a, int n_un
   }
 
   // ---- segment results: local end state (float32) and log cumulative decay ----
-  float* st = a.seg_state + (long)unit * DK * Dv;
+  float* st = a.seg_state + (long)unit * DK * DV;
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w + jj * kWaves;
+    const int jb = w + jj * NW;
     if (jb < NJB)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[(long)(kb * 16 + 4 * g4 + i) * Dv + j0 + jb * 16 + n16] = S[jj][kb][i];
+        store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
   }
-  if (tile == 0 && !krole && has_blk && tb == 0) {
+  if (!krole && has_item && tg == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a.seg_logdecay[(long)unit * DK + cb * 8 + e] = ldsum[e];
+    for (int e = 0; e < 8; ++e) a.seg_logdecay[(long)unit * DK + cg * 8 + e] = ldsum[e];
   }
 }
 
@@ -319,13 +333,12 @@ __global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n
   }
 }
 
-template <typename E, int C, int DK, int DVT>
+template <typename E, int C, int DK, int DV>
 struct FwdLocalLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
     const int n_units = a.BH * a.P;
-    const dim3 grid(round_up(n_units, 8) * (a.Dv / DVT));
-    hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DVT>), grid, dim3(kThreads), 0, s, a, n_units);
+    hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
@@ -342,7 +355,7 @@ struct CorrectFwdLauncher {
 };
 
 launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv) {
-  return lookup3<FwdLocalLauncher, Bf16Dk, F32Dk>(dtype, chunk, dk, tile_of(dv));
+  return lookup_cdd<FwdLocalLauncher>(dtype, chunk, dk, dv);
 }
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv) {
   return lookup3<CorrectFwdLauncher, Bf16Dk, F32Dk>(dtype, chunk, dk, tile_of(dv));

@@ -90,4 +90,24 @@ inline launch_fn lookup3(int dtype, int chunk, int d, int tile) {
   return r;
 }
 
+// Generic lookup over (dtype, chunk, dk, dv): Launcher<E, C, DK, DV>::run.
+template <template <typename, int, int, int> class Launcher>
+inline launch_fn lookup_cdd(int dtype, int chunk, int dk, int dv) {
+  launch_fn r = nullptr;
+  if (dtype == 1) {
+    dispatch_int(chunk, Bf16Chunks{}, [&](auto c) {
+      dispatch_int(dk, Bf16Dk{}, [&](auto a) {
+        dispatch_int(dv, Bf16Dv{}, [&](auto b) { r = &Launcher<__bf16, c.value, a.value, b.value>::run; });
+      });
+    });
+  } else if (dtype == 0) {
+    dispatch_int(chunk, F32Chunks{}, [&](auto c) {
+      dispatch_int(dk, F32Dk{}, [&](auto a) {
+        dispatch_int(dv, F32Dv{}, [&](auto b) { r = &Launcher<float, c.value, a.value, b.value>::run; });
+      });
+    });
+  }
+  return r;
+}
+
 }  // namespace gla
