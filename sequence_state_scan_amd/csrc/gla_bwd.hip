@@ -17,27 +17,6 @@
 
 namespace gla {
 
-// Gate prefix sums of one 4-token x 8-channel item per lane (see the forward's loader): on
-// return b[r][e] is the in-chunk inclusive running sum of g and lam[e] the chunk total.
-template <int NTG>
-__device__ __forceinline__ void chunk_gate_prefix(const Rows4x8<float>& pg, bool has_item, float (&b)[4][8],
-                                                  float (&lam)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float run = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      run += has_item ? pg.at(r, e) : 0.f;
-      b[r][e] = run;
-    }
-    const float incl = seg_scan_incl<NTG>(run);
-    const float excl = seg_prev<NTG>(incl);
-    lam[e] = seg_last<NTG>(incl);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) b[r][e] += excl;
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 // dq, dk, dg, D: one workgroup per unit; wave w owns the 16-row blocks cb = w, w+NW, ... of
 // U^T[j][c] (all j) and of the chunk state it reads for dq.
@@ -85,19 +64,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dqk_kernel(BwdArgs a, int n_units
   const long chunk0 = (long)unit * nchunks;
   const long SS = (long)DK * DV;  // one state
   const int w = wave_id();
-  // Loader role of a thread: q-role threads (first half) and k-role threads each own one
-  // 4-token x 8-channel item of the chunk (tokens 4tg.., channels 8cg..).
-  struct Role {
-    bool krole, has_item;
-    int tg, cg;
-    __device__ explicit Role(int tid) {
-      krole = tid >= RT;
-      const int rt = krole ? tid - RT : tid;
-      has_item = rt < NI;
-      tg = rt % NTG;
-      cg = rt / NTG;
-    }
-  };
+  typedef LoaderRole<RT, NTG, NI> Role;
 
   Rows4x8<float> pg;
   Rows4x8<E> px;

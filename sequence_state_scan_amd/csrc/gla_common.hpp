@@ -221,6 +221,48 @@ __device__ __forceinline__ f32x4 mma_regX(f32x4 acc, const f32x4 (&R)[NKB], cons
   return acc;
 }
 
+// acc[tT] += X . Y_tT^T for NTT row blocks of Y at once, X from accumulator registers as in
+// mma_regX (lane supplies X[m = n16][k = 16kb + 4g4 + i]); the lane's Y row for block tT is
+// Y0 + tT * ldblk.  The k steps run outermost, so each X step is converted to the element type once.
+template <typename E, int NKB, int NTT>
+__device__ __forceinline__ void mma_regX_rows(f32x4 (&acc)[NTT], const f32x4 (&R)[NKB], const E* Y0, int ldblk) {
+  const int g4 = lane_id() >> 4;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int p = 0; p < (NKB + 1) / 2; ++p) {
+      bf16x8 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (bf16)R[2 * p][i];
+        x[4 + i] = 2 * p + 1 < NKB ? (bf16)R[2 * p + 1][i] : (bf16)0.f;
+      }
+#pragma unroll
+      for (int tT = 0; tT < NTT; ++tT) {
+        const E* Yrow = Y0 + tT * ldblk;
+        const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 4 * g4);
+        bf16x4 yhi;
+        if (2 * p + 1 < NKB) yhi = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 16 + 4 * g4);
+        else yhi = bf16x4{};
+        bf16x8 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[i] = ylo[i];
+          y[4 + i] = yhi[i];
+        }
+        acc[tT] = Mma<bf16>::mma(x, y, acc[tT]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int tT = 0; tT < NTT; ++tT)
+          acc[tT] = Mma<float>::mma(R[kb][i], (Y0 + tT * ldblk)[16 * kb + 4 * g4 + i], acc[tT]);
+  }
+}
+
 // Same as mma_regX, with X given as pieces already in the element type: R[kb] holds
 // X[m = n16][k = 16*kb + 4*g4 + 0..3] (bf16x4 for bf16, f32x4 for float).
 template <typename E> struct Piece4 { typedef f32x4 type; };
@@ -229,6 +271,12 @@ template <> struct Piece4<bf16> { typedef bf16x4 type; };
 template <typename E>
 __device__ __forceinline__ typename Piece4<E>::type load_piece(const E* p) {
   return *reinterpret_cast<const typename Piece4<E>::type*>(p);
+}
+__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 widen(bf16x4 x) {
+  f32x4 r;
+  r[0] = (float)x[0]; r[1] = (float)x[1]; r[2] = (float)x[2]; r[3] = (float)x[3];
+  return r;
 }
 
 template <typename E, int NKB>
@@ -300,44 +348,90 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
 }
 
 // --------------------------------------------------------------------------------------------
-// Segmented scans across lanes: segments of W consecutive lanes (W a power of two dividing 64).
+// Store of one 16x16 accumulator tile X (lane (n16, g4) holds X[4g4 + i][n16]) into row-major
+// memory at base (row stride ld), with 8-byte (bf16) or 16-byte (float) stores of 4 consecutive
+// columns per lane.  bf16: the tile is transposed on the matrix core, X^T = X^T . I with the
+// tile as the A operand of a 16x16x16 MFMA (exact, one nonzero product per output), so lane
+// (n16, g4) ends up holding row n16, columns 4g4..4g4+3.  Returns the tile rounded to the
+// element type in its accumulator layout (the A operand), for reuse as an MFMA operand.
+// float: the 4x4 quad transpose above.
 // --------------------------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 identity_b_operand() {
+  // B[k = 4g4 + i][n = n16] = (k == n) for the 16x16x16 layout
+  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+  s16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (4 * g4 + i == n16) ? (short)0x3F80 : (short)0;
+  return b;
+}
+__device__ __forceinline__ bf16x4 store_tile(bf16* base, long ld, f32x4 x, s16x4 ident) {
+  bf16x4 xb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xb[i] = (bf16)x[i];
+  const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, xb), ident, zero4(), 0, 0, 0);
+  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+  store4(base + (long)n16 * ld + 4 * g4, t);
+  return xb;
+}
+__device__ __forceinline__ f32x4 store_tile(float* base, long ld, f32x4 x, s16x4) {
+  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+  store4(base + (long)(4 * g4 + (n16 & 3)) * ld + (n16 & ~3), quad_transpose(x));
+  return x;
+}
+
+// --------------------------------------------------------------------------------------------
+// Segmented scans across lanes: segments of W consecutive lanes (W a power of two, W <= 16), on
+// DPP row shifts inside the 16-lane rows (a lane whose source lies outside its row reads 0).
+// --------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_zero_fill(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int D> __device__ __forceinline__ float row_shr(float x) { return dpp_zero_fill<0x110 + D>(x); }
+template <int D> __device__ __forceinline__ float row_shl(float x) { return dpp_zero_fill<0x100 + D>(x); }
+
 // Inclusive prefix sum of x over the lanes of the segment (lane order).
 template <int W>
 __device__ __forceinline__ float seg_scan_incl(float x) {
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "segments of 1, 2, 4, 8 or 16 lanes");
   const int i = lane_id() & (W - 1);
-#pragma unroll
-  for (int d = 1; d < W; d <<= 1) {
-    const float y = __shfl_up(x, d, W);
-    if (i >= d) x += y;
-  }
+  if constexpr (W > 1) { const float y = row_shr<1>(x); x += (W == 16 || i >= 1) ? y : 0.f; }
+  if constexpr (W > 2) { const float y = row_shr<2>(x); x += (W == 16 || i >= 2) ? y : 0.f; }
+  if constexpr (W > 4) { const float y = row_shr<4>(x); x += (W == 16 || i >= 4) ? y : 0.f; }
+  if constexpr (W > 8) x += row_shr<8>(x);
   return x;
 }
 // Inclusive suffix sum of x over the lanes of the segment (from the segment's last lane down).
 template <int W>
 __device__ __forceinline__ float seg_scan_rev_incl(float x) {
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "segments of 1, 2, 4, 8 or 16 lanes");
   const int i = lane_id() & (W - 1);
-#pragma unroll
-  for (int d = 1; d < W; d <<= 1) {
-    const float y = __shfl_down(x, d, W);
-    if (i + d < W) x += y;
-  }
+  if constexpr (W > 1) { const float y = row_shl<1>(x); x += (W == 16 || i + 1 < W) ? y : 0.f; }
+  if constexpr (W > 2) { const float y = row_shl<2>(x); x += (W == 16 || i + 2 < W) ? y : 0.f; }
+  if constexpr (W > 4) { const float y = row_shl<4>(x); x += (W == 16 || i + 4 < W) ? y : 0.f; }
+  if constexpr (W > 8) x += row_shl<8>(x);
   return x;
 }
 // Value of x at the next lane of the segment (0 on the segment's last lane).
 template <int W>
 __device__ __forceinline__ float seg_next(float x) {
-  const float y = __shfl_down(x, 1, W);
-  return ((lane_id() & (W - 1)) != W - 1) ? y : 0.f;
+  const float y = row_shl<1>(x);
+  return (W == 16 || (lane_id() & (W - 1)) != W - 1) ? y : 0.f;
 }
-// Value of x at the segment's last lane, on every lane of the segment.
-template <int W>
-__device__ __forceinline__ float seg_last(float x) { return __shfl(x, W - 1, W); }
 // Value of x at the previous lane of the segment (0 on the segment's first lane).
 template <int W>
 __device__ __forceinline__ float seg_prev(float x) {
-  const float y = __shfl_up(x, 1, W);
-  return (lane_id() & (W - 1)) ? y : 0.f;
+  const float y = row_shr<1>(x);
+  return (W == 16 || (lane_id() & (W - 1)) != 0) ? y : 0.f;
+}
+// Value of x at the segment's last lane, on every lane of the segment.
+template <int W>
+__device__ __forceinline__ float seg_last(float x) {
+  if constexpr (W == 16)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xF, 0xF, false));  // row_newbcast:15
+  else
+    return __shfl(x, W - 1, W);
 }
 
 // Raw 4-row x 8-column tile piece of a row-major tensor, held in registers for prefetching.
@@ -363,6 +457,62 @@ template <> struct Rows4x8<float> {
     const float4 v = r[i][e >> 2];
     const int k = e & 3;
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+
+// Raw 4-row x 4-column tile piece of a row-major tensor, held in registers for prefetching.
+template <typename E> struct Rows4x4;
+template <> struct Rows4x4<bf16> {
+  bf16x4 r[4];
+  __device__ __forceinline__ void load(const bf16* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const bf16x4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float at(int i, int e) const { return (float)r[i][e]; }
+};
+template <> struct Rows4x4<float> {
+  f32x4 r[4];
+  __device__ __forceinline__ void load(const float* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const f32x4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float at(int i, int e) const { return r[i][e]; }
+};
+
+// Gate prefix sums of one 4-token x NE-channel item per lane (Rows: Rows4x8<float> or
+// Rows4x4<float>), the items of one channel group lying on NTG consecutive lanes in token order:
+// on return b[r][e] is the in-chunk inclusive running sum of g and lam[e] the chunk total.
+template <int NTG, int NE, class Rows>
+__device__ __forceinline__ void chunk_gate_prefix(const Rows& pg, bool has_item, float (&b)[4][NE], float (&lam)[NE]) {
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      run += has_item ? pg.at(r, e) : 0.f;
+      b[r][e] = run;
+    }
+    const float incl = seg_scan_incl<NTG>(run);
+    const float excl = seg_prev<NTG>(incl);
+    lam[e] = seg_last<NTG>(incl);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r][e] += excl;
+  }
+}
+
+// Loader role of a thread when q and k items are loaded side by side: threads [0, RT) each own
+// one 4-token x 8-channel item of q (tokens 4tg.., channels 8cg..), threads [RT, 2RT) the same
+// item of k; the NTG items of one channel group lie on consecutive lanes.
+template <int RT, int NTG, int NI>
+struct LoaderRole {
+  bool krole, has_item;
+  int tg, cg;
+  __device__ __forceinline__ explicit LoaderRole(int tid) {
+    krole = tid >= RT;
+    const int rt = krole ? tid - RT : tid;
+    has_item = NI == RT || rt < NI;
+    tg = rt % NTG;
+    cg = rt / NTG;
   }
 };
 

@@ -15,26 +15,24 @@
 namespace gla {
 
 // dk and dg: one workgroup per (unit, DKT-wide slice of d_k).  G[c][:] for the slice sits in
-// registers (wave w owns the 16-row blocks cb = w, w+4, ...) and feeds the MFMA A operand.
-template <typename E, int C, int DV, int DKT>
+// registers (wave w owns the 16-row blocks cb = w, w+4, ...) and feeds the MFMA A operand.  Every
+// global read of a chunk is issued before its writes (one memory round trip per chunk).
+template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, int n_units) {
-  constexpr int NTB = C / 8, NCB8 = DKT / 8, NKBLK = NTB * NCB8, NVB = NTB * (DV / 8);
+  constexpr int DKT = DK < 64 ? DK : 64, NT = DK / DKT;
+  constexpr int NTG = C / 4, NCG = DKT / 8, NI = NTG * NCG;
+  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, kThreads);
   constexpr int LDV = DV + kPad, LDL = DKT + 4;
   constexpr int NJB = DV / 16, NCB = DKT / 16, NTT = C / 16;
   constexpr int CPW = ceil_div(NCB, kWaves);
-  static_assert(NKBLK <= kThreads, "one 8x8 block per loader thread");
+  static_assert(NI <= kThreads, "one 4x8 item per thread");
   typedef typename Piece4<E>::type piece;
 
   __shared__ __attribute__((aligned(16))) E sV[C * LDV];      // V [t][j]
   __shared__ __attribute__((aligned(16))) float sE[C * LDL];  // exp(r_t) [t][c]
   __shared__ __attribute__((aligned(16))) float sKD[C * LDL]; // k * delta-dk [t][c]
-  __shared__ float sGtot[NTB * DKT];
-  __shared__ float sXt[NTB * DKT];
-  __shared__ float sEn[DKT];  // E_n
-  __shared__ float sR[DKT];   // R_n
+  __shared__ float sR[DKT];                                   // R_n
 
-  const int Dk = a.Dk;
-  const int NT = Dk / DKT;
   int unit, tile;
   xcd_map(blockIdx.x, NT, unit, tile);
   if (unit >= n_units) return;
@@ -49,11 +47,12 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, in
   const int bh = unit / a.P, p = unit - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
-  const long SS = (long)Dk * DV;
+  constexpr long SS = (long)DK * DV;
   const int c0 = tile * DKT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool has_blk = tid < NKBLK;
-  const int tb = tid / NCB8, cb8 = tid - (tid / NCB8) * NCB8;
+  // item of g and dg: tokens 4tg..4tg+3, slice channels 8cg..8cg+7
+  const bool has_item = tid < NI;
+  const int tg = tid % NTG, cg = tid / NTG;
 
   // G slice: R[cc][jb][i] = G[c0 + 16cb + n16][16jb + 4g4 + i]
   const float* gp = a.seg_grad + (long)unit * SS;
@@ -71,78 +70,72 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, in
   }
   if (!__syncthreads_or(nonzero)) return;  // G_p == 0: nothing to add
 
-  float gcarry[8];  // sum of g from the segment's end back to the current chunk (loader threads)
+  float gcarry[8];  // sum of g over the chunks after the current one, up to the segment's end
 #pragma unroll
   for (int e = 0; e < 8; ++e) gcarry[e] = 0.f;
   for (int n = nchunks - 1; n >= 0; --n) {
     const long t0 = tok0 + (long)n * C;
-    // global state before this chunk, in G's lane layout
-    piece Sp[CPW][NJB];
+    // every read of this chunk before its writes: g, V, dk, k and the global state before the
+    // chunk here, dg once the chunk is known to be live
+    Rows4x8<float> pg, pdg;
+    if (has_item) pg.load(g + (t0 + tg * 4) * DK + c0 + cg * 8, DK);
+    Vec8<E> pv[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + kThreads * i;
+      if (NVP % kThreads == 0 || pc < NVP) pv[i].load(v + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+    }
+    piece dkprev[CPW][NTT], kk[CPW][NTT], Sp[CPW][NJB];
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
       const int cb = w + cc * kWaves;
-      const long roff = (long)(c0 + cb * 16 + n16) * DV + 4 * g4;
+      if (cb < NCB) {
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        if (cb >= NCB) {
-          Sp[cc][jb] = piece{};
-        } else if (n > 0) {
-          Sp[cc][jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
+        for (int tT = 0; tT < NTT; ++tT) {
+          const long go = (t0 + tT * 16 + n16) * DK + c0 + cb * 16 + 4 * g4;
+          dkprev[cc][tT] = load_piece(dk + go);
+          kk[cc][tT] = load_piece(k + go);
+        }
+        const long roff = (long)(c0 + cb * 16 + n16) * DV + 4 * g4;
+        if (n > 0) {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) Sp[cc][jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
         } else {
-          const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sp[cc][jb][i] = (E)x[i];
+          for (int jb = 0; jb < NJB; ++jb) {
+            const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sp[cc][jb][i] = (E)x[i];
+          }
         }
       }
     }
-    float gv[8][8];
+    // exp(r_t), r_t = sum of g over the tokens after t up to the segment's end
+    float lam[8];
     int live = 0;
-    if (has_blk) {
-      load_blk<float>(gv, g + (t0 + tb * 8) * Dk + c0 + cb8 * 8, Dk);
-      float tot[8];
+    {
+      float b[4][8];
+      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      if (has_item) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tot[e] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          float x[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) tot[e] += gv[r][e];
-        sGtot[tb * DKT + cb8 * 8 + e] = tot[e];
-      }
-    }
-    for (int vb = tid; vb < NVB; vb += kThreads) {
-      const int vtb = vb / (DV / 8), vjb = vb - (vb / (DV / 8)) * (DV / 8);
-      float vv[8][8];
-      load_blk<E>(vv, v + (t0 + vtb * 8) * DV + vjb * 8, DV);
-      store_blk_rows<E>(sV + (vtb * 8) * LDV + vjb * 8, LDV, vv);
-    }
-    __syncthreads();
-    if (has_blk) {
-      float run[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = gcarry[e];
-      for (int u = NTB - 1; u >= 0; --u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = sGtot[u * DKT + cb8 * 8 + e];
-          if (u > tb) run[e] += s;
-          gcarry[e] += s;
+          for (int e = 0; e < 8; ++e) {
+            x[e] = __expf(gcarry[e] + (lam[e] - b[r][e]));
+            live |= x[e] != 0.f;
+          }
+          store8(sE + (tg * 4 + r) * LDL + cg * 8, x);
         }
       }
-      // exclusive: tokens strictly after t (within the segment)
+    }
 #pragma unroll
-      for (int r = 7; r >= 0; --r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ex = __expf(run[e]);
-          run[e] += gv[r][e];
-          gv[r][e] = ex;
-          live |= ex != 0.f;
-        }
-      store_blk_rows<float>(sE + (tb * 8) * LDL + cb8 * 8, LDL, gv);
-      if (tb == 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sEn[cb8 * 8 + e] = __expf(gcarry[e]);
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + kThreads * i;
+      if (NVP % kThreads == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
     }
     if (!__syncthreads_or(live)) break;
+    if (has_item) pdg.load(dg + (t0 + tg * 4) * DK + c0 + cg * 8, DK);
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
       const int cb = w + cc * kWaves;
@@ -152,10 +145,8 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, in
           const int t = tT * 16 + n16;
           f32x4 acc = mma_regX<E, NJB>(zero4(), R[cc], sV + t * LDV);  // (G v_t)[c]
           acc *= load4(sE + t * LDL + cb * 16 + 4 * g4);
-          E* dkp = dk + (t0 + t) * Dk + c0 + cb * 16 + 4 * g4;
-          const f32x4 kk = load4(k + (t0 + t) * Dk + c0 + cb * 16 + 4 * g4);
-          store4(dkp, load4(dkp) + acc);
-          store4(sKD + t * LDL + cb * 16 + 4 * g4, kk * acc);
+          store4(dk + (t0 + t) * DK + c0 + cb * 16 + 4 * g4, widen(dkprev[cc][tT]) + acc);
+          store4(sKD + t * LDL + cb * 16 + 4 * g4, widen(kk[cc][tT]) * acc);
         }
         float part = 0.f;  // R_n = rowsum(S_{n-1} * G)
 #pragma unroll
@@ -165,62 +156,59 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, in
       }
     }
     __syncthreads();
-    float xs[8][8];
-    if (has_blk) {
+    // dg[t] += E_n R_n + sum_{s < t in the chunk} k_s delta-dk_s, E_n = exp(sum of g from the
+    // chunk's first token to the segment's end)
+    {
+      float xs[4][8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) load8(sKD + (tb * 8 + r) * LDL + cb8 * 8, xs[r]);
-      // exclusive prefix over the block's tokens
-      float run[8];
+      for (int r = 0; r < 4; ++r) {
+        if (has_item) load8(sKD + (tg * 4 + r) * LDL + cg * 8, xs[r]);
+        else
 #pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = 0.f;
+          for (int e = 0; e < 8; ++e) xs[r][e] = 0.f;
+      }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int e = 0; e < 8; ++e) {
+        float run = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int r = 0; r < 4; ++r) {
           const float x = xs[r][e];
-          xs[r][e] = run[e];
-          run[e] += x;
+          xs[r][e] = run;
+          run += x;
         }
+        const float excl = seg_prev<NTG>(seg_scan_incl<NTG>(run));
+        const float base = has_item ? __expf(gcarry[e] + lam[e]) * sR[cg * 8 + e] + excl : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sXt[tb * DKT + cb8 * 8 + e] = run[e];
-    }
-    __syncthreads();
-    if (has_blk) {
-      float base[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) base[e] = sEn[cb8 * 8 + e] * sR[cb8 * 8 + e];
-      for (int u = 0; u < tb; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) base[e] += sXt[u * DKT + cb8 * 8 + e];
+        for (int r = 0; r < 4; ++r) xs[r][e] += base;
       }
+      if (has_item)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        float* dgp = dg + (t0 + tb * 8 + r) * Dk + c0 + cb8 * 8;
-        float cur[8];
-        load8(dgp, cur);
+        for (int r = 0; r < 4; ++r) {
+          float outv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cur[e] += base[e] + xs[r][e];
-        store8(dgp, cur);
-      }
+          for (int e = 0; e < 8; ++e) outv[e] = pdg.at(r, e) + xs[r][e];
+          store8(dg + (t0 + tg * 4 + r) * DK + c0 + cg * 8, outv);
+        }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gcarry[e] += lam[e];
     __syncthreads();
   }
 }
 
 // dv: one workgroup per (unit, DVT-wide slice of d_v).  G^T[j][:] for the slice in registers.
-template <typename E, int C, int DK, int DVT>
+template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void correct_bwd_dv_kernel(CorrArgs a, int n_units) {
-  constexpr int NTB = C / 8, NCB8 = DK / 8, NQB = NTB * NCB8;
+  constexpr int DVT = DV < 64 ? DV : 64, NT = DV / DVT;
+  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG;
   constexpr int LDQ = DK + kPad;
   constexpr int NJB = DVT / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, kWaves);
-  static_assert(NQB <= kThreads, "one 8x8 block per loader thread");
+  static_assert(NI <= kThreads, "one 4x8 item per thread");
+  typedef typename Piece4<E>::type piece;
 
-  __shared__ __attribute__((aligned(16))) E sEK[C * LDQ];  // e_t * k_t [t][c]
-  __shared__ float sGtot[NTB * DK];
+  __shared__ __attribute__((aligned(16))) E sEK[2][C * LDQ];  // exp(r_t) k_t [t][c], by chunk parity
 
-  const int Dv = a.Dv;
-  const int NT = Dv / DVT;
   int unit, tile;
   xcd_map(blockIdx.x, NT, unit, tile);
   if (unit >= n_units) return;
@@ -232,23 +220,24 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dv_kernel(CorrArgs a, in
   const long tok0 = (long)bh * a.T + (long)p * L;
   const int j0 = tile * DVT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool has_blk = tid < NQB;
-  const int tb = tid / NCB8, cb8 = tid - (tid / NCB8) * NCB8;
+  const bool has_item = tid < NI;
+  const int tg = tid % NTG, cg = tid / NTG;
 
   // G^T slice: R[jj][kb][i] = G[16kb + 4g4 + i][j0 + 16jb + n16]
-  const float* gp = a.seg_grad + (long)unit * DK * Dv;
+  const float* gp = a.seg_grad + (long)unit * DK * DV;
   f32x4 R[JPW][NKB];
   int nonzero = 0;
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int jb = w + jj * kWaves;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 x = jb < NJB ? load4(gp + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3))
+                               : zero4();
+      R[jj][kb] = quad_transpose(x);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        R[jj][kb][i] = jb < NJB ? gp[(long)(kb * 16 + 4 * g4 + i) * Dv + j0 + jb * 16 + n16] : 0.f;
-        nonzero |= R[jj][kb][i] != 0.f;
-      }
+      for (int i = 0; i < 4; ++i) nonzero |= x[i] != 0.f;
+    }
   }
   if (!__syncthreads_or(nonzero)) return;
 
@@ -258,42 +247,41 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dv_kernel(CorrArgs a, in
   const int nchunks = L / C;
   for (int n = nchunks - 1; n >= 0; --n) {
     const long t0 = tok0 + (long)n * C;
-    float gv[8][8], kv[8][8];
-    int live = 0;
-    if (has_blk) {
-      load_blk<float>(gv, g + (t0 + tb * 8) * DK + cb8 * 8, DK);
-      load_blk<E>(kv, k + (t0 + tb * 8) * DK + cb8 * 8, DK);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float tot = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) tot += gv[r][e];
-        sGtot[tb * DK + cb8 * 8 + e] = tot;
-      }
+    const int par = n & 1;
+    Rows4x8<float> pg;
+    Rows4x8<E> pk;
+    if (has_item) {
+      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
+      pk.load(k + (t0 + tg * 4) * DK + cg * 8, DK);
     }
-    __syncthreads();
-    if (has_blk) {
-      float run[8];
+    piece dvprev[JPW][NTT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = gcarry[e];
-      for (int u = NTB - 1; u >= 0; --u) {
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jb = w + jj * kWaves;
+      if (jb < NJB)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = sGtot[u * DK + cb8 * 8 + e];
-          if (u > tb) run[e] += s;
-          gcarry[e] += s;
+        for (int tT = 0; tT < NTT; ++tT)
+          dvprev[jj][tT] = load_piece(dv + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4);
+    }
+    int live = 0;
+    {
+      float b[4][8], lam[8];
+      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      if (has_item) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float ex = __expf(gcarry[e] + (lam[e] - b[r][e]));
+            live |= ex != 0.f;
+            x[e] = pk.at(r, e) * ex;
+          }
+          store8(&sEK[par][(tg * 4 + r) * LDQ + cg * 8], x);
         }
       }
 #pragma unroll
-      for (int r = 7; r >= 0; --r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ex = __expf(run[e]);
-          run[e] += gv[r][e];
-          live |= ex != 0.f;
-          kv[r][e] *= ex;
-        }
-      store_blk_rows<E>(sEK + (tb * 8) * LDQ + cb8 * 8, LDQ, kv);
+      for (int e = 0; e < 8; ++e) gcarry[e] += lam[e];
     }
     if (!__syncthreads_or(live)) break;
 #pragma unroll
@@ -303,42 +291,42 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dv_kernel(CorrArgs a, in
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
           const int t = tT * 16 + n16;
-          const f32x4 acc = mma_regX<E, NKB>(zero4(), R[jj], sEK + t * LDQ);  // (G^T (e k_t))[j]
-          E* dvp = dv + (t0 + t) * Dv + j0 + jb * 16 + 4 * g4;
-          store4(dvp, load4(dvp) + acc);
+          const f32x4 acc = mma_regX<E, NKB>(widen(dvprev[jj][tT]), R[jj], &sEK[par][t * LDQ]);  // + G^T (e k_t)
+          store4(dv + (t0 + t) * DV + j0 + jb * 16 + 4 * g4, acc);
         }
       }
     }
-    __syncthreads();
   }
 }
 
-template <typename E, int C, int DV, int DKT>
+template <typename E, int C, int DK, int DV>
 struct CorrectBwdDkLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
     const int n_units = a.BH * a.P;
-    const dim3 grid(round_up(n_units, 8) * (a.Dk / DKT));
-    hipLaunchKernelGGL((correct_bwd_dk_kernel<E, C, DV, DKT>), grid, dim3(kThreads), 0, s, a, n_units);
+    constexpr int NT = DK / (DK < 64 ? DK : 64);
+    const dim3 grid(round_up(n_units, 8) * NT);
+    hipLaunchKernelGGL((correct_bwd_dk_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
-template <typename E, int C, int DK, int DVT>
+template <typename E, int C, int DK, int DV>
 struct CorrectBwdDvLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
     const int n_units = a.BH * a.P;
-    const dim3 grid(round_up(n_units, 8) * (a.Dv / DVT));
-    hipLaunchKernelGGL((correct_bwd_dv_kernel<E, C, DK, DVT>), grid, dim3(kThreads), 0, s, a, n_units);
+    constexpr int NT = DV / (DV < 64 ? DV : 64);
+    const dim3 grid(round_up(n_units, 8) * NT);
+    hipLaunchKernelGGL((correct_bwd_dv_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
 
 launch_fn lookup_correct_bwd_dk(int dtype, int chunk, int dk, int dv) {
-  return lookup3<CorrectBwdDkLauncher, Bf16Dv, F32Dv>(dtype, chunk, dv, tile_of(dk));
+  return lookup_cdd<CorrectBwdDkLauncher>(dtype, chunk, dk, dv);
 }
 launch_fn lookup_correct_bwd_dv(int dtype, int chunk, int dk, int dv) {
-  return lookup3<CorrectBwdDvLauncher, Bf16Dk, F32Dk>(dtype, chunk, dk, tile_of(dv));
+  return lookup_cdd<CorrectBwdDvLauncher>(dtype, chunk, dk, dv);
 }
 
 }  // namespace gla

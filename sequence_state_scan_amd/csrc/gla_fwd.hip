@@ -22,20 +22,21 @@ namespace gla {
 // element type E): the local chunk states the correction turns into global ones and the
 // backward reads.
 //
-// Per chunk: (1) the gate's running sum is taken with a shuffle scan across the lanes that hold
-// one 8-channel column (4 tokens per lane), q/k are scaled and every tile is staged in LDS, and
-// the next chunk's q, k, g, v are requested into registers; (2) the intra-chunk scores;
-// (3) outputs and the state update on MFMA.  The requests of (1) are in flight during (2)-(3).
+// Per chunk: (1) every thread takes one 4-token x 4-channel item of q, k and g: the gate's running
+// sum comes from a DPP scan across the 16 lanes that hold one channel group, q and k are scaled
+// and every tile is staged in LDS, and the next chunk's q, k, g, v are requested into registers;
+// (2) the intra-chunk scores; (3) outputs and the state update on MFMA.  The requests of (1) are
+// in flight during (2)-(3).
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG, RT = NT / 2;
+  constexpr int NTG = C / 4, NCG = DK / 4, NI = NTG * NCG;
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
   constexpr int LDQ = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   constexpr int KS = Mma<E>::KSTEP;
-  static_assert(NI <= RT, "one 4x8 item of q (and one of k) per loader thread");
+  static_assert(NI <= NT, "one 4x4 item of q, k and g per thread");
 
   __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
   __shared__ __attribute__((aligned(16))) E sK[C * LDQ];   // Kbar [s][c]
@@ -57,22 +58,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const int bh = unit / a.P, p = unit - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
+  const int w = wave_id();
+  const s16x4 ident = identity_b_operand();
 
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool krole = tid >= RT;
-  const int rt = krole ? tid - RT : tid;
-  const bool has_item = rt < NI;
-  const int tg = rt % NTG, cg = rt / NTG;
-  const E* __restrict__ xsrc = krole ? k : q;
-
-  Rows4x8<float> pg;
-  Rows4x8<E> px;
+  // item of a thread: tokens 4tg..4tg+3, channels 4cg..4cg+3 (tg = tid % NTG: the NTG items of one
+  // channel group lie on consecutive lanes)
+  Rows4x4<float> pg;
+  Rows4x4<E> pq, pk;
   Vec8<E> pv[VPT];
-  auto prefetch = [&](int n) {
+  auto prefetch = [&](int n, int tid) {
     const long t0 = tok0 + (long)n * C;
-    if (has_item) {
-      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
-      px.load(xsrc + (t0 + tg * 4) * DK + cg * 8, DK);
+    if (NI == NT || tid < NI) {
+      const long off = (t0 + (tid % NTG) * 4) * DK + (tid / NTG) * 4;
+      pg.load(g + off, DK);
+      pq.load(q + off, DK);
+      pk.load(k + off, DK);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -81,66 +81,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     }
   };
 
-  f32x4 S[JPW][NKB];
+  f32x4 S[JPW][NKB];  // S[jj][kb][i] = S[16kb + 4g4 + i][16jb + n16]
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) S[jj][kb] = zero4();
-  float ldsum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ldsum[e] = 0.f;
+  float ldsum[4] = {0.f, 0.f, 0.f, 0.f};  // log cumulative decay of the segment (item threads with tg == 0)
 
-  prefetch(0);
+  prefetch(0, threadIdx.x);
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
-    // ---- (1) gate prefix sums, scaled q / k, V -> LDS; request the next chunk ----
+    const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
+    const bool has_item = NI == NT || tid < NI;
+    const int tg = tid % NTG, cg = tid / NTG;
+    // ---- (1) gate prefix sums, Qbar, Kbar, Ktil, V -> LDS; request the next chunk ----
     {
-      float b[4][8], lam[8];
+      float b[4][4], lam[4];
+      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      if (has_item) {
+        f32x4 el;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float run = 0.f;
+        for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          run += has_item ? pg.at(r, e) : 0.f;
-          b[r][e] = run;
+          f32x4 xq, xk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float eb = __expf(b[r][e]);
+            xq[e] = pq.at(r, e) * eb;
+            xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb);  // exp(-b) to one ulp
+          }
+          const int off = (tg * 4 + r) * LDQ + cg * 4;
+          store4(sQ + off, xq);
+          store4(sK + off, xk);
+          store4(sKt + off, xk * el);
         }
-        const float incl = seg_scan_incl<NTG>(run);
-        const float excl = seg_prev<NTG>(incl);
-        lam[e] = seg_last<NTG>(incl);
+        if (tg == 0) {
+          store4(sLamE + cg * 4, el);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[r][e] += excl;
-      }
-      if (has_item) {
-        if (!krole) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = px.at(r, e) * __expf(b[r][e]);
-            store8(sQ + (tg * 4 + r) * LDQ + cg * 8, x);
-          }
-          if (tg == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              sLamE[cg * 8 + e] = __expf(lam[e]);
-              ldsum[e] += lam[e];
-            }
-          }
-        } else {
-          float el[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float xb[8], xt[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              xb[e] = px.at(r, e) * __expf(-b[r][e]);
-              xt[e] = xb[e] * el[e];
-            }
-            store8(sK + (tg * 4 + r) * LDQ + cg * 8, xb);
-            store8(sKt + (tg * 4 + r) * LDQ + cg * 8, xt);
-          }
+          for (int e = 0; e < 4; ++e) ldsum[e] += lam[e];
         }
       }
 #pragma unroll
@@ -150,7 +129,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the next chunk's loads after this chunk's staging
-    if (n + 1 < nchunks) prefetch(n + 1);
+    if (n + 1 < nchunks) prefetch(n + 1, tid);
     __syncthreads();
     // ---- (2) intra-chunk scores: A^T[s][t] = Kbar[s] . Qbar[t], kept for s <= t, stored as A[t][s] ----
     for (int idx = w; idx < NTT * NTT; idx += NW) {
@@ -170,21 +149,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     for (int jj = 0; jj < JPW; ++jj) {
       const int jb = w + jj * NW;
       if (jb < NJB) {
+        f32x4 acc[NTT];
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
-          f32x4 acc = zero4();
           const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
-          acc = mma<E, true, false>(acc, sV + jb * 16, LDV, sA + tT * 16 * LDT, LDT, 0, ke);
-          acc = mma_regX<E, NKB>(acc, S[jj], sQ + (tT * 16 + n16) * LDQ);
-          store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc);
+          acc[tT] = mma<E, true, false>(zero4(), sV + jb * 16, LDV, sA + tT * 16 * LDT, LDT, 0, ke);
         }
+        mma_regX_rows<E, NKB, NTT>(acc, S[jj], sQ + n16 * LDQ, 16 * LDQ);
+#pragma unroll
+        for (int tT = 0; tT < NTT; ++tT) store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc[tT]);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) S[jj][kb][i] *= sLamE[kb * 16 + 4 * g4 + i];
           S[jj][kb] = mma<E, true, true>(S[jj][kb], sKt + kb * 16, LDQ, sV + jb * 16, LDV, 0, C);
-          // lane (n16 = 4m + r) stores row 16kb + 4g4 + r, columns 16jb + 4m .. +3
-          store4(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
+          store_tile(cs + (long)kb * 16 * DV + jb * 16, DV, S[jj][kb], ident);
         }
       }
     }
@@ -193,6 +172,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 
   // ---- segment results: local end state (float32) and log cumulative decay ----
   float* st = a.seg_state + (long)unit * DK * DV;
+  const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int jb = w + jj * NW;
@@ -201,31 +181,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
       for (int kb = 0; kb < NKB; ++kb)
         store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
   }
-  if (!krole && has_item && tg == 0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a.seg_logdecay[(long)unit * DK + cg * 8 + e] = ldsum[e];
-  }
+  const int tid = threadIdx.x;
+  if ((NI == NT || tid < NI) && tid % NTG == 0) store4(a.seg_logdecay + (long)unit * DK + (tid / NTG) * 4,
+                                                      f32x4{ldsum[0], ldsum[1], ldsum[2], ldsum[3]});
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
 //   o_t              += (q_t * a_t) . S_in[p],   a_t = exp(sum of g from the segment start to t)
 //   chunk_states[n]  += diag(a at the end of chunk n) S_in[p]
-// One workgroup per (unit, d_v slice); S_in's slice sits in registers in the accumulator layout
-// and feeds the MFMA A operand directly.  With g <= 0, a_t only decreases: once every a_t of a
-// chunk is exactly 0.0f, so are all later ones (and the chunk-end decays), and the loop stops.
-template <typename E, int C, int DK, int DVT>
+// One workgroup per (unit, DVT-wide slice of d_v); S_in's slice sits in registers in the
+// accumulator layout and feeds the MFMA A operand directly.  Every global read of a chunk (q, g,
+// the outputs and the chunk state to update) is issued before any of its writes, so a chunk costs
+// one memory round trip, not one per read-modify-write.  With g <= 0, a_t only decreases: once
+// every a_t of a chunk is exactly 0.0f, so are all later ones (and the chunk-end decays), and the
+// loop stops.
+template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n_units) {
-  constexpr int NTB = C / 8, NCB8 = DK / 8, NQB = NTB * NCB8;
+  constexpr int DVT = DV < 64 ? DV : 64, NT = DV / DVT;
+  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG;
   constexpr int LDQ = DK + kPad;
   constexpr int NJB = DVT / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, kWaves);
-  static_assert(NQB <= kThreads, "one 8x8 block of q per loader thread");
+  static_assert(NI <= kThreads, "one 4x8 item of q per thread");
+  typedef typename Piece4<E>::type piece;
 
-  __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];  // q * a   [t][c]
-  __shared__ float sGtot[NTB * DK];
-  __shared__ float sAend[DK];                              // a at the chunk's last token
+  // double-buffered by chunk parity, so one barrier per chunk suffices
+  __shared__ __attribute__((aligned(16))) E sQ[2][C * LDQ];  // q * a   [t][c]
+  __shared__ float sAend[2][DK];                              // a at the chunk's last token
 
-  const int NT = a.Dv / DVT;
   int unit, tile;
   xcd_map(blockIdx.x, NT, unit, tile);
   if (unit >= n_units) return;
@@ -233,7 +216,6 @@ __global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n
   const float* __restrict__ g = a.g;
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
-  const int Dv = a.Dv;
   const int L = a.T / a.P;
   const int nchunks = L / C;
   const int bh = unit / a.P, p = unit - bh * a.P;
@@ -241,95 +223,97 @@ __global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n
   const long chunk0 = (long)unit * nchunks;
   const int j0 = tile * DVT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool has_blk = tid < NQB;
-  const int tb = tid / NCB8, cb = tid - (tid / NCB8) * NCB8;
+  // item of q and g: tokens 4tg..4tg+3, channels 8cg..8cg+7 (the NTG items of a channel group
+  // lie on consecutive lanes)
+  const bool has_item = tid < NI;
+  const int tg = tid % NTG, cg = tid / NTG;
 
-  // incoming state slice, accumulator layout: R[jj][kb][i] = S_in[16kb + 4g4 + i][j0 + 16jb + n16]
-  f32x4 R[JPW][NKB];
-  const float* sin = a.seg_in + (long)unit * DK * Dv;
+  // incoming state slice, accumulator layout: R[jj][kb][i] = S_in[16kb + 4g4 + i][j0 + 16jb + n16];
+  // RT is the same slice quad-transposed: RT[jj][kb][i] = S_in[16kb + 4g4 + (n16&3)][j0 + 16jb + (n16&~3) + i]
+  f32x4 R[JPW][NKB], RT[JPW][NKB];
+  const float* sin = a.seg_in + (long)unit * DK * DV;
   int nonzero = 0;
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int jb = w + jj * kWaves;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      RT[jj][kb] = jb < NJB ? load4(sin + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3))
+                            : zero4();
+      R[jj][kb] = quad_transpose(RT[jj][kb]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        R[jj][kb][i] = jb < NJB ? sin[(long)(kb * 16 + 4 * g4 + i) * Dv + j0 + jb * 16 + n16] : 0.f;
-        nonzero |= R[jj][kb][i] != 0.f;
-      }
+      for (int i = 0; i < 4; ++i) nonzero |= RT[jj][kb][i] != 0.f;
+    }
   }
   if (!__syncthreads_or(nonzero)) return;  // zero incoming state: nothing to add
 
-  float carry[8];
+  float carry[8];  // sum of g from the segment start to the end of the previous chunk
 #pragma unroll
   for (int e = 0; e < 8; ++e) carry[e] = 0.f;
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
-    float gv[8][8], xv[8][8];
-    int live = 0;
-    if (has_blk) {
-      load_blk<float>(gv, g + (t0 + tb * 8) * DK + cb * 8, DK);
-      load_blk<E>(xv, q + (t0 + tb * 8) * DK + cb * 8, DK);
-#pragma unroll
-      for (int r = 1; r < 8; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[r][e] += gv[r - 1][e];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sGtot[tb * DK + cb * 8 + e] = gv[7][e];
+    const int par = n & 1;
+    E* const cs = cst + (chunk0 + n) * (long)DK * DV;
+    // every read of this chunk first
+    Rows4x8<float> pg;
+    Rows4x8<E> px;
+    if (has_item) {
+      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
+      px.load(q + (t0 + tg * 4) * DK + cg * 8, DK);
     }
-    __syncthreads();
-    if (has_blk) {
-      float pre[8], tot[8];
+    piece oprev[JPW][NTT], cprev[JPW][NKB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { pre[e] = carry[e]; tot[e] = 0.f; }
-      for (int u = 0; u < NTB; ++u) {
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jb = w + jj * kWaves;
+      if (jb < NJB) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = sGtot[u * DK + cb * 8 + e];
-          if (u < tb) pre[e] += s;
-          tot[e] += s;
+        for (int tT = 0; tT < NTT; ++tT)
+          oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          cprev[jj][kb] = load_piece(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3));
+      }
+    }
+    int live = 0;
+    {
+      float b[4][8], lam[8];
+      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      if (has_item) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float av = __expf(carry[e] + b[r][e]);
+            live |= av != 0.f;
+            x[e] = px.at(r, e) * av;
+          }
+          store8(&sQ[par][(tg * 4 + r) * LDQ + cg * 8], x);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int e = 0; e < 8; ++e) carry[e] += lam[e];
+      if (has_item && tg == 0)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float av = __expf(gv[r][e] + pre[e]);
-          live |= av != 0.f;
-          xv[r][e] *= av;
-        }
-      store_blk_rows<E>(sQ + (tb * 8) * LDQ + cb * 8, LDQ, xv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) carry[e] += tot[e];
-      if (tb == 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sAend[cb * 8 + e] = __expf(carry[e]);
+        for (int e = 0; e < 8; ++e) sAend[par][cg * 8 + e] = __expf(carry[e]);
     }
     if (!__syncthreads_or(live)) break;  // every a_t of this chunk (and all later ones) is 0
-    E* cs = cst + (chunk0 + n) * (long)DK * Dv;
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
       const int jb = w + jj * kWaves;
       if (jb < NJB) {
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
-          f32x4 acc = mma_regX<E, NKB>(zero4(), R[jj], sQ + (tT * 16 + n16) * LDQ);
-          E* op = o + (t0 + tT * 16 + n16) * Dv + j0 + jb * 16 + 4 * g4;
-          const f32x4 prev = load4(op);
-          store4(op, prev + acc);
+          const f32x4 acc = mma_regX<E, NKB>(widen(oprev[jj][tT]), R[jj], &sQ[par][(tT * 16 + n16) * LDQ]);
+          store4(o + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4, acc);
         }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = kb * 16 + 4 * g4 + i;
-            E* sp = cs + (long)c * Dv + j0 + jb * 16 + n16;
-            *sp = (E)((float)*sp + sAend[c] * R[jj][kb][i]);
-          }
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int c = kb * 16 + 4 * g4 + (n16 & 3);
+          store4(cs + (long)c * DV + j0 + jb * 16 + (n16 & ~3), widen(cprev[jj][kb]) + sAend[par][c] * RT[jj][kb]);
+        }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -343,13 +327,14 @@ struct FwdLocalLauncher {
   }
 };
 
-template <typename E, int C, int DK, int DVT>
+template <typename E, int C, int DK, int DV>
 struct CorrectFwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
     const int n_units = a.BH * a.P;
-    const dim3 grid(round_up(n_units, 8) * (a.Dv / DVT));
-    hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DVT>), grid, dim3(kThreads), 0, s, a, n_units);
+    constexpr int NT = DV / (DV < 64 ? DV : 64);
+    const dim3 grid(round_up(n_units, 8) * NT);
+    hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
@@ -358,7 +343,7 @@ launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv) {
   return lookup_cdd<FwdLocalLauncher>(dtype, chunk, dk, dv);
 }
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv) {
-  return lookup3<CorrectFwdLauncher, Bf16Dk, F32Dk>(dtype, chunk, dk, tile_of(dv));
+  return lookup_cdd<CorrectFwdLauncher>(dtype, chunk, dk, dv);
 }
 
 }  // namespace gla
