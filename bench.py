@@ -7,11 +7,19 @@ Inputs are drawn once (seeded, synthetic) and stay resident in HBM; every output
 buffer is allocated before the timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--gate VARIANT]
+                  [--no-cpu-baseline] [--copy-calibration]
+
+The roofline's "traffic" is the HBM bytes per launch of the dominant call as read by rocprofv3
+counters (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a device copy of
+known size); it is taken from profiles/<call>_<workload>_traffic.md and reported only while the
+kernel sources still hash to the value recorded there (null otherwise).
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -26,6 +34,37 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "sequence_state_scan_amd", "csrc")
+# the sources that build each call's kernels (their hash dates a traffic measurement)
+CALL_SOURCES = {
+    "gla_chunk_fwd": ["gla_fwd.hip", "gla_common.hpp", "gla_kernels.hpp"],
+    "gla_chunk_bwd": ["gla_bwd.hip", "gla_common.hpp", "gla_kernels.hpp"],
+}
+COPY_CALIBRATION_BYTES = 1 << 30
+KERNELS_OF = {"gla_chunk_bwd": " (bwd_dqk_kernel + bwd_dv_kernel)", "gla_chunk_fwd": " (fwd_local_kernel)"}
+
+
+def sources_hash(call):
+    h = hashlib.sha256()
+    for f in CALL_SOURCES.get(call, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(call, workload):
+    """HBM bytes per launch from the committed counter summary, if it still matches the sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (call, workload))
+    if call not in CALL_SOURCES or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_h = re.search(r"^sources_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != sources_hash(call):
+        return None
+    return int(m_b.group(1))
 
 
 def alg_bytes(w, part):
@@ -53,9 +92,9 @@ def alg_flops(w, part):
     return th * (fwd if part == "fwd" else bwd)
 
 
-def cpu_baseline(w, gate, budget_s=12.0):
+def cpu_baseline(w, gate, budget_s=15.0):
     """The oracle (plain float64 recurrence, fwd+bwd) on a bounded sample of the workload: head 0,
-    the first n segments, n grown until the run takes about budget_s."""
+    the first n segments, n grown until one run takes at least 2/3 of budget_s (or covers the head)."""
     import numpy as np
     import oracle
     from sequence_state_scan_amd import inputs
@@ -74,9 +113,9 @@ def cpu_baseline(w, gate, budget_s=12.0):
         oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["do"])
         dt = time.perf_counter() - t0
         spent, tokens = dt, t1
-        if dt >= budget_s / 4 or t1 >= w.T or n >= 64:
+        if dt >= budget_s * 2 / 3 or t1 >= w.T:
             break
-        n = max(n + 1, int(n * math.ceil(budget_s / 4 / max(dt, 1e-3))))
+        n = max(n + 1, int(n * budget_s / max(dt, 1e-3)))
     # tokens of the workload per second: one head of `tokens` tokens is tokens / H workload tokens
     value = (tokens / (w.B * w.H)) / spent
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -92,6 +131,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--gate", default="logsigmoid16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy %d bytes device to device (untimed), the reference for the byte counters"
+                         % COPY_CALIBRATION_BYTES)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs every segment on a single MI355X and has no "
@@ -149,6 +191,14 @@ def main():
                                                                       dv=buf["dv"], dg=buf["dg"])),
     ]
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: %d bytes copied" % COPY_CALIBRATION_BYTES)
+
     stream = torch.cuda.current_stream(dev)  # the stream every call launches on
     for _ in range(args.warmup):
         for _, fn in calls:
@@ -187,7 +237,8 @@ def main():
     if dom_bytes:
         ach = dom_bytes / (per_call[dom] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, w.name),
+                "kernel": dom + KERNELS_OF.get(dom, ""),
                 "alg_bytes_per_launch": dom_bytes,
                 "mfma_frac": round(dom_flops / (per_call[dom] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     step_bytes = alg_bytes(w, "fwd") + alg_bytes(w, "bwd")

@@ -27,6 +27,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kWaves = 4;
 constexpr int kPad = 8;        // LDS row padding in elements (keeps 16-byte alignment)
+// Row padding of tiles that are only read with the transposing load: the 4 rows one 16-lane
+// group reads then start 16 elements (8 banks) apart and cover disjoint banks.
+constexpr int kPadT = 16;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

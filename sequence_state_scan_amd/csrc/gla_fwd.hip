@@ -32,18 +32,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   constexpr int NT = NW * 64;
   constexpr int NTG = C / 4, NCG = DK / 4, NI = NTG * NCG;
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDQ = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
+  constexpr int LDQ = DK + kPad, LDKT = DK + kPadT, LDV = DV + kPadT, LDT = C + kPad;
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
-  constexpr int KS = Mma<E>::KSTEP;
+  constexpr int KS = Mma<E>::KSTEP, NKS = C / KS;
   static_assert(NI <= NT, "one 4x4 item of q, k and g per thread");
+  static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
 
   __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
   __shared__ __attribute__((aligned(16))) E sK[C * LDQ];   // Kbar [s][c]
-  __shared__ __attribute__((aligned(16))) E sKt[C * LDQ];  // Ktil [s][c]
+  __shared__ __attribute__((aligned(16))) E sKt[C * LDKT]; // Ktil [s][c]
   __shared__ __attribute__((aligned(16))) E sV[C * LDV];   // V    [s][j]
   __shared__ __attribute__((aligned(16))) E sA[C * LDT];   // A    [t][s], masked
-  __shared__ float sLamE[DK];                              // exp(lam) per channel
+  __shared__ __attribute__((aligned(16))) float sLamE[DK];  // exp(lam) per channel
 
   const int unit = blockIdx.x;
   if (unit >= n_units) return;
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const long chunk0 = (long)unit * nchunks;
   const int w = wave_id();
   const s16x4 ident = identity_b_operand();
+  typedef typename Mma<E>::frag frag;
 
   // item of a thread: tokens 4tg..4tg+3, channels 4cg..4cg+3 (tg = tid % NTG: the NTG items of one
   // channel group lie on consecutive lanes)
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
           const int off = (tg * 4 + r) * LDQ + cg * 4;
           store4(sQ + off, xq);
           store4(sK + off, xk);
-          store4(sKt + off, xk * el);
+          store4(sKt + (tg * 4 + r) * LDKT + cg * 4, xk * el);
         }
         if (tg == 0) {
           store4(sLamE + cg * 4, el);
@@ -144,26 +146,78 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     }
     __syncthreads();
     // ---- (3) outputs O^T[j][t] = V^T A^T + S_prev^T Qbar^T, then the state update ----
-    E* cs = cst + (chunk0 + n) * (long)DK * DV;
+    // Every operand fragment is read from LDS once per chunk: V^T of the wave's column blocks
+    // serves the intra-chunk outputs and the state update; each A, Qbar and Ktil^T fragment
+    // serves all of the wave's column blocks.
+    if (w < NJB) {
+      E* cs = cst + (chunk0 + n) * (long)DK * DV;
+      frag fv[JPW][NKS];
 #pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * NW;
-      if (jb < NJB) {
-        f32x4 acc[NTT];
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
-          acc[tT] = mma<E, true, false>(zero4(), sV + jb * 16, LDV, sA + tT * 16 * LDT, LDT, 0, ke);
+        for (int ks = 0; ks < NKS; ++ks) fv[jj][ks] = frag_ld<E, true>(sV + (w + jj * NW) * 16, LDV, ks * KS);
+      f32x4 acc[JPW][NTT];
+#pragma unroll
+      for (int tT = 0; tT < NTT; ++tT) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) acc[jj][tT] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          if (ks * KS < (tT + 1) * 16) {  // tokens s <= t only
+            const frag fa = frag_ld<E, false>(sA + tT * 16 * LDT, LDT, ks * KS);
+#pragma unroll
+            for (int jj = 0; jj < JPW; ++jj) acc[jj][tT] = Mma<E>::mma(fv[jj][ks], fa, acc[jj][tT]);
+          }
+      }
+      if constexpr (sizeof(E) == 2) {
+        static_assert(NKB % 2 == 0, "d_k a multiple of 32");
+#pragma unroll
+        for (int pp = 0; pp < NKB / 2; ++pp) {
+          bf16x8 x[JPW];
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[jj][i] = (bf16)S[jj][2 * pp][i];
+              x[jj][4 + i] = (bf16)S[jj][2 * pp + 1][i];
+            }
+#pragma unroll
+          for (int tT = 0; tT < NTT; ++tT) {
+            const E* yr = sQ + (tT * 16 + n16) * LDQ + 32 * pp + 4 * g4;
+            const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(yr);
+            const bf16x4 yhi = *reinterpret_cast<const bf16x4*>(yr + 16);
+            bf16x8 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              y[i] = ylo[i];
+              y[4 + i] = yhi[i];
+            }
+#pragma unroll
+            for (int jj = 0; jj < JPW; ++jj) acc[jj][tT] = Mma<bf16>::mma(x[jj], y, acc[jj][tT]);
+          }
         }
-        mma_regX_rows<E, NKB, NTT>(acc, S[jj], sQ + n16 * LDQ, 16 * LDQ);
+      } else {
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc[tT]);
+        for (int jj = 0; jj < JPW; ++jj) mma_regX_rows<E, NKB, NTT>(acc[jj], S[jj], sQ + n16 * LDQ, 16 * LDQ);
+      }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) S[jj][kb][i] *= sLamE[kb * 16 + 4 * g4 + i];
-          S[jj][kb] = mma<E, true, true>(S[jj][kb], sKt + kb * 16, LDQ, sV + jb * 16, LDV, 0, C);
-          store_tile(cs + (long)kb * 16 * DV + jb * 16, DV, S[jj][kb], ident);
+        for (int tT = 0; tT < NTT; ++tT)
+          store4(o + (t0 + tT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4, acc[jj][tT]);
+      // S = diag(exp(lam)) S + Ktil^T V
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 lamE = load4(sLamE + kb * 16 + 4 * g4);
+        frag fk[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) fk[ks] = frag_ld<E, true>(sKt + kb * 16, LDKT, ks * KS);
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          S[jj][kb] *= lamE;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
+          store_tile(cs + (long)kb * 16 * DV + (w + jj * NW) * 16, DV, S[jj][kb], ident);
         }
       }
     }
