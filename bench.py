@@ -43,7 +43,7 @@ CALL_SOURCES = {
     "gla_chunk_bwd": ["gla_bwd.hip", "gla_common.hpp", "gla_kernels.hpp"],
 }
 COPY_CALIBRATION_BYTES = 1 << 30
-KERNELS_OF = {"gla_chunk_bwd": " (bwd_dqk_kernel + bwd_dv_kernel)", "gla_chunk_fwd": " (fwd_local_kernel)"}
+KERNELS_OF = {"gla_chunk_bwd": " (bwd_kernel)", "gla_chunk_fwd": " (fwd_local_kernel)"}
 
 
 def sources_hash(call):

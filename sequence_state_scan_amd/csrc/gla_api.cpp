@@ -43,18 +43,17 @@ bool shape_listed(int dtype, int dk, int dv, int chunk) {
 }
 
 struct Kernels {
-  gla::launch_fn fwd, corr_fwd, dqk, dv, corr_dk, corr_dv;
+  gla::launch_fn fwd, corr_fwd, bwd, corr_dk, corr_dv;
 };
 
 bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
   if (!shape_listed(dtype, dk, dv, chunk)) return false;
   k->fwd = gla::lookup_fwd_local(dtype, chunk, dk, dv);
   k->corr_fwd = gla::lookup_correct_fwd(dtype, chunk, dk, dv);
-  k->dqk = gla::lookup_bwd_dqk(dtype, chunk, dk, dv);
-  k->dv = gla::lookup_bwd_dv(dtype, chunk, dk, dv);
+  k->bwd = gla::lookup_bwd(dtype, chunk, dk, dv);
   k->corr_dk = gla::lookup_correct_bwd_dk(dtype, chunk, dk, dv);
   k->corr_dv = gla::lookup_correct_bwd_dv(dtype, chunk, dk, dv);
-  return k->fwd && k->corr_fwd && k->dqk && k->dv && k->corr_dk && k->corr_dv;
+  return k->fwd && k->corr_fwd && k->bwd && k->corr_dk && k->corr_dv;
 }
 
 // Shape checks shared by the chunked entry points.
@@ -175,9 +174,7 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
   gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate, B * H, T, dk, dv, P};
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = kern.dqk(&a, s);
-  if (e == hipSuccess) e = kern.dv(&a, s);
-  return launched(fn, e);
+  return launched(fn, kern.bwd(&a, s));
 }
 
 }  // extern "C"

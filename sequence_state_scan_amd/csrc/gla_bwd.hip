@@ -1,4 +1,4 @@
-// Backward kernels of the chunkwise form, per segment, given the GLOBAL state after every chunk
+// Backward of the chunkwise form, per segment, given the GLOBAL state after every chunk
 // (chunk_states, written by the local pass and corrected by the forward correction) and the
 // segment's global incoming state S_in.  With b, lam, Qbar, Kbar as in the forward, per chunk n:
 //   dA[t][s] = do_t . v_s  for s <= t,    A = (Qbar Kbar^T) masked the same way
@@ -9,42 +9,56 @@
 //   dg_t     = sum_{t <= t' in chunk n} (q dq - k dk)_t' + rowsum(S_n * U_n)
 // The last line is exact: over the segment's tokens after chunk n the running sum of
 // q dq - k dk equals rowsum(S_n * U_n) (the closed form of dg applied to that suffix), so no sum
-// ever runs over more than one chunk.  Two kernels walk every segment backwards, one workgroup
-// of NW waves per segment each: one keeps U^T (all of d_v, all of d_k) for dq, dk, dg and the
-// segment's local state gradient D; the other keeps U for dv.
+// ever runs over more than one chunk.
+//
+// One workgroup of NW waves walks each segment from its end.  Wave w keeps the 16 rows
+// c = 16w.. of U^T (all of d_v) in accumulator registers: they feed dq and dk, which contract U
+// and the chunk state over d_v.  dv contracts U over d_k instead, so once per chunk the waves
+// write exp(lam) U into LDS (as rows U[c][:], half of d_v at a time), and dv's tiles read it
+// back with the transposing load.  q, k, g, v and do are read from HBM once per chunk.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 
 namespace gla {
 
-// ------------------------------------------------------------------------------------------
-// dq, dk, dg, D: one workgroup per unit; wave w owns the 16-row blocks cb = w, w+NW, ... of
-// U^T[j][c] (all j) and of the chunk state it reads for dq.
-// ------------------------------------------------------------------------------------------
+// Value of x at the first lane of the 16-lane row, on every lane of the row.
+__device__ __forceinline__ float row_first(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150, 0xF, 0xF, false));  // row_newbcast:0
+}
+
 template <typename E, int C, int DK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dqk_kernel(BwdArgs a, int n_units) {
+__global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG, RT = NT / 2;
+  constexpr int NTG = C / 4, NCG = DK / 4, NI = NTG * NCG;  // 4-token x 4-channel items of q, k, g
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDV = DV + kPad, LDQ = DK + kPad, LDT = C + kPad, LDX = DK + 4;
-  constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16;
-  constexpr int CPW = ceil_div(NCB, NW);
+  constexpr int LDV = DV + kPad, LDQ = DK + kPad, LDT = C + kPad;
+  constexpr int DVH = DV < 128 ? DV : 128, NH = DV / DVH;  // d_v columns of U staged at a time
+  constexpr int LDU = DVH + kPadT;
+  constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NJH = DVH / 16;
   constexpr int KS = Mma<E>::KSTEP;
   constexpr int KU = sizeof(E) == 2 ? 2 : 1;  // 16-wide d_v blocks per k-step of the MFMA
-  constexpr int RAWB = (C * LDV * (int)sizeof(E) > C * LDX * 4) ? C * LDV * (int)sizeof(E) : C * LDX * 4;
-  static_assert(NI <= RT, "one 4x8 item of q (and one of k) per loader thread");
+  constexpr int NDVT = ceil_div(NJH * NTT, NW);  // dv tiles per wave per half
+  static_assert(NI <= NT, "one 4x4 item of q, k and g per thread");
+  static_assert(NCB <= NW, "one 16-row block of U^T per wave");
+  static_assert(NJB % KU == 0, "d_v blocks pair up for bf16");
   typedef typename Piece4<E>::type piece;
 
-  __shared__ __attribute__((aligned(16))) E sdO[C * LDV];          // dO   [t][j]
-  __shared__ __attribute__((aligned(16))) unsigned char sRaw[RAWB];  // V [s][j], then x [t][c] (f32)
-  __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];           // Qbar [t][c]
-  __shared__ __attribute__((aligned(16))) E sK[C * LDQ];           // Kbar [s][c]
-  __shared__ __attribute__((aligned(16))) E sLam[C * LDQ];         // exp(b) [t][c]
-  __shared__ __attribute__((aligned(16))) E sdAT[C * LDT];         // dA^T [s][t], masked
-  __shared__ float sLamE[DK];
-  __shared__ float sCarry[2][DK];  // rowsum(S_n * U_n), by chunk parity
-  E* const sV = reinterpret_cast<E*>(sRaw);
-  float* const sX = reinterpret_cast<float*>(sRaw);
+  // LDS.  sV and sLam are dead once dq / dk are done; the U staging area then reuses them.
+  constexpr int SZ_V = C * LDV * (int)sizeof(E), SZ_Q = C * LDQ * (int)sizeof(E), SZ_T = C * LDT * (int)sizeof(E);
+  constexpr int SZ_U = DK * LDU * (int)sizeof(E);
+  constexpr int SZ_VL = SZ_V + SZ_Q > SZ_U ? SZ_V + SZ_Q : SZ_U;  // V and exp(b), later the U staging
+  constexpr int OFF_DO = 0, OFF_V = OFF_DO + SZ_V, OFF_LAM = OFF_V + SZ_V, OFF_Q = OFF_V + SZ_VL,
+                OFF_K = OFF_Q + SZ_Q, OFF_DAT = OFF_K + SZ_Q, OFF_AT = OFF_DAT + SZ_T, SMEM = OFF_AT + SZ_T;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  __shared__ __attribute__((aligned(16))) float sLamE[DK];
+  E* const sdO = reinterpret_cast<E*>(smem + OFF_DO);    // dO   [t][j]
+  E* const sV = reinterpret_cast<E*>(smem + OFF_V);      // V    [s][j]
+  E* const sU = reinterpret_cast<E*>(smem + OFF_V);      // exp(lam) U [c][j - half start], after dq / dk
+  E* const sLam = reinterpret_cast<E*>(smem + OFF_LAM);  // exp(b) [t][c]
+  E* const sQ = reinterpret_cast<E*>(smem + OFF_Q);      // Qbar [t][c]
+  E* const sK = reinterpret_cast<E*>(smem + OFF_K);      // Kbar [s][c]
+  E* const sdAT = reinterpret_cast<E*>(smem + OFF_DAT);  // dA^T [s][t], masked
+  E* const sAT = reinterpret_cast<E*>(smem + OFF_AT);    // A^T  [s][t], masked
 
   const int unit = blockIdx.x;
   if (unit >= n_units) return;
@@ -56,42 +70,43 @@ __global__ __launch_bounds__(NW * 64) void bwd_dqk_kernel(BwdArgs a, int n_units
   const float* __restrict__ g = a.g;
   E* __restrict__ dq = static_cast<E*>(a.dq);
   E* __restrict__ dk = static_cast<E*>(a.dk);
+  E* __restrict__ dv = static_cast<E*>(a.dv);
   float* __restrict__ dg = a.dg;
   const int L = a.T / a.P;
   const int nchunks = L / C;
   const int bh = unit / a.P, p = unit - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
-  const long SS = (long)DK * DV;  // one state
+  constexpr long SS = (long)DK * DV;  // one state
   const int w = wave_id();
-  typedef LoaderRole<RT, NTG, NI> Role;
+  const int cb = w;                   // this wave's 16-row block of U^T (waves w >= NCB hold none)
+  const bool urole = cb < NCB;
 
-  Rows4x8<float> pg;
-  Rows4x8<E> px;
+  // item of a thread: tokens 4tg..4tg+3, channels 4cg..4cg+3 (the NTG items of one channel group
+  // lie on consecutive lanes)
+  Rows4x4<float> pg;
+  Rows4x4<E> pq, pk;
   auto prefetch = [&](int n, int tid) {
-    const Role r(tid);
-    const long t0 = tok0 + (long)n * C;
-    if (r.has_item) {
-      pg.load(g + (t0 + r.tg * 4) * DK + r.cg * 8, DK);
-      px.load((r.krole ? k : q) + (t0 + r.tg * 4) * DK + r.cg * 8, DK);
+    if (NI == NT || tid < NI) {
+      const long off = (tok0 + (long)n * C + (tid % NTG) * 4) * DK + (tid / NTG) * 4;
+      pg.load(g + off, DK);
+      pq.load(q + off, DK);
+      pk.load(k + off, DK);
     }
   };
 
-  f32x4 U[CPW][NJB];  // U[cc][jb][i] = U[16cb + n16][16jb + 4g4 + i]
+  f32x4 U[NJB];  // U[jb][i] = U[16cb + n16][16jb + 4g4 + i]
 #pragma unroll
-  for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) U[cc][jb] = zero4();
-  if (threadIdx.x < DK) sCarry[(nchunks - 1) & 1][threadIdx.x] = 0.f;  // nothing after the last chunk
+  for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
+  float carry = 0.f;  // rowsum(S_n * U_n) for c = 16cb + n16: nothing after the last chunk
 
   prefetch(nchunks - 1, threadIdx.x);
   for (int n = nchunks - 1; n >= 0; --n) {
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
-    const Role role(tid);
-    const bool krole = role.krole, has_item = role.has_item;
-    const int tg = role.tg, cg = role.cg;
-    // this chunk's V and dO, and the global state before it (same lane layout as U)
+    const bool has_item = NI == NT || tid < NI;
+    const int tg = tid % NTG, cg = tid / NTG;
+    // this chunk's V and dO
     Vec8<E> pv[VPT], pd[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -104,32 +119,28 @@ __global__ __launch_bounds__(NW * 64) void bwd_dqk_kernel(BwdArgs a, int n_units
     }
     // ---- (1) gate prefix sums, Qbar, Kbar, exp(b); V, dO -> LDS ----
     {
-      float b[4][8], lam[8];
+      float b[4][4], lam[4];
       chunk_gate_prefix<NTG>(pg, has_item, b, lam);
       if (has_item) {
-        if (!krole) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8], e8[8];
+        for (int r = 0; r < 4; ++r) {
+          f32x4 xq, xk, eb4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              e8[e] = __expf(b[r][e]);
-              x[e] = px.at(r, e) * e8[e];
-            }
-            store8(sQ + (tg * 4 + r) * LDQ + cg * 8, x);
-            store8(sLam + (tg * 4 + r) * LDQ + cg * 8, e8);
+          for (int e = 0; e < 4; ++e) {
+            eb4[e] = __expf(b[r][e]);
+            xq[e] = pq.at(r, e) * eb4[e];
+            xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb4[e]);  // exp(-b) to one ulp
           }
-          if (tg == 0)
+          const int off = (tg * 4 + r) * LDQ + cg * 4;
+          store4(sQ + off, xq);
+          store4(sK + off, xk);
+          store4(sLam + off, eb4);
+        }
+        if (tg == 0) {
+          f32x4 el;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sLamE[cg * 8 + e] = __expf(lam[e]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = px.at(r, e) * __expf(-b[r][e]);
-            store8(sK + (tg * 4 + r) * LDQ + cg * 8, x);
-          }
+          for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
+          store4(sLamE + cg * 4, el);
         }
       }
 #pragma unroll
@@ -145,305 +156,173 @@ __global__ __launch_bounds__(NW * 64) void bwd_dqk_kernel(BwdArgs a, int n_units
     __builtin_amdgcn_sched_barrier(0);
     if (n > 0) prefetch(n - 1, tid);
     // the global state before this chunk, in U's lane layout (read during (2), used in (3))
-    piece Sp[CPW][NJB];
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int cb = w + cc * NW;
+    piece Sp[NJB];
+    if (urole) {
       const long roff = (long)(cb * 16 + n16) * DV + 4 * g4;
-      if (cb >= NCB) {
+      if (n > 0) {
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) Sp[cc][jb] = piece{};
-      } else if (n > 0) {
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) Sp[cc][jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
+        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
           const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sp[cc][jb][i] = (E)x[i];
+          for (int i = 0; i < 4; ++i) Sp[jb][i] = (E)x[i];
         }
       }
     }
     __syncthreads();
-    // ---- (2) dA[t][s] = dO[t] . V[s], stored as dA^T[s][t] for t >= s ----
-    for (int idx = w; idx < NTT * NTT; idx += NW) {
-      const int tT = idx / NTT, sT = idx - (idx / NTT) * NTT;
+    // ---- (2) dA[t][s] = dO[t] . V[s] and A[t][s] = Qbar[t] . Kbar[s], stored transposed, s <= t ----
+    for (int idx = w; idx < 2 * NTT * NTT; idx += NW) {
+      const bool isA = idx >= NTT * NTT;
+      const int r = isA ? idx - NTT * NTT : idx;
+      const int tT = r / NTT, sT = r - (r / NTT) * NTT;
       f32x4 acc = zero4();
-      if (sT <= tT) acc = mma<E, false, false>(acc, sdO + tT * 16 * LDV, LDV, sV + sT * 16 * LDV, LDV, 0, DV);
+      if (sT <= tT) {
+        if (isA) acc = mma<E, false, false>(acc, sQ + tT * 16 * LDQ, LDQ, sK + sT * 16 * LDQ, LDQ, 0, DK);
+        else acc = mma<E, false, false>(acc, sdO + tT * 16 * LDV, LDV, sV + sT * 16 * LDV, LDV, 0, DV);
+      }
       const int s = sT * 16 + n16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (tT * 16 + 4 * g4 + i < s) acc[i] = 0.f;
-      store4(sdAT + s * LDT + tT * 16 + 4 * g4, acc);
+      store4((isA ? sAT : sdAT) + s * LDT + tT * 16 + 4 * g4, acc);
     }
     __syncthreads();
-    // ---- (3) dq, dk, the U update and the next carry ----
-    // The d_v sum of dq (over the chunk state) and of dk (over exp(lam) U) runs in KU-block steps
-    // so that only one step's worth of the chunk state is live at a time.
-    const int par = n & 1;
-    f32x4 xr[CPW][NTT];  // q dq - k dk for this wave's rows, accumulator layout
+    // ---- (3) exp(lam) U, dq, dk, dg ----
+    if (urole) {
+      const float le = sLamE[cb * 16 + n16];
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int cb = w + cc * NW;
-      if (cb < NCB) {
-        const float le = sLamE[cb * 16 + n16];
-        f32x4 aq[NTT], ak[NTT];
+      for (int jb = 0; jb < NJB; ++jb) U[jb] *= le;  // exp(lam) U_n
+      // dq^T[c][t] = sum_j S[c][j] dO[t][j] + ...;  dk^T[c][s] = sum_j (exp(lam)U)[c][j] V[s][j] + ...
+      f32x4 aq[NTT], ak[NTT];
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) aq[tT] = ak[tT] = zero4();
-        float part = 0.f;
+      for (int tT = 0; tT < NTT; ++tT) aq[tT] = ak[tT] = zero4();
 #pragma unroll
-        for (int j0 = 0; j0 < NJB; j0 += KU) {
-          piece sp[KU];
-          f32x4 ue[KU];
+      for (int j0 = 0; j0 < NJB; j0 += KU) {
+        piece sp[KU];
+        f32x4 ue[KU];
 #pragma unroll
-          for (int u = 0; u < KU; ++u) {
-            sp[u] = Sp[cc][j0 + u];
-            ue[u] = U[cc][j0 + u] * le;  // exp(lam) U_n
-          }
-#pragma unroll
-          for (int tT = 0; tT < NTT; ++tT) {
-            const int t = tT * 16 + n16;
-            // dq^T[c][t] += sum_j S[c][j] dO[t][j];  dk^T[c][s] += sum_j (exp(lam)U)[c][j] V[s][j]
-            aq[tT] = mma_regX_e<E, KU>(aq[tT], sp, sdO + t * LDV + j0 * 16);
-            ak[tT] = mma_regX<E, KU>(ak[tT], ue, sV + t * LDV + j0 * 16);
-          }
-#pragma unroll
-          for (int u = 0; u < KU; ++u) {
-            // U_{n-1}: U^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]
-            U[cc][j0 + u] = mma<E, true, true>(ue[u], sdO + (j0 + u) * 16, LDV, sQ + cb * 16, LDQ, 0, C);
-            part += piece_dot(sp[u], U[cc][j0 + u]);  // carry into chunk n-1: rowsum(S_{n-1} * U_{n-1})
-          }
+        for (int u = 0; u < KU; ++u) {
+          sp[u] = Sp[j0 + u];
+          ue[u] = U[j0 + u];
         }
-        part = sum_over_g4(part);
-        if (g4 == 0) sCarry[par ^ 1][cb * 16 + n16] = part;
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
-          const int t = tT * 16 + n16;  // the token of this lane's column (t for dq, s for dk)
-          // dq^T[c][t] += sum_s Kbar^T[c][s] dA[t][s];  dk^T[c][s] += sum_t Qbar^T[c][t] dA^T[s][t]
-          const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
-          const f32x4 q_ = mma<E, true, true>(aq[tT], sK + cb * 16, LDQ, sdAT + tT * 16, LDT, 0, ke);
-          const f32x4 k_ = mma<E, true, false>(ak[tT], sQ + cb * 16, LDQ, sdAT + tT * 16 * LDT, LDT,
-                                               (tT * 16 / KS) * KS, C);
-          const f32x4 lam4 = load4(sLam + t * LDQ + cb * 16 + 4 * g4);
-          const f32x4 qb4 = load4(sQ + t * LDQ + cb * 16 + 4 * g4);
-          const f32x4 kb4 = load4(sK + t * LDQ + cb * 16 + 4 * g4);
-          const long go = (t0 + t) * DK + cb * 16 + 4 * g4;
-          store4(dq + go, q_ * lam4);
-          store4(dk + go, k_ / lam4);
-          xr[cc][tT] = qb4 * q_ - kb4 * k_;  // q dq - k dk
+          const int t = tT * 16 + n16;
+          aq[tT] = mma_regX_e<E, KU>(aq[tT], sp, sdO + t * LDV + j0 * 16);
+          ak[tT] = mma_regX<E, KU>(ak[tT], ue, sV + t * LDV + j0 * 16);
         }
       }
-    }
-    __syncthreads();  // V is dead: its space takes x
+      // carry into this chunk, in the lane layout of dq^T: c = 16cb + 4g4 + i
+      float cin[4];
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int cb = w + cc * NW;
-      if (cb < NCB)
+      for (int i = 0; i < 4; ++i) cin[i] = __shfl(carry, (l & ~15) | (4 * g4 + i));
+      f32x4 xr[NTT];  // q dq - k dk at t = 16tT + n16, c = 16cb + 4g4 + i
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) store4(sX + (tT * 16 + n16) * LDX + cb * 16 + 4 * g4, xr[cc][tT]);
-    }
-    __syncthreads();
-    // ---- (4) dg: in-chunk reverse running sum of q dq - k dk plus the exact carry ----
-    if (!krole) {
-      float xs[4][8], suf[8];
+      for (int tT = 0; tT < NTT; ++tT) {
+        const int t = tT * 16 + n16;
+        // + sum_s Kbar^T[c][s] dA[t][s];  + sum_t Qbar^T[c][t] dA^T[s][t]
+        const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
+        const f32x4 q_ = mma<E, true, true>(aq[tT], sK + cb * 16, LDQ, sdAT + tT * 16, LDT, 0, ke);
+        const f32x4 k_ = mma<E, true, false>(ak[tT], sQ + cb * 16, LDQ, sdAT + tT * 16 * LDT, LDT,
+                                             (tT * 16 / KS) * KS, C);
+        const f32x4 lam4 = load4(sLam + t * LDQ + cb * 16 + 4 * g4);
+        const f32x4 qb4 = load4(sQ + t * LDQ + cb * 16 + 4 * g4);
+        const f32x4 kb4 = load4(sK + t * LDQ + cb * 16 + 4 * g4);
+        f32x4 rl;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (has_item) load8(sX + (tg * 4 + r) * LDX + cg * 8, xs[r]);
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xs[r][e] = 0.f;
+        for (int i = 0; i < 4; ++i) rl[i] = __builtin_amdgcn_rcpf(lam4[i]);
+        const long go = (t0 + t) * DK + cb * 16 + 4 * g4;
+        store4(dq + go, q_ * lam4);
+        store4(dk + go, k_ * rl);
+        xr[tT] = qb4 * q_ - kb4 * k_;
       }
+      // dg[t][c] = sum_{t' >= t in the chunk} xr[t'][c] + carry[c]: suffix sums over the 16 tokens of
+      // each row block (one DPP row: the lanes n16 of one g4), then over the later row blocks
+      f32x4 later;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float run = 0.f;
+      for (int i = 0; i < 4; ++i) later[i] = cin[i];
 #pragma unroll
-        for (int r = 3; r >= 0; --r) {
-          run += xs[r][e];
-          xs[r][e] = run;
+      for (int tT = NTT - 1; tT >= 0; --tT) {
+        f32x4 d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float suf = seg_scan_rev_incl<16>(xr[tT][i]);
+          d[i] = suf + later[i];
+          later[i] += row_first(suf);
         }
-        const float incl = seg_scan_rev_incl<NTG>(run);
-        suf[e] = seg_next<NTG>(incl) + (has_item ? sCarry[par][cg * 8 + e] : 0.f);
+        store4(dg + (t0 + tT * 16 + n16) * DK + cb * 16 + 4 * g4, d);
       }
-      if (has_item)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float outv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) outv[e] = xs[r][e] + suf[e];
-          store8(dg + (t0 + tg * 4 + r) * DK + cg * 8, outv);
-        }
     }
-    __syncthreads();
+    __syncthreads();  // V and exp(b) are dead: the U staging area takes their place
+    // ---- (4) dv = A^T dO + Kbar (exp(lam) U), half of d_v at a time; (5) U_{n-1} and the carry ----
+    piece hold[NJB - NJH > 0 ? NJB - NJH : 1];  // exp(lam) U of the later halves, kept across (5)
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      if (urole) {
+#pragma unroll
+        for (int jl = 0; jl < NJH; ++jl) {
+          const int jb = h * NJH + jl;
+          piece x;
+          if (h == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (E)U[jb][i];
+          } else {
+            x = hold[jb - NJH];
+          }
+          *reinterpret_cast<piece*>(sU + (cb * 16 + n16) * LDU + jl * 16 + 4 * g4) = x;
+        }
+        if (h == 0) {
+#pragma unroll
+          for (int jb = NJH; jb < NJB; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hold[jb - NJH][i] = (E)U[jb][i];
+          // (5) U_{n-1}^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]; carry for chunk n-1
+          float part = 0.f;
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) {
+            U[jb] = mma<E, true, true>(U[jb], sdO + jb * 16, LDV, sQ + cb * 16, LDQ, 0, C);
+            part += piece_dot(Sp[jb], U[jb]);  // rowsum(S_{n-1} * U_{n-1})
+          }
+          carry = sum_over_g4(part);
+        }
+      }
+      __syncthreads();
+      // dv^T[j][s] = sum_t dO^T[j][t] A^T[s][t] + sum_c (exp(lam)U)^T[j][c] Kbar[s][c]
+#pragma unroll
+      for (int m = 0; m < NDVT; ++m) {
+        const int idx = w + NW * m;
+        if (idx < NJH * NTT) {
+          const int jl = idx / NTT, sT = idx - (idx / NTT) * NTT;
+          f32x4 acc = mma<E, true, false>(zero4(), sdO + h * DVH + jl * 16, LDV, sAT + sT * 16 * LDT, LDT,
+                                          (sT * 16 / KS) * KS, C);
+          acc = mma<E, true, false>(acc, sU + jl * 16, LDU, sK + sT * 16 * LDQ, LDQ, 0, DK);
+          store4(dv + (t0 + sT * 16 + n16) * DV + h * DVH + jl * 16 + 4 * g4, acc);
+        }
+      }
+      __syncthreads();
+    }
   }
   // D = gradient w.r.t. the state entering the segment (from this segment's outputs)
-  float* dst = a.seg_dstate + (long)unit * SS;
-  const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
+  if (urole) {
+    float* dst = a.seg_dstate + (long)unit * SS;
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
-  for (int cc = 0; cc < CPW; ++cc) {
-    const int cb = w + cc * NW;
-    if (cb < NCB)
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[cc][jb]);
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// dv: one workgroup per unit; wave w owns the 16-column blocks jb = w, w+NW, ... of U[c][j]
-// (all c).
-// ------------------------------------------------------------------------------------------
-template <typename E, int C, int DK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(BwdArgs a, int n_units) {
-  constexpr int NT = NW * 64;
-  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG, RT = NT / 2;
-  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDQ = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
-  constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
-  constexpr int JPW = ceil_div(NJB, NW);
-  constexpr int KS = Mma<E>::KSTEP;
-  static_assert(NI <= RT, "one 4x8 item of q (and one of k) per loader thread");
-
-  __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];    // Qbar [t][c]
-  __shared__ __attribute__((aligned(16))) E sK[C * LDQ];    // Kbar [s][c]
-  __shared__ __attribute__((aligned(16))) E sdO[C * LDV];   // dO   [t][j]
-  __shared__ __attribute__((aligned(16))) E sAT[C * LDT];   // A^T  [s][t], masked
-  __shared__ float sLamE[DK];
-
-  const int unit = blockIdx.x;
-  if (unit >= n_units) return;
-  const E* __restrict__ q = static_cast<const E*>(a.q);
-  const E* __restrict__ k = static_cast<const E*>(a.k);
-  const E* __restrict__ dO = static_cast<const E*>(a.dO);
-  const float* __restrict__ g = a.g;
-  E* __restrict__ dv = static_cast<E*>(a.dv);
-  const int L = a.T / a.P;
-  const int nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool krole = tid >= RT;
-  const int rt = krole ? tid - RT : tid;
-  const bool has_item = rt < NI;
-  const int tg = rt % NTG, cg = rt / NTG;
-  const E* __restrict__ xsrc = krole ? k : q;
-
-  Rows4x8<float> pg;
-  Rows4x8<E> px;
-  Vec8<E> pd[VPT];
-  auto prefetch = [&](int n) {
-    const long t0 = tok0 + (long)n * C;
-    if (has_item) {
-      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
-      px.load(xsrc + (t0 + tg * 4) * DK + cg * 8, DK);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int pc = tid + NT * i;
-      if (NVP % NT == 0 || pc < NVP) pd[i].load(dO + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
-    }
-  };
-
-  f32x4 U[JPW][NKB];  // U[jj][kb][i] = U[16kb + 4g4 + i][16jb + n16]
-#pragma unroll
-  for (int jj = 0; jj < JPW; ++jj)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) U[jj][kb] = zero4();
-
-  prefetch(nchunks - 1);
-  for (int n = nchunks - 1; n >= 0; --n) {
-    const long t0 = tok0 + (long)n * C;
-    {
-      float b[4][8], lam[8];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
-      if (has_item) {
-        if (!krole) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = px.at(r, e) * __expf(b[r][e]);
-            store8(sQ + (tg * 4 + r) * LDQ + cg * 8, x);
-          }
-          if (tg == 0)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sLamE[cg * 8 + e] = __expf(lam[e]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = px.at(r, e) * __expf(-b[r][e]);
-            store8(sK + (tg * 4 + r) * LDQ + cg * 8, x);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int pc = tid + NT * i;
-        if (NVP % NT == 0 || pc < NVP) pd[i].store(sdO + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (n > 0) prefetch(n - 1);
-    __syncthreads();
-    // A[t][s] = Qbar[t] . Kbar[s], stored transposed as A^T[s][t] for t >= s
-    for (int idx = w; idx < NTT * NTT; idx += NW) {
-      const int tT = idx / NTT, sT = idx - (idx / NTT) * NTT;
-      f32x4 acc = zero4();
-      if (sT <= tT) acc = mma<E, false, false>(acc, sQ + tT * 16 * LDQ, LDQ, sK + sT * 16 * LDQ, LDQ, 0, DK);
-      const int s = sT * 16 + n16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tT * 16 + 4 * g4 + i < s) acc[i] = 0.f;
-      store4(sAT + s * LDT + tT * 16 + 4 * g4, acc);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * NW;
-      if (jb < NJB) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) U[jj][kb][i] *= sLamE[kb * 16 + 4 * g4 + i];  // exp(lam) U
-        // dv^T[j][s] = sum_t dO^T[j][t] A^T[s][t] + sum_c (exp(lam)U)^T[j][c] Kbar[s][c]
-#pragma unroll
-        for (int sT = 0; sT < NTT; ++sT) {
-          f32x4 acc = mma<E, true, false>(zero4(), sdO + jb * 16, LDV, sAT + sT * 16 * LDT, LDT,
-                                          (sT * 16 / KS) * KS, C);
-          acc = mma_regX<E, NKB>(acc, U[jj], sK + (sT * 16 + n16) * LDQ);
-          store4(dv + (t0 + sT * 16 + n16) * DV + jb * 16 + 4 * g4, acc);
-        }
-        // U[c][j] += sum_t Qbar^T[c][t] dO^T[j][t]
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          U[jj][kb] = mma<E, true, true>(U[jj][kb], sQ + kb * 16, LDQ, sdO + jb * 16, LDV, 0, C);
-      }
-    }
-    __syncthreads();
+    for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[jb]);
   }
 }
 
 template <typename E, int C, int DK, int DV>
-struct BwdDqkLauncher {
+struct BwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
     const int n_units = a.BH * a.P;
-    hipLaunchKernelGGL((bwd_dqk_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
-    return hipGetLastError();
-  }
-};
-template <typename E, int C, int DK, int DV>
-struct BwdDvLauncher {
-  static hipError_t run(const void* pa, hipStream_t s) {
-    const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
-    const int n_units = a.BH * a.P;
-    hipLaunchKernelGGL((bwd_dv_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    hipLaunchKernelGGL((bwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
 
-launch_fn lookup_bwd_dqk(int dtype, int chunk, int dk, int dv) { return lookup_cdd<BwdDqkLauncher>(dtype, chunk, dk, dv); }
-launch_fn lookup_bwd_dv(int dtype, int chunk, int dk, int dv) { return lookup_cdd<BwdDvLauncher>(dtype, chunk, dk, dv); }
+launch_fn lookup_bwd(int dtype, int chunk, int dk, int dv) { return lookup_cdd<BwdLauncher>(dtype, chunk, dk, dv); }
 
 }  // namespace gla

@@ -61,8 +61,7 @@ inline int tile_of(int d) { return d < 64 ? d : 64; }
 // dtype: 0 = f32, 1 = bf16.
 launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv);
-launch_fn lookup_bwd_dqk(int dtype, int chunk, int dk, int dv);
-launch_fn lookup_bwd_dv(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_bwd(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_bwd_dk(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_bwd_dv(int dtype, int chunk, int dk, int dv);
 
