@@ -29,18 +29,18 @@ __device__ __forceinline__ float row_first(float x) {
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int NTG = C / 4, NCG = DK / 4, NI = NTG * NCG;  // 4-token x 4-channel items of q, k, g
+  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of q, k, g: RI tokens x 4 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
   constexpr int LDV = DV + kPad, LDQ = DK + kPad, LDT = C + kPad;
   constexpr int DVH = DV < 128 ? DV : 128, NH = DV / DVH;  // d_v columns of U staged at a time
-  constexpr int LDU = DVH + kPadT;
+  constexpr int LDU = DVH + kPad;
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NJH = DVH / 16;
   constexpr int KS = Mma<E>::KSTEP;
   constexpr int KU = sizeof(E) == 2 ? 2 : 1;  // 16-wide d_v blocks per k-step of the MFMA
-  constexpr int NDVT = ceil_div(NJH * NTT, NW);  // dv tiles per wave per half
-  static_assert(NI <= NT, "one 4x4 item of q, k and g per thread");
+  static_assert(NI <= NT, "one strided item of q, k and g per thread");
   static_assert(NCB <= NW, "one 16-row block of U^T per wave");
   static_assert(NJB % KU == 0, "d_v blocks pair up for bf16");
+  static_assert(NW % NTT == 0, "the waves split evenly over the chunk's 16-token blocks");
   typedef typename Piece4<E>::type piece;
 
   // LDS.  sV and sLam are dead once dq / dk are done; the U staging area then reuses them.
@@ -82,16 +82,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   const int cb = w;                   // this wave's 16-row block of U^T (waves w >= NCB hold none)
   const bool urole = cb < NCB;
 
-  // item of a thread: tokens 4tg..4tg+3, channels 4cg..4cg+3 (the NTG items of one channel group
-  // lie on consecutive lanes)
-  Rows4x4<float> pg;
-  Rows4x4<E> pq, pk;
+  // item of a thread: tokens 16i + n16 (i < RI), channels 4cg..4cg+3 with cg = tid / 16, so the 16
+  // lanes of a row hold 16 consecutive tokens of one channel group (their LDS writes hit 16
+  // consecutive rows: no bank conflicts)
+  RowsRx4<float, RI> pg;
+  RowsRx4<E, RI> pq, pk;
   auto prefetch = [&](int n, int tid) {
     if (NI == NT || tid < NI) {
-      const long off = (tok0 + (long)n * C + (tid % NTG) * 4) * DK + (tid / NTG) * 4;
-      pg.load(g + off, DK);
-      pq.load(q + off, DK);
-      pk.load(k + off, DK);
+      const long off = (tok0 + (long)n * C + (tid & 15)) * DK + (tid >> 4) * 4;
+      pg.load(g + off, 16 * DK);
+      pq.load(q + off, 16 * DK);
+      pk.load(k + off, 16 * DK);
     }
   };
 
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     const bool has_item = NI == NT || tid < NI;
-    const int tg = tid % NTG, cg = tid / NTG;
+    const int cg = tid >> 4;
     // this chunk's V and dO
     Vec8<E> pv[VPT], pd[VPT];
 #pragma unroll
@@ -119,11 +120,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     }
     // ---- (1) gate prefix sums, Qbar, Kbar, exp(b); V, dO -> LDS ----
     {
-      float b[4][4], lam[4];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      float b[RI][4], lam[4];
+      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
       if (has_item) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < RI; ++r) {
           f32x4 xq, xk, eb4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -131,12 +132,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
             xq[e] = pq.at(r, e) * eb4[e];
             xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb4[e]);  // exp(-b) to one ulp
           }
-          const int off = (tg * 4 + r) * LDQ + cg * 4;
+          const int off = (16 * r + n16) * LDQ + cg * 4;
           store4(sQ + off, xq);
           store4(sK + off, xk);
           store4(sLam + off, eb4);
         }
-        if (tg == 0) {
+        if (n16 == 0) {
           f32x4 el;
 #pragma unroll
           for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
@@ -218,15 +219,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       float cin[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) cin[i] = __shfl(carry, (l & ~15) | (4 * g4 + i));
+      // + sum_s Kbar^T[c][s] dA[t][s] (s <= t);  + sum_t Qbar^T[c][t] dA^T[s][t] (t >= s): the Kbar^T and
+      // Qbar^T fragments of this wave's rows are read once per k step for all row blocks
+#pragma unroll
+      for (int ks = 0; ks < C / KS; ++ks) {
+        const typename Mma<E>::frag fk = frag_ld<E, true>(sK + cb * 16, LDQ, ks * KS);
+        const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
+#pragma unroll
+        for (int tT = 0; tT < NTT; ++tT) {
+          if (ks * KS < (tT + 1) * 16) aq[tT] = Mma<E>::mma(fk, frag_ld<E, true>(sdAT + tT * 16, LDT, ks * KS), aq[tT]);
+          if ((ks + 1) * KS > tT * 16) ak[tT] = Mma<E>::mma(fq, frag_ld<E, false>(sdAT + tT * 16 * LDT, LDT, ks * KS), ak[tT]);
+        }
+      }
       f32x4 xr[NTT];  // q dq - k dk at t = 16tT + n16, c = 16cb + 4g4 + i
 #pragma unroll
       for (int tT = 0; tT < NTT; ++tT) {
         const int t = tT * 16 + n16;
-        // + sum_s Kbar^T[c][s] dA[t][s];  + sum_t Qbar^T[c][t] dA^T[s][t]
-        const int ke = round_up((tT + 1) * 16, KS) < C ? round_up((tT + 1) * 16, KS) : C;
-        const f32x4 q_ = mma<E, true, true>(aq[tT], sK + cb * 16, LDQ, sdAT + tT * 16, LDT, 0, ke);
-        const f32x4 k_ = mma<E, true, false>(ak[tT], sQ + cb * 16, LDQ, sdAT + tT * 16 * LDT, LDT,
-                                             (tT * 16 / KS) * KS, C);
+        const f32x4 q_ = aq[tT], k_ = ak[tT];
         const f32x4 lam4 = load4(sLam + t * LDQ + cb * 16 + 4 * g4);
         const f32x4 qb4 = load4(sQ + t * LDQ + cb * 16 + 4 * g4);
         const f32x4 kb4 = load4(sK + t * LDQ + cb * 16 + 4 * g4);
@@ -279,25 +288,39 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) hold[jb - NJH][i] = (E)U[jb][i];
           // (5) U_{n-1}^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]; carry for chunk n-1
+#pragma unroll
+          for (int ks = 0; ks < C / KS; ++ks) {
+            const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+              U[jb] = Mma<E>::mma(frag_ld<E, true>(sdO + jb * 16, LDV, ks * KS), fq, U[jb]);
+          }
           float part = 0.f;
 #pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) {
-            U[jb] = mma<E, true, true>(U[jb], sdO + jb * 16, LDV, sQ + cb * 16, LDQ, 0, C);
-            part += piece_dot(Sp[jb], U[jb]);  // rowsum(S_{n-1} * U_{n-1})
-          }
+          for (int jb = 0; jb < NJB; ++jb) part += piece_dot(Sp[jb], U[jb]);  // rowsum(S_{n-1} * U_{n-1})
           carry = sum_over_g4(part);
         }
       }
       __syncthreads();
-      // dv^T[j][s] = sum_t dO^T[j][t] A^T[s][t] + sum_c (exp(lam)U)^T[j][c] Kbar[s][c]
+      // dv^T[j][s] = sum_t dO^T[j][t] A^T[s][t] + sum_c (exp(lam)U)^T[j][c] Kbar[s][c].  This wave takes
+      // the row block sT = w % NTT and the column blocks jl = w / NTT, w / NTT + NW / NTT, ...; its
+      // A^T and Kbar fragments are read once for all of them.
+      {
+        const int sT = w % NTT;
+        typename Mma<E>::frag fa[C / KS], fkb[DK / KS];
 #pragma unroll
-      for (int m = 0; m < NDVT; ++m) {
-        const int idx = w + NW * m;
-        if (idx < NJH * NTT) {
-          const int jl = idx / NTT, sT = idx - (idx / NTT) * NTT;
-          f32x4 acc = mma<E, true, false>(zero4(), sdO + h * DVH + jl * 16, LDV, sAT + sT * 16 * LDT, LDT,
-                                          (sT * 16 / KS) * KS, C);
-          acc = mma<E, true, false>(acc, sU + jl * 16, LDU, sK + sT * 16 * LDQ, LDQ, 0, DK);
+        for (int ks = 0; ks < C / KS; ++ks)
+          if ((ks + 1) * KS > sT * 16) fa[ks] = frag_ld<E, false>(sAT + sT * 16 * LDT, LDT, ks * KS);  // t >= s only
+#pragma unroll
+        for (int ks = 0; ks < DK / KS; ++ks) fkb[ks] = frag_ld<E, false>(sK + sT * 16 * LDQ, LDQ, ks * KS);
+        for (int jl = w / NTT; jl < NJH; jl += NW / NTT) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < C / KS; ++ks)
+            if ((ks + 1) * KS > sT * 16)
+              acc = Mma<E>::mma(frag_ld<E, true>(sdO + h * DVH + jl * 16, LDV, ks * KS), fa[ks], acc);
+#pragma unroll
+          for (int ks = 0; ks < DK / KS; ++ks) acc = Mma<E>::mma(frag_ld<E, true>(sU + jl * 16, LDU, ks * KS), fkb[ks], acc);
           store4(dv + (t0 + sT * 16 + n16) * DV + h * DVH + jl * 16 + 4 * g4, acc);
         }
       }

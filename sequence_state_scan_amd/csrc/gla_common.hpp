@@ -26,10 +26,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kWaves = 4;
-constexpr int kPad = 8;        // LDS row padding in elements (keeps 16-byte alignment)
-// Row padding of tiles that are only read with the transposing load: the 4 rows one 16-lane
-// group reads then start 16 elements (8 banks) apart and cover disjoint banks.
-constexpr int kPadT = 16;
+// LDS row padding in elements (keeps 16-byte alignment).  A row of 2^m + 8 elements puts 16
+// consecutive rows 4 banks apart: row-wise 8- and 16-byte accesses of 16 lanes to 16 rows, and the
+// transposing reads, run without bank conflicts (measured on gfx950 with the LDS conflict counter).
+constexpr int kPad = 8;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -481,6 +481,46 @@ template <> struct Rows4x4<float> {
   }
   __device__ __forceinline__ float at(int i, int e) const { return r[i][e]; }
 };
+
+// R rows of 4 consecutive elements of a row-major tensor (rows ld apart), held in registers for
+// prefetching.  With ld = 16 rows of the tensor this is a "strided item": lane n16 of a 16-lane row
+// holds tokens n16, n16 + 16, ... of a chunk, so the 16 lanes of a row cover 16 consecutive tokens.
+template <typename E, int R> struct RowsRx4;
+template <int R> struct RowsRx4<bf16, R> {
+  bf16x4 r[R];
+  __device__ __forceinline__ void load(const bf16* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) r[i] = *reinterpret_cast<const bf16x4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float at(int i, int e) const { return (float)r[i][e]; }
+};
+template <int R> struct RowsRx4<float, R> {
+  f32x4 r[R];
+  __device__ __forceinline__ void load(const float* p, long ld) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) r[i] = *reinterpret_cast<const f32x4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float at(int i, int e) const { return r[i][e]; }
+};
+
+// Gate prefix sums of a strided item (tokens 16i + n16 of the chunk, i < R; 4 channels), the 16
+// lanes of a row holding 16 consecutive tokens: on return b[i][e] is the in-chunk inclusive running
+// sum of g at token 16i + n16 and lam[e] the chunk total.  One DPP row scan per 16-token block.
+template <int R, class Rows>
+__device__ __forceinline__ void chunk_gate_prefix_strided(const Rows& pg, bool has_item, float (&b)[R][4],
+                                                          float (&lam)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float incl = seg_scan_incl<16>(has_item ? pg.at(i, e) : 0.f);
+      b[i][e] = run + incl;
+      run += seg_last<16>(incl);
+    }
+    lam[e] = run;
+  }
+}
 
 // Gate prefix sums of one 4-token x NE-channel item per lane (Rows: Rows4x8<float> or
 // Rows4x4<float>), the items of one channel group lying on NTG consecutive lanes in token order:

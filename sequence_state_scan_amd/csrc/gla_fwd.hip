@@ -30,13 +30,13 @@ namespace gla {
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int NTG = C / 4, NCG = DK / 4, NI = NTG * NCG;
+  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items: RI tokens x 4 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDQ = DK + kPad, LDKT = DK + kPadT, LDV = DV + kPadT, LDT = C + kPad;
+  constexpr int LDQ = DK + kPad, LDKT = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   constexpr int KS = Mma<E>::KSTEP, NKS = C / KS;
-  static_assert(NI <= NT, "one 4x4 item of q, k and g per thread");
+  static_assert(NI <= NT, "one strided item of q, k and g per thread");
   static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
 
   __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
@@ -63,18 +63,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const s16x4 ident = identity_b_operand();
   typedef typename Mma<E>::frag frag;
 
-  // item of a thread: tokens 4tg..4tg+3, channels 4cg..4cg+3 (tg = tid % NTG: the NTG items of one
-  // channel group lie on consecutive lanes)
-  Rows4x4<float> pg;
-  Rows4x4<E> pq, pk;
+  // item of a thread: tokens 16i + n16 (i < RI), channels 4cg..4cg+3 with cg = tid / 16, so the 16
+  // lanes of a row hold 16 consecutive tokens of one channel group (their LDS writes hit 16
+  // consecutive rows: no bank conflicts)
+  RowsRx4<float, RI> pg;
+  RowsRx4<E, RI> pq, pk;
   Vec8<E> pv[VPT];
   auto prefetch = [&](int n, int tid) {
     const long t0 = tok0 + (long)n * C;
     if (NI == NT || tid < NI) {
-      const long off = (t0 + (tid % NTG) * 4) * DK + (tid / NTG) * 4;
-      pg.load(g + off, DK);
-      pq.load(q + off, DK);
-      pk.load(k + off, DK);
+      const long off = (t0 + (tid & 15)) * DK + (tid >> 4) * 4;
+      pg.load(g + off, 16 * DK);
+      pq.load(q + off, 16 * DK);
+      pk.load(k + off, 16 * DK);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -95,17 +96,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     const bool has_item = NI == NT || tid < NI;
-    const int tg = tid % NTG, cg = tid / NTG;
+    const int cg = tid >> 4;
     // ---- (1) gate prefix sums, Qbar, Kbar, Ktil, V -> LDS; request the next chunk ----
     {
-      float b[4][4], lam[4];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
+      float b[RI][4], lam[4];
+      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
       if (has_item) {
         f32x4 el;
 #pragma unroll
         for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < RI; ++r) {
           f32x4 xq, xk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -113,12 +114,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
             xq[e] = pq.at(r, e) * eb;
             xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb);  // exp(-b) to one ulp
           }
-          const int off = (tg * 4 + r) * LDQ + cg * 4;
-          store4(sQ + off, xq);
-          store4(sK + off, xk);
-          store4(sKt + (tg * 4 + r) * LDKT + cg * 4, xk * el);
+          const int row = 16 * r + n16;
+          store4(sQ + row * LDQ + cg * 4, xq);
+          store4(sK + row * LDQ + cg * 4, xk);
+          store4(sKt + row * LDKT + cg * 4, xk * el);
         }
-        if (tg == 0) {
+        if (n16 == 0) {
           store4(sLamE + cg * 4, el);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ldsum[e] += lam[e];
@@ -236,8 +237,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
   }
   const int tid = threadIdx.x;
-  if ((NI == NT || tid < NI) && tid % NTG == 0) store4(a.seg_logdecay + (long)unit * DK + (tid / NTG) * 4,
-                                                      f32x4{ldsum[0], ldsum[1], ldsum[2], ldsum[3]});
+  if ((NI == NT || tid < NI) && (tid & 15) == 0)
+    store4(a.seg_logdecay + (long)unit * DK + (tid >> 4) * 4, f32x4{ldsum[0], ldsum[1], ldsum[2], ldsum[3]});
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
