@@ -96,10 +96,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     }
   };
 
+  // V and dO of a chunk, requested one chunk ahead (issued once the previous chunk's dq / dk are done)
+  Vec8<E> pv[VPT], pd[VPT];
+  auto prefetch_vd = [&](int n, int tid) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) {
+        const long off = (tok0 + (long)n * C + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8;
+        pv[i].load(v + off);
+        pd[i].load(dO + off);
+      }
+    }
+  };
+
   f32x4 U[NJB];  // U[jb][i] = U[16cb + n16][16jb + 4g4 + i]
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
-  float carry = 0.f;  // rowsum(S_n * U_n) for c = 16cb + n16: nothing after the last chunk
+  // carry into the current chunk: rowsum(S_n * U_n) for c = 16cb + 4g4 + i (nothing after the last chunk)
+  float cin[4] = {0.f, 0.f, 0.f, 0.f};
 
   prefetch(nchunks - 1, threadIdx.x);
   for (int n = nchunks - 1; n >= 0; --n) {
@@ -107,17 +122,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     const bool has_item = NI == NT || tid < NI;
     const int cg = tid >> 4;
-    // this chunk's V and dO
-    Vec8<E> pv[VPT], pd[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int pc = tid + NT * i;
-      if (NVP % NT == 0 || pc < NVP) {
-        const long off = (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8;
-        pv[i].load(v + off);
-        pd[i].load(dO + off);
-      }
-    }
+    prefetch_vd(n, tid);  // this chunk's V and dO
     // ---- (1) gate prefix sums, Qbar, Kbar, exp(b); V, dO -> LDS ----
     {
       float b[RI][4], lam[4];
@@ -193,8 +198,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     // ---- (3) exp(lam) U, dq, dk, dg ----
     if (urole) {
       const float le = sLamE[cb * 16 + n16];
+      float part = 0.f;  // rowsum(S_{n-1} * exp(lam) U_n), c = 16cb + n16
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) U[jb] *= le;  // exp(lam) U_n
+      for (int jb = 0; jb < NJB; ++jb) {
+        U[jb] *= le;  // exp(lam) U_n
+        part += piece_dot(Sp[jb], U[jb]);
+      }
+      part = sum_over_g4(part);
       // dq^T[c][t] = sum_j S[c][j] dO[t][j] + ...;  dk^T[c][s] = sum_j (exp(lam)U)[c][j] V[s][j] + ...
       f32x4 aq[NTT], ak[NTT];
 #pragma unroll
@@ -215,10 +225,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
           ak[tT] = mma_regX<E, KU>(ak[tT], ue, sV + t * LDV + j0 * 16);
         }
       }
-      // carry into this chunk, in the lane layout of dq^T: c = 16cb + 4g4 + i
-      float cin[4];
+      // the carry into chunk n-1, rowsum(S_{n-1} * U_{n-1}) with U_{n-1} = exp(lam) U_n + Qbar^T dO, is
+      // rowsum(S_{n-1} * exp(lam) U_n) + sum_t Qbar[t] * (dO_t S_{n-1}^T): the second term uses the
+      // inter-chunk part of dq^T before the intra-chunk part is added
+      f32x4 qs = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cin[i] = __shfl(carry, (l & ~15) | (4 * g4 + i));
+      for (int tT = 0; tT < NTT; ++tT) qs += load4(sQ + (tT * 16 + n16) * LDQ + cb * 16 + 4 * g4) * aq[tT];
       // + sum_s Kbar^T[c][s] dA[t][s] (s <= t);  + sum_t Qbar^T[c][t] dA^T[s][t] (t >= s): the Kbar^T and
       // Qbar^T fragments of this wave's rows are read once per k step for all row blocks
 #pragma unroll
@@ -263,31 +275,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         }
         store4(dg + (t0 + tT * 16 + n16) * DK + cb * 16 + 4 * g4, d);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i)) + seg_last<16>(seg_scan_incl<16>(qs[i]));
     }
     __syncthreads();  // V and exp(b) are dead: the U staging area takes their place
-    // ---- (4) dv = A^T dO + Kbar (exp(lam) U), half of d_v at a time; (5) U_{n-1} and the carry ----
-    piece hold[NJB - NJH > 0 ? NJB - NJH : 1];  // exp(lam) U of the later halves, kept across (5)
+    // ---- (4) dv = A^T dO + Kbar (exp(lam) U), half of d_v at a time; (5) U_{n-1} once the last half
+    // of exp(lam) U is staged ----
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       if (urole) {
 #pragma unroll
         for (int jl = 0; jl < NJH; ++jl) {
-          const int jb = h * NJH + jl;
           piece x;
-          if (h == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (E)U[jb][i];
-          } else {
-            x = hold[jb - NJH];
-          }
+          for (int i = 0; i < 4; ++i) x[i] = (E)U[h * NJH + jl][i];
           *reinterpret_cast<piece*>(sU + (cb * 16 + n16) * LDU + jl * 16 + 4 * g4) = x;
         }
-        if (h == 0) {
-#pragma unroll
-          for (int jb = NJH; jb < NJB; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hold[jb - NJH][i] = (E)U[jb][i];
-          // (5) U_{n-1}^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]; carry for chunk n-1
+        if (h == NH - 1) {
+          // (5) U_{n-1}^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]
 #pragma unroll
           for (int ks = 0; ks < C / KS; ++ks) {
             const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
@@ -295,10 +301,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
             for (int jb = 0; jb < NJB; ++jb)
               U[jb] = Mma<E>::mma(frag_ld<E, true>(sdO + jb * 16, LDV, ks * KS), fq, U[jb]);
           }
-          float part = 0.f;
-#pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) part += piece_dot(Sp[jb], U[jb]);  // rowsum(S_{n-1} * U_{n-1})
-          carry = sum_over_g4(part);
         }
       }
       __syncthreads();
