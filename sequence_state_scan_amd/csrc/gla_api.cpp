@@ -43,7 +43,7 @@ bool shape_listed(int dtype, int dk, int dv, int chunk) {
 }
 
 struct Kernels {
-  gla::launch_fn fwd, corr_fwd, bwd, corr_dk, corr_dv;
+  gla::launch_fn fwd, corr_fwd, bwd, corr_bwd;
 };
 
 bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
@@ -51,9 +51,8 @@ bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
   k->fwd = gla::lookup_fwd_local(dtype, chunk, dk, dv);
   k->corr_fwd = gla::lookup_correct_fwd(dtype, chunk, dk, dv);
   k->bwd = gla::lookup_bwd(dtype, chunk, dk, dv);
-  k->corr_dk = gla::lookup_correct_bwd_dk(dtype, chunk, dk, dv);
-  k->corr_dv = gla::lookup_correct_bwd_dv(dtype, chunk, dk, dv);
-  return k->fwd && k->corr_fwd && k->bwd && k->corr_dk && k->corr_dv;
+  k->corr_bwd = gla::lookup_correct_bwd(dtype, chunk, dk, dv);
+  return k->fwd && k->corr_fwd && k->bwd && k->corr_bwd;
 }
 
 // Shape checks shared by the chunked entry points.
@@ -153,9 +152,7 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
   if (!k || !v || !g || !seg_in || !seg_grad || !chunk_states || !dk_ || !dv_ || !dg)
     return fail(GLA_ERR_INVALID_ARG,
                 "%s(GLA_BWD): k, v, g, seg_in, seg_grad, chunk_states, dk, dv and dg must be non-null", fn);
-  hipError_t e = kern.corr_dk(&a, s);
-  if (e == hipSuccess) e = kern.corr_dv(&a, s);
-  return launched(fn, e);
+  return launched(fn, kern.corr_bwd(&a, s));
 }
 
 gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* do_,

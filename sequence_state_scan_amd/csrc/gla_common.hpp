@@ -311,6 +311,12 @@ __device__ __forceinline__ f32x4 mma_regX_e(f32x4 acc, const typename Piece4<E>:
 }
 
 __device__ __forceinline__ float piece_dot(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+// bf16 pieces on both sides: two v_dot2_f32_bf16 (bf16 products are exact in fp32, summed in fp32).
+__device__ __forceinline__ float piece_dot(bf16x4 a, bf16x4 b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 alo = {a[0], a[1]}, ahi = {a[2], a[3]}, blo = {b[0], b[1]}, bhi = {b[2], b[3]};
+  return __builtin_amdgcn_fdot2_f32_bf16(ahi, bhi, __builtin_amdgcn_fdot2_f32_bf16(alo, blo, 0.f, false), false);
+}
 __device__ __forceinline__ float piece_dot(bf16x4 a, f32x4 b) {
   return (float)a[0] * b[0] + (float)a[1] * b[1] + (float)a[2] * b[2] + (float)a[3] * b[3];
 }

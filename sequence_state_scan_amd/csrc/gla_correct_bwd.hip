@@ -14,33 +14,36 @@
 
 namespace gla {
 
-// dk and dg: one workgroup per (unit, DKT-wide slice of d_k).  G[c][:] for the slice sits in
-// registers (wave w owns the 16-row blocks cb = w, w+4, ...) and feeds the MFMA A operand.  Every
-// global read of a chunk is issued before its writes (one memory round trip per chunk).
-template <typename E, int C, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, int n_units) {
-  constexpr int DKT = DK < 64 ? DK : 64, NT = DK / DKT;
-  constexpr int NTG = C / 4, NCG = DKT / 8, NI = NTG * NCG;
-  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, kThreads);
-  constexpr int LDV = DV + kPad, LDL = DKT + 4;
-  constexpr int NJB = DV / 16, NCB = DKT / 16, NTT = C / 16;
-  constexpr int CPW = ceil_div(NCB, kWaves);
-  static_assert(NI <= kThreads, "one 4x8 item per thread");
+// One workgroup of NW waves per unit.  G is constant over the segment and sits in registers,
+// rounded to the element type (the MFMA operand type), in two lane layouts: wave w holds the rows
+// c = 16w.. of G (all of d_v) for dk and dg, which contract G over d_v, and the columns
+// j = 16w.., 16(w + NW).. of G (all of d_k) for dv, which contracts it over d_k.  Per live chunk,
+// every read of g, k, V and of the outputs to update is issued first; the global state before the
+// chunk (for R_n) is read after the chunk is known to be live.
+template <typename E, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_units) {
+  constexpr int NT = NW * 64;
+  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and k
+  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
+  constexpr int LDV = DV + kPad, LDQ = DK + kPad;
+  constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NKB = DK / 16;
+  constexpr int JPW = ceil_div(NJB, NW);
+  static_assert(NI <= NT, "one strided item of g and k per thread");
+  static_assert(NCB <= NW, "one 16-row block of G per wave");
+  static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
   typedef typename Piece4<E>::type piece;
 
-  __shared__ __attribute__((aligned(16))) E sV[C * LDV];      // V [t][j]
-  __shared__ __attribute__((aligned(16))) float sE[C * LDL];  // exp(r_t) [t][c]
-  __shared__ __attribute__((aligned(16))) float sKD[C * LDL]; // k * delta-dk [t][c]
-  __shared__ float sR[DKT];                                   // R_n
+  __shared__ __attribute__((aligned(16))) E sV[C * LDV];   // V [t][j]
+  __shared__ __attribute__((aligned(16))) E sEK[C * LDQ];  // exp(r_t) k_t [t][c]
 
-  int unit, tile;
-  xcd_map(blockIdx.x, NT, unit, tile);
+  const int unit = blockIdx.x;
   if (unit >= n_units) return;
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
   const E* __restrict__ cst = static_cast<const E*>(a.chunk_states);
   const float* __restrict__ g = a.g;
   E* __restrict__ dk = static_cast<E*>(a.dk);
+  E* __restrict__ dv = static_cast<E*>(a.dv);
   float* __restrict__ dg = a.dg;
   const int L = a.T / a.P;
   const int nchunks = L / C;
@@ -48,285 +51,169 @@ __global__ __launch_bounds__(kThreads) void correct_bwd_dk_kernel(CorrArgs a, in
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
   constexpr long SS = (long)DK * DV;
-  const int c0 = tile * DKT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  // item of g and dg: tokens 4tg..4tg+3, slice channels 8cg..8cg+7
-  const bool has_item = tid < NI;
-  const int tg = tid % NTG, cg = tid / NTG;
+  const bool krole = w < NCB;            // holds rows 16w.. of G
+  const bool vrole = w < NJB;            // holds columns 16w.. (and 16(w + NW)..) of G
+  // item of a thread: tokens 16r + n16 (r < RI), channels 4cg.. with cg = tid / 16 = 4w + g4: exactly
+  // the (t, c) of the lane's dk accumulators below
+  const bool has_item = NI == NT || tid < NI;
+  const int cg = tid >> 4;
 
-  // G slice: R[cc][jb][i] = G[c0 + 16cb + n16][16jb + 4g4 + i]
+  // G rows: Gr[jb][i] = G[16w + n16][16jb + 4g4 + i];  G columns: Gt[jj][kb][i] = G[16kb + 4g4 + i][16jb + n16]
   const float* gp = a.seg_grad + (long)unit * SS;
-  f32x4 R[CPW][NJB];
+  piece Gr[NJB], Gt[JPW][NKB];
   int nonzero = 0;
 #pragma unroll
-  for (int cc = 0; cc < CPW; ++cc) {
-    const int cb = w + cc * kWaves;
+  for (int jb = 0; jb < NJB; ++jb) {
+    const f32x4 x = krole ? load4(gp + (long)(w * 16 + n16) * DV + jb * 16 + 4 * g4) : zero4();
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      R[cc][jb] = cb < NCB ? load4(gp + (long)(c0 + cb * 16 + n16) * DV + jb * 16 + 4 * g4) : zero4();
+    for (int i = 0; i < 4; ++i) {
+      Gr[jb][i] = (E)x[i];
+      nonzero |= x[i] != 0.f;
+    }
+  }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nonzero |= R[cc][jb][i] != 0.f;
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int jb = w + jj * NW;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 x = vrole ? quad_transpose(load4(gp + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3)))
+                            : zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Gt[jj][kb][i] = (E)x[i];
     }
   }
   if (!__syncthreads_or(nonzero)) return;  // G_p == 0: nothing to add
 
-  float gcarry[8];  // sum of g over the chunks after the current one, up to the segment's end
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gcarry[e] = 0.f;
+  float gcarry[4] = {0.f, 0.f, 0.f, 0.f};  // sum of g over the chunks after the current one
   for (int n = nchunks - 1; n >= 0; --n) {
     const long t0 = tok0 + (long)n * C;
-    // every read of this chunk before its writes: g, V, dk, k and the global state before the
-    // chunk here, dg once the chunk is known to be live
-    Rows4x8<float> pg, pdg;
-    if (has_item) pg.load(g + (t0 + tg * 4) * DK + c0 + cg * 8, DK);
+    // ---- every read of the chunk but the state: g, k, V and the outputs to update ----
+    RowsRx4<float, RI> pg;
+    RowsRx4<E, RI> pk;
+    if (has_item) {
+      const long off = (t0 + n16) * DK + cg * 4;
+      pg.load(g + off, 16 * DK);
+      pk.load(k + off, 16 * DK);
+    }
     Vec8<E> pv[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int pc = tid + kThreads * i;
-      if (NVP % kThreads == 0 || pc < NVP) pv[i].load(v + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pv[i].load(v + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
     }
-    piece dkprev[CPW][NTT], kk[CPW][NTT], Sp[CPW][NJB];
+    piece dkprev[NTT];
+    f32x4 dgprev[NTT];
+    if (krole) {
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int cb = w + cc * kWaves;
-      if (cb < NCB) {
-#pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const long go = (t0 + tT * 16 + n16) * DK + c0 + cb * 16 + 4 * g4;
-          dkprev[cc][tT] = load_piece(dk + go);
-          kk[cc][tT] = load_piece(k + go);
-        }
-        const long roff = (long)(c0 + cb * 16 + n16) * DV + 4 * g4;
-        if (n > 0) {
-#pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) Sp[cc][jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
-        } else {
-#pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) {
-            const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sp[cc][jb][i] = (E)x[i];
-          }
-        }
+      for (int tT = 0; tT < NTT; ++tT) {
+        const long go = (t0 + tT * 16 + n16) * DK + w * 16 + 4 * g4;
+        dkprev[tT] = load_piece(dk + go);
+        dgprev[tT] = load4(dg + go);
       }
     }
-    // exp(r_t), r_t = sum of g over the tokens after t up to the segment's end
-    float lam[8];
+    piece dvprev[JPW][NTT];
+    if (vrole) {
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int sT = 0; sT < NTT; ++sT)
+          dvprev[jj][sT] = load_piece(dv + (t0 + sT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4);
+    }
+    // ---- exp(r_t), r_t = sum of g over the tokens after t up to the segment's end; exp(r) k -> LDS ----
+    float er[RI][4], lam[4];
     int live = 0;
     {
-      float b[4][8];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
-      if (has_item) {
+      float b[RI][4];
+      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x[8];
+      for (int r = 0; r < RI; ++r) {
+        f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x[e] = __expf(gcarry[e] + (lam[e] - b[r][e]));
-            live |= x[e] != 0.f;
-          }
-          store8(sE + (tg * 4 + r) * LDL + cg * 8, x);
+        for (int e = 0; e < 4; ++e) {
+          er[r][e] = has_item ? __expf(gcarry[e] + (lam[e] - b[r][e])) : 0.f;
+          live |= er[r][e] != 0.f;
+          x[e] = pk.at(r, e) * er[r][e];
         }
+        if (has_item) store4(sEK + (16 * r + n16) * LDQ + cg * 4, x);
       }
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int pc = tid + kThreads * i;
-      if (NVP % kThreads == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
     }
     if (!__syncthreads_or(live)) break;
-    if (has_item) pdg.load(dg + (t0 + tg * 4) * DK + c0 + cg * 8, DK);
+    // ---- dk and dg (rows 16w.. of G) ----
+    if (krole) {
+      // R_n = rowsum(S_{n-1} * G) for c = 16w + n16
+      const long roff = (long)(w * 16 + n16) * DV + 4 * g4;
+      float part = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int cb = w + cc * kWaves;
-      if (cb < NCB) {
+      for (int jb = 0; jb < NJB; ++jb) {
+        piece sp;
+        if (n > 0) {
+          sp = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
+        } else {
+          const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const int t = tT * 16 + n16;
-          f32x4 acc = mma_regX<E, NJB>(zero4(), R[cc], sV + t * LDV);  // (G v_t)[c]
-          acc *= load4(sE + t * LDL + cb * 16 + 4 * g4);
-          store4(dk + (t0 + t) * DK + c0 + cb * 16 + 4 * g4, widen(dkprev[cc][tT]) + acc);
-          store4(sKD + t * LDL + cb * 16 + 4 * g4, widen(kk[cc][tT]) * acc);
+          for (int i = 0; i < 4; ++i) sp[i] = (E)x[i];
         }
-        float part = 0.f;  // R_n = rowsum(S_{n-1} * G)
+        part += piece_dot(sp, Gr[jb]);
+      }
+      part = sum_over_g4(part);
+      // dk[t][c] += exp(r_t) (G v_t)[c];  dg[t][c] += E_n R_n + sum_{s < t in the chunk} k_s dk'_s
+      f32x4 before;  // E_n R_n plus the sums of the earlier row blocks, c = 16w + 4g4 + i
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) part += piece_dot(Sp[cc][jb], R[cc][jb]);
-        part = sum_over_g4(part);
-        if (g4 == 0) sR[cb * 16 + n16] = part;
+      for (int i = 0; i < 4; ++i)
+        before[i] = __expf(gcarry[i] + lam[i]) * __shfl(part, (l & ~15) | (4 * g4 + i));
+#pragma unroll
+      for (int tT = 0; tT < NTT; ++tT) {
+        const int t = tT * 16 + n16;
+        f32x4 acc = mma_regX_e<E, NJB>(zero4(), Gr, sV + t * LDV);  // (G v_t)[c]
+        f32x4 ddk, kd, d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ddk[i] = acc[i] * er[tT][i];
+          kd[i] = pk.at(tT, i) * ddk[i];
+          const float incl = seg_scan_incl<16>(kd[i]);
+          d[i] = dgprev[tT][i] + before[i] + (incl - kd[i]);
+          before[i] += seg_last<16>(incl);
+        }
+        const long go = (t0 + t) * DK + w * 16 + 4 * g4;
+        store4(dk + go, widen(dkprev[tT]) + ddk);
+        store4(dg + go, d);
       }
     }
-    __syncthreads();
-    // dg[t] += E_n R_n + sum_{s < t in the chunk} k_s delta-dk_s, E_n = exp(sum of g from the
-    // chunk's first token to the segment's end)
-    {
-      float xs[4][8];
+    // ---- dv (columns of G) ----
+    if (vrole) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (has_item) load8(sKD + (tg * 4 + r) * LDL + cg * 8, xs[r]);
-        else
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xs[r][e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float run = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = xs[r][e];
-          xs[r][e] = run;
-          run += x;
-        }
-        const float excl = seg_prev<NTG>(seg_scan_incl<NTG>(run));
-        const float base = has_item ? __expf(gcarry[e] + lam[e]) * sR[cg * 8 + e] + excl : 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xs[r][e] += base;
-      }
-      if (has_item)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float outv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) outv[e] = pdg.at(r, e) + xs[r][e];
-          store8(dg + (t0 + tg * 4 + r) * DK + c0 + cg * 8, outv);
+        for (int sT = 0; sT < NTT; ++sT) {
+          // dv^T[j][s] += sum_c G^T[j][c] (exp(r_s) k_s)[c]
+          const f32x4 acc = mma_regX_e<E, NKB>(widen(dvprev[jj][sT]), Gt[jj], sEK + (sT * 16 + n16) * LDQ);
+          store4(dv + (t0 + sT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4, acc);
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gcarry[e] += lam[e];
+    for (int e = 0; e < 4; ++e) gcarry[e] += lam[e];
     __syncthreads();
   }
 }
 
-// dv: one workgroup per (unit, DVT-wide slice of d_v).  G^T[j][:] for the slice in registers.
 template <typename E, int C, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void correct_bwd_dv_kernel(CorrArgs a, int n_units) {
-  constexpr int DVT = DV < 64 ? DV : 64, NT = DV / DVT;
-  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG;
-  constexpr int LDQ = DK + kPad;
-  constexpr int NJB = DVT / 16, NKB = DK / 16, NTT = C / 16;
-  constexpr int JPW = ceil_div(NJB, kWaves);
-  static_assert(NI <= kThreads, "one 4x8 item per thread");
-  typedef typename Piece4<E>::type piece;
-
-  __shared__ __attribute__((aligned(16))) E sEK[2][C * LDQ];  // exp(r_t) k_t [t][c], by chunk parity
-
-  int unit, tile;
-  xcd_map(blockIdx.x, NT, unit, tile);
-  if (unit >= n_units) return;
-  const E* __restrict__ k = static_cast<const E*>(a.k);
-  const float* __restrict__ g = a.g;
-  E* __restrict__ dv = static_cast<E*>(a.dv);
-  const int L = a.T / a.P;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const int j0 = tile * DVT;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool has_item = tid < NI;
-  const int tg = tid % NTG, cg = tid / NTG;
-
-  // G^T slice: R[jj][kb][i] = G[16kb + 4g4 + i][j0 + 16jb + n16]
-  const float* gp = a.seg_grad + (long)unit * DK * DV;
-  f32x4 R[JPW][NKB];
-  int nonzero = 0;
-#pragma unroll
-  for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w + jj * kWaves;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const f32x4 x = jb < NJB ? load4(gp + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3))
-                               : zero4();
-      R[jj][kb] = quad_transpose(x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) nonzero |= x[i] != 0.f;
-    }
-  }
-  if (!__syncthreads_or(nonzero)) return;
-
-  float gcarry[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gcarry[e] = 0.f;
-  const int nchunks = L / C;
-  for (int n = nchunks - 1; n >= 0; --n) {
-    const long t0 = tok0 + (long)n * C;
-    const int par = n & 1;
-    Rows4x8<float> pg;
-    Rows4x8<E> pk;
-    if (has_item) {
-      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
-      pk.load(k + (t0 + tg * 4) * DK + cg * 8, DK);
-    }
-    piece dvprev[JPW][NTT];
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * kWaves;
-      if (jb < NJB)
-#pragma unroll
-        for (int tT = 0; tT < NTT; ++tT)
-          dvprev[jj][tT] = load_piece(dv + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4);
-    }
-    int live = 0;
-    {
-      float b[4][8], lam[8];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
-      if (has_item) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float ex = __expf(gcarry[e] + (lam[e] - b[r][e]));
-            live |= ex != 0.f;
-            x[e] = pk.at(r, e) * ex;
-          }
-          store8(&sEK[par][(tg * 4 + r) * LDQ + cg * 8], x);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gcarry[e] += lam[e];
-    }
-    if (!__syncthreads_or(live)) break;
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * kWaves;
-      if (jb < NJB) {
-#pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const int t = tT * 16 + n16;
-          const f32x4 acc = mma_regX<E, NKB>(widen(dvprev[jj][tT]), R[jj], &sEK[par][t * LDQ]);  // + G^T (e k_t)
-          store4(dv + (t0 + t) * DV + j0 + jb * 16 + 4 * g4, acc);
-        }
-      }
-    }
-  }
-}
-
-template <typename E, int C, int DK, int DV>
-struct CorrectBwdDkLauncher {
+struct CorrectBwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
     const int n_units = a.BH * a.P;
-    constexpr int NT = DK / (DK < 64 ? DK : 64);
-    const dim3 grid(round_up(n_units, 8) * NT);
-    hipLaunchKernelGGL((correct_bwd_dk_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
-    return hipGetLastError();
-  }
-};
-template <typename E, int C, int DK, int DV>
-struct CorrectBwdDvLauncher {
-  static hipError_t run(const void* pa, hipStream_t s) {
-    const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
-    const int n_units = a.BH * a.P;
-    constexpr int NT = DV / (DV < 64 ? DV : 64);
-    const dim3 grid(round_up(n_units, 8) * NT);
-    hipLaunchKernelGGL((correct_bwd_dv_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
+    hipLaunchKernelGGL((correct_bwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
 
-launch_fn lookup_correct_bwd_dk(int dtype, int chunk, int dk, int dv) {
-  return lookup_cdd<CorrectBwdDkLauncher>(dtype, chunk, dk, dv);
-}
-launch_fn lookup_correct_bwd_dv(int dtype, int chunk, int dk, int dv) {
-  return lookup_cdd<CorrectBwdDvLauncher>(dtype, chunk, dk, dv);
+launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv) {
+  return lookup_cdd<CorrectBwdLauncher>(dtype, chunk, dk, dv);
 }
 
 }  // namespace gla

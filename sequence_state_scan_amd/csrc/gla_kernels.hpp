@@ -62,8 +62,7 @@ inline int tile_of(int d) { return d < 64 ? d : 64; }
 launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_bwd(int dtype, int chunk, int dk, int dv);
-launch_fn lookup_correct_bwd_dk(int dtype, int chunk, int dk, int dv);
-launch_fn lookup_correct_bwd_dv(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv);
 
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
