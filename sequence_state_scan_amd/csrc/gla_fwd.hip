@@ -244,28 +244,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 // Correction of segment p's local results with its incoming global state S_in[p]:
 //   o_t              += (q_t * a_t) . S_in[p],   a_t = exp(sum of g from the segment start to t)
 //   chunk_states[n]  += diag(a at the end of chunk n) S_in[p]
-// One workgroup per (unit, DVT-wide slice of d_v); S_in's slice sits in registers in the
-// accumulator layout and feeds the MFMA A operand directly.  Every global read of a chunk (q, g,
-// the outputs and the chunk state to update) is issued before any of its writes, so a chunk costs
-// one memory round trip, not one per read-modify-write.  With g <= 0, a_t only decreases: once
-// every a_t of a chunk is exactly 0.0f, so are all later ones (and the chunk-end decays), and the
-// loop stops.
-template <typename E, int C, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n_units) {
-  constexpr int DVT = DV < 64 ? DV : 64, NT = DV / DVT;
-  constexpr int NTG = C / 4, NCG = DK / 8, NI = NTG * NCG;
-  constexpr int LDQ = DK + kPad;
-  constexpr int NJB = DVT / 16, NKB = DK / 16, NTT = C / 16;
-  constexpr int JPW = ceil_div(NJB, kWaves);
-  static_assert(NI <= kThreads, "one 4x8 item of q per thread");
+// With g <= 0, a_t only decreases: once every a_t of a chunk is exactly 0.0f, so are all later
+// ones (and the chunk-end decays), and the loop stops.
+//
+// One workgroup of NW waves per unit.  S_in is constant over the segment: wave w owns its d_v
+// column blocks j = 16w.., 16(w + NW).., held in fp32 registers in the store layout (4
+// consecutive j of one row c) for S_n += a_end S_in, and S_in^T sits in LDS in the element type
+// as the MFMA operand of o += (q * a) S_in, each fragment read once per chunk for all token
+// tiles.  Per live chunk every read (g, q, o, the chunk state) is issued first; q * a goes to
+// LDS, double-buffered by chunk parity so one barrier per chunk suffices.
+template <typename E, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_units) {
+  constexpr int NT = NW * 64;
+  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and q
+  constexpr int LDQ = DK + kPad, LDR = DK + kPad;
+  constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
+  constexpr int JPW = ceil_div(NJB, NW);
+  static_assert(NI <= NT, "one strided item of g and q per thread");
+  static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
   typedef typename Piece4<E>::type piece;
 
-  // double-buffered by chunk parity, so one barrier per chunk suffices
+  __shared__ __attribute__((aligned(16))) E sRT[DV * LDR];   // S_in^T  [j][c]
   __shared__ __attribute__((aligned(16))) E sQ[2][C * LDQ];  // q * a   [t][c]
   __shared__ float sAend[2][DK];                              // a at the chunk's last token
 
-  int unit, tile;
-  xcd_map(blockIdx.x, NT, unit, tile);
+  const int unit = blockIdx.x;
   if (unit >= n_units) return;
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const float* __restrict__ g = a.g;
@@ -276,96 +279,102 @@ __global__ __launch_bounds__(kThreads) void correct_fwd_kernel(CorrArgs a, int n
   const int bh = unit / a.P, p = unit - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
-  const int j0 = tile * DVT;
+  constexpr long SS = (long)DK * DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  // item of q and g: tokens 4tg..4tg+3, channels 8cg..8cg+7 (the NTG items of a channel group
-  // lie on consecutive lanes)
-  const bool has_item = tid < NI;
-  const int tg = tid % NTG, cg = tid / NTG;
+  const bool vrole = w < NJB;
+  // item of a thread: tokens 16r + n16 (r < RI), channels 4cg.. with cg = tid / 16
+  const bool has_item = NI == NT || tid < NI;
+  const int cg = tid >> 4;
 
-  // incoming state slice, accumulator layout: R[jj][kb][i] = S_in[16kb + 4g4 + i][j0 + 16jb + n16];
-  // RT is the same slice quad-transposed: RT[jj][kb][i] = S_in[16kb + 4g4 + (n16&3)][j0 + 16jb + (n16&~3) + i]
-  f32x4 R[JPW][NKB], RT[JPW][NKB];
-  const float* sin = a.seg_in + (long)unit * DK * DV;
+  // ST[jj][kb][i] = S_in[16kb + 4g4 + (n16&3)][16jb + (n16&~3) + i]  (store layout, fp32);
+  // its quad transpose, S_in[16kb + 4g4 + i][16jb + n16], is 4 consecutive c of row j of S_in^T
+  const float* sin = a.seg_in + (long)unit * SS;
+  f32x4 ST[JPW][NKB];
   int nonzero = 0;
+  if (vrole) {
 #pragma unroll
-  for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w + jj * kWaves;
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jb = w + jj * NW;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      RT[jj][kb] = jb < NJB ? load4(sin + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3))
-                            : zero4();
-      R[jj][kb] = quad_transpose(RT[jj][kb]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        ST[jj][kb] = load4(sin + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3));
+        store4(sRT + (jb * 16 + n16) * LDR + kb * 16 + 4 * g4, quad_transpose(ST[jj][kb]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nonzero |= RT[jj][kb][i] != 0.f;
+        for (int i = 0; i < 4; ++i) nonzero |= ST[jj][kb][i] != 0.f;
+      }
     }
   }
   if (!__syncthreads_or(nonzero)) return;  // zero incoming state: nothing to add
 
-  float carry[8];  // sum of g from the segment start to the end of the previous chunk
-#pragma unroll
-  for (int e = 0; e < 8; ++e) carry[e] = 0.f;
+  float carry[4] = {0.f, 0.f, 0.f, 0.f};  // sum of g from the segment start to the end of the previous chunk
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
     const int par = n & 1;
-    E* const cs = cst + (chunk0 + n) * (long)DK * DV;
-    // every read of this chunk first
-    Rows4x8<float> pg;
-    Rows4x8<E> px;
+    E* const cs = cst + (chunk0 + n) * SS;
+    // ---- every read of the chunk first ----
+    RowsRx4<float, RI> pg;
+    RowsRx4<E, RI> px;
     if (has_item) {
-      pg.load(g + (t0 + tg * 4) * DK + cg * 8, DK);
-      px.load(q + (t0 + tg * 4) * DK + cg * 8, DK);
+      const long off = (t0 + n16) * DK + cg * 4;
+      pg.load(g + off, 16 * DK);
+      px.load(q + off, 16 * DK);
     }
     piece oprev[JPW][NTT], cprev[JPW][NKB];
+    if (vrole) {
 #pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * kWaves;
-      if (jb < NJB) {
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jb = w + jj * NW;
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT)
-          oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4);
+        for (int tT = 0; tT < NTT; ++tT) oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          cprev[jj][kb] = load_piece(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + j0 + jb * 16 + (n16 & ~3));
+          cprev[jj][kb] = load_piece(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3));
       }
     }
+    // ---- a_t = exp(sum of g from the segment start to t); q * a -> LDS ----
     int live = 0;
     {
-      float b[4][8], lam[8];
-      chunk_gate_prefix<NTG>(pg, has_item, b, lam);
-      if (has_item) {
+      float b[RI][4], lam[4];
+      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x[8];
+      for (int r = 0; r < RI; ++r) {
+        f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float av = __expf(carry[e] + b[r][e]);
-            live |= av != 0.f;
-            x[e] = px.at(r, e) * av;
-          }
-          store8(&sQ[par][(tg * 4 + r) * LDQ + cg * 8], x);
+        for (int e = 0; e < 4; ++e) {
+          const float av = has_item ? __expf(carry[e] + b[r][e]) : 0.f;
+          live |= av != 0.f;
+          x[e] = px.at(r, e) * av;
         }
+        if (has_item) store4(&sQ[par][(16 * r + n16) * LDQ + cg * 4], x);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) carry[e] += lam[e];
-      if (has_item && tg == 0)
+      for (int e = 0; e < 4; ++e) carry[e] += lam[e];
+      if (has_item && n16 == 0)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sAend[par][cg * 8 + e] = __expf(carry[e]);
+        for (int e = 0; e < 4; ++e) sAend[par][cg * 4 + e] = __expf(carry[e]);
     }
     if (!__syncthreads_or(live)) break;  // every a_t of this chunk (and all later ones) is 0
+    if (vrole) {
 #pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * kWaves;
-      if (jb < NJB) {
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jb = w + jj * NW;
+        // o^T[j][t] += sum_c S_in^T[j][c] (q_t a_t)[c]
+        f32x4 acc[NTT];
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const f32x4 acc = mma_regX<E, NKB>(widen(oprev[jj][tT]), R[jj], &sQ[par][(tT * 16 + n16) * LDQ]);
-          store4(o + (t0 + tT * 16 + n16) * DV + j0 + jb * 16 + 4 * g4, acc);
+        for (int tT = 0; tT < NTT; ++tT) acc[tT] = widen(oprev[jj][tT]);
+#pragma unroll
+        for (int kk = 0; kk < DK; kk += Mma<E>::KSTEP) {
+          const typename Mma<E>::frag x = frag_ld<E, false>(sRT + jb * 16 * LDR, LDR, kk);
+#pragma unroll
+          for (int tT = 0; tT < NTT; ++tT)
+            acc[tT] = Mma<E>::mma(x, frag_ld<E, false>(&sQ[par][tT * 16 * LDQ], LDQ, kk), acc[tT]);
         }
+#pragma unroll
+        for (int tT = 0; tT < NTT; ++tT) store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc[tT]);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int c = kb * 16 + 4 * g4 + (n16 & 3);
-          store4(cs + (long)c * DV + j0 + jb * 16 + (n16 & ~3), widen(cprev[jj][kb]) + sAend[par][c] * RT[jj][kb]);
+          store4(cs + (long)c * DV + jb * 16 + (n16 & ~3), widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
         }
       }
     }
@@ -387,9 +396,7 @@ struct CorrectFwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
     const int n_units = a.BH * a.P;
-    constexpr int NT = DV / (DV < 64 ? DV : 64);
-    const dim3 grid(round_up(n_units, 8) * NT);
-    hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV>), grid, dim3(kThreads), 0, s, a, n_units);
+    hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
