@@ -29,7 +29,7 @@ __device__ __forceinline__ float row_first(float x) {
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of q, k, g: RI tokens x 4 channels
+  typedef GateTile8<E, C, DK, NW * 64> GT;  // items of q, k, g: 16 tokens x 8 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
   constexpr int LDV = DV + kPad, LDQ = DK + kPad, LDT = C + kPad;
   constexpr int DVH = DV < 128 ? DV : 128, NH = DV / DVH;  // d_v columns of U staged at a time
@@ -37,7 +37,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NJH = DVH / 16;
   constexpr int KS = Mma<E>::KSTEP;
   constexpr int KU = sizeof(E) == 2 ? 2 : 1;  // 16-wide d_v blocks per k-step of the MFMA
-  static_assert(NI <= NT, "one strided item of q, k and g per thread");
   static_assert(NCB <= NW, "one 16-row block of U^T per wave");
   static_assert(NJB % KU == 0, "d_v blocks pair up for bf16");
   static_assert(NW % NTT == 0, "the waves split evenly over the chunk's 16-token blocks");
@@ -51,6 +50,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
                 OFF_K = OFF_Q + SZ_Q, OFF_DAT = OFF_K + SZ_Q, OFF_AT = OFF_DAT + SZ_T, SMEM = OFF_AT + SZ_T;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __shared__ __attribute__((aligned(16))) float sLamE[DK];
+  __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];  // per-set gate totals
   E* const sdO = reinterpret_cast<E*>(smem + OFF_DO);    // dO   [t][j]
   E* const sV = reinterpret_cast<E*>(smem + OFF_V);      // V    [s][j]
   E* const sU = reinterpret_cast<E*>(smem + OFF_V);      // exp(lam) U [c][j - half start], after dq / dk
@@ -82,21 +82,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   const int cb = w;                   // this wave's 16-row block of U^T (waves w >= NCB hold none)
   const bool urole = cb < NCB;
 
-  // item of a thread: tokens 16i + n16 (i < RI), channels 4cg..4cg+3 with cg = tid / 16, so the 16
-  // lanes of a row hold 16 consecutive tokens of one channel group (their LDS writes hit 16
-  // consecutive rows: no bank conflicts)
-  RowsRx4<float, RI> pg;
-  RowsRx4<E, RI> pq, pk;
-  auto prefetch = [&](int n, int tid) {
-    if (NI == NT || tid < NI) {
-      const long off = (tok0 + (long)n * C + (tid & 15)) * DK + (tid >> 4) * 4;
-      pg.load(g + off, 16 * DK);
-      pq.load(q + off, 16 * DK);
-      pk.load(k + off, 16 * DK);
-    }
-  };
+  // the gate tile of q, k, g (the 16 lanes of a row hold 16 consecutive tokens of 8 channels: their
+  // 16-byte LDS writes hit 16 consecutive rows, no bank conflicts)
+  GT pgt;
+  auto prefetch = [&](int n, int tid) { pgt.load(g, q, k, (tok0 + (long)n * C) * DK, tid); };
 
-  // V and dO of a chunk, requested one chunk ahead (issued once the previous chunk's dq / dk are done)
+  // V and dO of a chunk, requested at the chunk's start
   Vec8<E> pv[VPT], pd[VPT];
   auto prefetch_vd = [&](int n, int tid) {
 #pragma unroll
@@ -120,33 +111,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   for (int n = nchunks - 1; n >= 0; --n) {
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
-    const bool has_item = NI == NT || tid < NI;
-    const int cg = tid >> 4;
     prefetch_vd(n, tid);  // this chunk's V and dO
     // ---- (1) gate prefix sums, Qbar, Kbar, exp(b); V, dO -> LDS ----
     {
-      float b[RI][4], lam[4];
-      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
-      if (has_item) {
+      float b[GT::RI][8], lam[8];
+      pgt.prefix(tid, sTot, b, lam);
+      if (GT::active(tid)) {
+        const int x = GT::group_of(tid);
 #pragma unroll
-        for (int r = 0; r < RI; ++r) {
-          f32x4 xq, xk, eb4;
+        for (int r = 0; r < GT::RI; ++r) {
+          float xq[8], xk[8], eb[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            eb4[e] = __expf(b[r][e]);
-            xq[e] = pq.at(r, e) * eb4[e];
-            xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb4[e]);  // exp(-b) to one ulp
+          for (int e = 0; e < 8; ++e) {
+            eb[e] = __expf(b[r][e]);
+            xq[e] = pgt.q[r].at(e) * eb[e];
+            xk[e] = pgt.k[r].at(e) * __builtin_amdgcn_rcpf(eb[e]);  // exp(-b) to one ulp
           }
-          const int off = (16 * r + n16) * LDQ + cg * 4;
-          store4(sQ + off, xq);
-          store4(sK + off, xk);
-          store4(sLam + off, eb4);
+          const int off = GT::row(tid, r) * LDQ + 8 * x;
+          store8(sQ + off, xq);
+          store8(sK + off, xk);
+          store8(sLam + off, eb);
         }
-        if (n16 == 0) {
-          f32x4 el;
+        if (GT::set_of(tid) == 0 && n16 == 0) {
+          float el[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
-          store4(sLamE + cg * 4, el);
+          for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
+          store8(sLamE + 8 * x, el);
         }
       }
 #pragma unroll

@@ -528,6 +528,106 @@ __device__ __forceinline__ void chunk_gate_prefix_strided(const Rows& pg, bool h
   }
 }
 
+// 8 consecutive elements of a row in registers: one 16-byte piece for bf16, two for float.
+template <typename E> struct Piece8;
+template <> struct Piece8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ float at(int e) const { return (float)v[e]; }
+};
+template <> struct Piece8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = load4(p);
+    hi = load4(p + 4);
+  }
+  __device__ __forceinline__ float at(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
+
+// Gate tile of a chunk in items of 16 tokens x 8 channels.  Lane row R = tid / 16 takes channel
+// group x = R % (DK / 8), channels 8x..8x+7, and the RI token blocks set*RI.. with set =
+// R / (DK / 8); lane n16 of the row holds token 16 * block + n16 of each.  So a load of q or k
+// reads 16 bytes per lane and the 4 lane rows of a wave cover 64 contiguous bytes of each of 16
+// token rows; a load of g reads 4 channels per lane and the pair of loads covers 128 contiguous
+// bytes per token row.  The 16 lanes of a row hold 16 consecutive tokens, so the in-block
+// running sums are DPP row scans; the NSET sets of token blocks meet through LDS.
+template <typename E, int C, int DK, int NT>
+struct GateTile8 {
+  static constexpr int NCG = DK / 8, NTB = C / 16, NROW = NT / 16;
+  static constexpr int RI = NTB * NCG >= NROW ? NTB * NCG / NROW : 1;  // token blocks per lane row
+  static constexpr int NSET = NTB / RI;                                 // lane rows per channel group
+  static constexpr int NACT = 16 * NCG * NSET;                          // threads holding an item
+  static_assert(NTB % RI == 0 && NACT <= NT, "items of 16 tokens x 8 channels tile the chunk");
+  f32x4 g[RI][2];
+  Piece8<E> q[RI], k[RI];
+
+  static __device__ __forceinline__ bool active(int tid) { return NACT == NT || tid < NACT; }
+  static __device__ __forceinline__ int set_of(int tid) { return (tid >> 4) / NCG; }
+  static __device__ __forceinline__ int group_of(int tid) { return (tid >> 4) % NCG; }
+  // chunk row (token) of block r of the thread's item
+  static __device__ __forceinline__ int row(int tid, int r) { return 16 * (set_of(tid) * RI + r) + (tid & 15); }
+
+  // chunk_elem: element offset of the chunk's first token (token index * DK)
+  __device__ __forceinline__ void load(const float* gp, const E* qp, const E* kp, long chunk_elem, int tid) {
+    if (!active(tid)) return;
+    const long off = chunk_elem + (long)row(tid, 0) * DK + 8 * group_of(tid);
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      g[r][0] = load4(gp + off + r * 16 * DK);
+      g[r][1] = load4(gp + off + r * 16 * DK + 4);
+      q[r].load(qp + off + r * 16 * DK);
+      k[r].load(kp + off + r * 16 * DK);
+    }
+  }
+  __device__ __forceinline__ float gat(int r, int e) const { return g[r][e >> 2][e & 3]; }
+
+  // b[r][e]: in-chunk inclusive running sum of g at the thread's token of block r, channel 8x + e;
+  // lam[e]: the chunk total of that channel.  sTot: NSET * DK floats of LDS.  With NSET > 1 this
+  // holds a barrier: every thread of the workgroup calls it.
+  __device__ __forceinline__ void prefix(int tid, float* sTot, float (&b)[RI][8], float (&lam)[8]) const {
+    const bool act = active(tid);
+    float run[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      run[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < RI; ++r) {
+        const float incl = seg_scan_incl<16>(act ? gat(r, e) : 0.f);
+        b[r][e] = run[e] + incl;
+        run[e] += seg_last<16>(incl);
+      }
+      lam[e] = run[e];
+    }
+    if constexpr (NSET > 1) {
+      const int set = set_of(tid), x = group_of(tid);
+      if (act && (tid & 15) == 0) {
+        store4(sTot + set * DK + 8 * x, f32x4{run[0], run[1], run[2], run[3]});
+        store4(sTot + set * DK + 8 * x + 4, f32x4{run[4], run[5], run[6], run[7]});
+      }
+      __syncthreads();
+      if (act) {
+        float before[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) before[e] = lam[e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+          const f32x4 lo = load4(sTot + s * DK + 8 * x), hi = load4(sTot + s * DK + 8 * x + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = e < 4 ? lo[e] : hi[e - 4];
+            lam[e] += t;
+            if (s < set) before[e] += t;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[r][e] += before[e];
+      }
+    }
+  }
+};
+
 // Gate prefix sums of one 4-token x NE-channel item per lane (Rows: Rows4x8<float> or
 // Rows4x4<float>), the items of one channel group lying on NTG consecutive lanes in token order:
 // on return b[r][e] is the in-chunk inclusive running sum of g and lam[e] the chunk total.

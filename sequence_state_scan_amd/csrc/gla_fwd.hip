@@ -22,21 +22,21 @@ namespace gla {
 // element type E): the local chunk states the correction turns into global ones and the
 // backward reads.
 //
-// Per chunk: (1) every thread takes one 4-token x 4-channel item of q, k and g: the gate's running
-// sum comes from a DPP scan across the 16 lanes that hold one channel group, q and k are scaled
-// and every tile is staged in LDS, and the next chunk's q, k, g, v are requested into registers;
+// Per chunk: (1) every 16-lane row takes items of 16 tokens x 8 channels of q, k and g: the gate's
+// running sum comes from DPP scans across the 16 lanes (one token each) and the totals of the
+// token-block sets meet in LDS, q and k are scaled and every tile is staged in LDS, and the next
+// chunk's q, k, g, v are requested into registers;
 // (2) the intra-chunk scores; (3) outputs and the state update on MFMA.  The requests of (1) are
 // in flight during (2)-(3).
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
-  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items: RI tokens x 4 channels
+  typedef GateTile8<E, C, DK, NW * 64> GT;  // items of q, k, g: 16 tokens x 8 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
   constexpr int LDQ = DK + kPad, LDKT = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   constexpr int KS = Mma<E>::KSTEP, NKS = C / KS;
-  static_assert(NI <= NT, "one strided item of q, k and g per thread");
   static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
 
   __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
@@ -45,6 +45,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) E sV[C * LDV];   // V    [s][j]
   __shared__ __attribute__((aligned(16))) E sA[C * LDT];   // A    [t][s], masked
   __shared__ __attribute__((aligned(16))) float sLamE[DK];  // exp(lam) per channel
+  __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];  // per-set gate totals
 
   const int unit = blockIdx.x;
   if (unit >= n_units) return;
@@ -63,20 +64,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const s16x4 ident = identity_b_operand();
   typedef typename Mma<E>::frag frag;
 
-  // item of a thread: tokens 16i + n16 (i < RI), channels 4cg..4cg+3 with cg = tid / 16, so the 16
-  // lanes of a row hold 16 consecutive tokens of one channel group (their LDS writes hit 16
-  // consecutive rows: no bank conflicts)
-  RowsRx4<float, RI> pg;
-  RowsRx4<E, RI> pq, pk;
+  // the gate tile of q, k, g (the 16 lanes of a row hold 16 consecutive tokens of 8 channels: their
+  // 16-byte LDS writes hit 16 consecutive rows, no bank conflicts)
+  GT pgt;
   Vec8<E> pv[VPT];
   auto prefetch = [&](int n, int tid) {
     const long t0 = tok0 + (long)n * C;
-    if (NI == NT || tid < NI) {
-      const long off = (t0 + (tid & 15)) * DK + (tid >> 4) * 4;
-      pg.load(g + off, 16 * DK);
-      pq.load(q + off, 16 * DK);
-      pk.load(k + off, 16 * DK);
-    }
+    pgt.load(g, q, k, t0 * DK, tid);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int pc = tid + NT * i;
@@ -89,40 +83,40 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) S[jj][kb] = zero4();
-  float ldsum[4] = {0.f, 0.f, 0.f, 0.f};  // log cumulative decay of the segment (item threads with tg == 0)
+  float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // log cumulative decay of the segment (set 0, n16 == 0)
 
   prefetch(0, threadIdx.x);
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
-    const bool has_item = NI == NT || tid < NI;
-    const int cg = tid >> 4;
     // ---- (1) gate prefix sums, Qbar, Kbar, Ktil, V -> LDS; request the next chunk ----
     {
-      float b[RI][4], lam[4];
-      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
-      if (has_item) {
-        f32x4 el;
+      float b[GT::RI][8], lam[8];
+      pgt.prefix(tid, sTot, b, lam);
+      if (GT::active(tid)) {
+        const int x = GT::group_of(tid);
+        float el[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) el[e] = __expf(lam[e]);
+        for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
 #pragma unroll
-        for (int r = 0; r < RI; ++r) {
-          f32x4 xq, xk;
+        for (int r = 0; r < GT::RI; ++r) {
+          float xq[8], xk[8], xkt[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
             const float eb = __expf(b[r][e]);
-            xq[e] = pq.at(r, e) * eb;
-            xk[e] = pk.at(r, e) * __builtin_amdgcn_rcpf(eb);  // exp(-b) to one ulp
+            xq[e] = pgt.q[r].at(e) * eb;
+            xk[e] = pgt.k[r].at(e) * __builtin_amdgcn_rcpf(eb);  // exp(-b) to one ulp
+            xkt[e] = xk[e] * el[e];
           }
-          const int row = 16 * r + n16;
-          store4(sQ + row * LDQ + cg * 4, xq);
-          store4(sK + row * LDQ + cg * 4, xk);
-          store4(sKt + row * LDKT + cg * 4, xk * el);
+          const int row = GT::row(tid, r);
+          store8(sQ + row * LDQ + 8 * x, xq);
+          store8(sK + row * LDQ + 8 * x, xk);
+          store8(sKt + row * LDKT + 8 * x, xkt);
         }
-        if (n16 == 0) {
-          store4(sLamE + cg * 4, el);
+        if (GT::set_of(tid) == 0 && n16 == 0) {
+          store8(sLamE + 8 * x, el);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ldsum[e] += lam[e];
+          for (int e = 0; e < 8; ++e) ldsum[e] += lam[e];
         }
       }
 #pragma unroll
@@ -237,8 +231,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
   }
   const int tid = threadIdx.x;
-  if ((NI == NT || tid < NI) && (tid & 15) == 0)
-    store4(a.seg_logdecay + (long)unit * DK + (tid >> 4) * 4, f32x4{ldsum[0], ldsum[1], ldsum[2], ldsum[3]});
+  if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
+    store8(a.seg_logdecay + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
