@@ -295,8 +295,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       }
       __syncthreads();
       // dv^T[j][s] = sum_t dO^T[j][t] A^T[s][t] + sum_c (exp(lam)U)^T[j][c] Kbar[s][c].  This wave takes
-      // the row block sT = w % NTT and the column blocks jl = w / NTT, w / NTT + NW / NTT, ...; its
-      // A^T and Kbar fragments are read once for all of them.
+      // the row block sT = w % NTT and the column blocks jl = w / NTT, w / NTT + NW / NTT, ... (in
+      // bf16, pairs of adjacent blocks, stored together); its A^T and Kbar fragments are read once
+      // for all of them.
       {
         const int sT = w % NTT;
         typename Mma<E>::frag fa[C / KS], fkb[DK / KS];
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
           if ((ks + 1) * KS > sT * 16) fa[ks] = frag_ld<E, false>(sAT + sT * 16 * LDT, LDT, ks * KS);  // t >= s only
 #pragma unroll
         for (int ks = 0; ks < DK / KS; ++ks) fkb[ks] = frag_ld<E, false>(sK + sT * 16 * LDQ, LDQ, ks * KS);
-        for (int jl = w / NTT; jl < NJH; jl += NW / NTT) {
+        auto dv_tile = [&](int jl) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int ks = 0; ks < C / KS; ++ks)
@@ -313,7 +314,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
               acc = Mma<E>::mma(frag_ld<E, true>(sdO + h * DVH + jl * 16, LDV, ks * KS), fa[ks], acc);
 #pragma unroll
           for (int ks = 0; ks < DK / KS; ++ks) acc = Mma<E>::mma(frag_ld<E, true>(sU + jl * 16, LDU, ks * KS), fkb[ks], acc);
-          store4(dv + (t0 + sT * 16 + n16) * DV + h * DVH + jl * 16 + 4 * g4, acc);
+          return acc;
+        };
+        E* const dvrow = dv + (t0 + sT * 16 + n16) * DV + h * DVH;
+        if constexpr (sizeof(E) == 2) {
+          static_assert(NJH % 2 == 0, "d_v blocks pair up for bf16");
+          for (int jp = w / NTT; jp < NJH / 2; jp += NW / NTT) {
+            const f32x4 x = dv_tile(2 * jp), y = dv_tile(2 * jp + 1);
+            *reinterpret_cast<bf16x8*>(dvrow + jp * 32 + pair_col(g4)) = merge_pair(to_bf16x4(x), to_bf16x4(y));
+          }
+        } else {
+          for (int jl = w / NTT; jl < NJH; jl += NW / NTT) store4(dvrow + jl * 16 + 4 * g4, dv_tile(jl));
         }
       }
       __syncthreads();

@@ -383,6 +383,42 @@ __device__ __forceinline__ bf16x4 store_tile(bf16* base, long ld, f32x4 x, s16x4
   store4(base + (long)n16 * ld + 4 * g4, t);
   return xb;
 }
+// The transpose of store_tile without the store: lane (n16, g4) gets row n16, columns 4g4.. of X^T.
+__device__ __forceinline__ bf16x4 transpose_tile(f32x4 x, s16x4 ident) {
+  bf16x4 xb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xb[i] = (bf16)x[i];
+  const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, xb), ident, zero4(), 0, 0, 0);
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)t[i];  // exact: t holds bf16 values
+  return r;
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+  return r;
+}
+
+// --------------------------------------------------------------------------------------------
+// Wider stores of two adjacent 16-column blocks.  X and Y hold, in lane (n16, g4), row n16 and
+// columns 4g4..4g4+3 of the left and the right block.  v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second: swapping the packed pairs of X and Y
+// leaves lane rows 0 and 2 with 8 consecutive columns of X (0..7, 8..15) and rows 1 and 3 with
+// those of Y.  Each lane then stores 16 bytes at column pair_col(g4) of the 32-column pair, the
+// four lane rows covering 64 contiguous bytes of each row.
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 merge_pair(bf16x4 X, bf16x4 Y) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x2 xd = __builtin_bit_cast(u32x2, X), yd = __builtin_bit_cast(u32x2, Y);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(xd[0], yd[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(xd[1], yd[1], false, false);
+  const u32x4 r = {s0[0], s1[0], s0[1], s1[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ int pair_col(int g4) { return 8 * (g4 >> 1) + 16 * (g4 & 1); }
 __device__ __forceinline__ f32x4 store_tile(float* base, long ld, f32x4 x, s16x4) {
   const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
   store4(base + (long)(4 * g4 + (n16 & 3)) * ld + (n16 & ~3), quad_transpose(x));

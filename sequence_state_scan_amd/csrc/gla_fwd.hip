@@ -17,8 +17,9 @@
 namespace gla {
 
 // One workgroup of NW waves = one (batch*head, segment) unit, all of d_v.  The state S (float32,
-// dk x dv) lives in accumulator registers for the whole segment: wave w owns the 16-column
-// blocks jb = w, w+NW, ...  After every chunk the state is also written out (chunk_states,
+// dk x dv) lives in accumulator registers for the whole segment: wave w owns JPW adjacent
+// 16-column blocks (jb = JPW w ..), so in bf16 its output and state tiles leave as 32-column
+// pairs, 16 bytes per lane.  After every chunk the state is also written out (chunk_states,
 // element type E): the local chunk states the correction turns into global ones and the
 // backward reads.
 //
@@ -144,13 +145,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     // Every operand fragment is read from LDS once per chunk: V^T of the wave's column blocks
     // serves the intra-chunk outputs and the state update; each A, Qbar and Ktil^T fragment
     // serves all of the wave's column blocks.
-    if (w < NJB) {
+    if (w * JPW < NJB) {
       E* cs = cst + (chunk0 + n) * (long)DK * DV;
       frag fv[JPW][NKS];
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) fv[jj][ks] = frag_ld<E, true>(sV + (w + jj * NW) * 16, LDV, ks * KS);
+        for (int ks = 0; ks < NKS; ++ks) fv[jj][ks] = frag_ld<E, true>(sV + (w * JPW + jj) * 16, LDV, ks * KS);
       f32x4 acc[JPW][NTT];
 #pragma unroll
       for (int tT = 0; tT < NTT; ++tT) {
@@ -195,11 +196,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) mma_regX_rows<E, NKB, NTT>(acc[jj], S[jj], sQ + n16 * LDQ, 16 * LDQ);
       }
-#pragma unroll
-      for (int jj = 0; jj < JPW; ++jj)
+      if constexpr (sizeof(E) == 2 && JPW == 2) {
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT)
-          store4(o + (t0 + tT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4, acc[jj][tT]);
+          *reinterpret_cast<bf16x8*>(o + (t0 + tT * 16 + n16) * DV + w * 32 + pair_col(g4)) =
+              merge_pair(to_bf16x4(acc[0][tT]), to_bf16x4(acc[1][tT]));
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+          for (int tT = 0; tT < NTT; ++tT)
+            store4(o + (t0 + tT * 16 + n16) * DV + (w * JPW + jj) * 16 + 4 * g4, acc[jj][tT]);
+      }
       // S = diag(exp(lam)) S + Ktil^T V
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -212,7 +220,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
           S[jj][kb] *= lamE;
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
-          store_tile(cs + (long)kb * 16 * DV + (w + jj * NW) * 16, DV, S[jj][kb], ident);
+        }
+        if constexpr (sizeof(E) == 2 && JPW == 2) {
+          *reinterpret_cast<bf16x8*>(cs + (long)(kb * 16 + n16) * DV + w * 32 + pair_col(g4)) =
+              merge_pair(transpose_tile(S[0][kb], ident), transpose_tile(S[1][kb], ident));
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) store_tile(cs + (long)kb * 16 * DV + (w * JPW + jj) * 16, DV, S[jj][kb], ident);
         }
       }
     }
@@ -224,8 +238,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w + jj * NW;
-    if (jb < NJB)
+    const int jb = w * JPW + jj;
+    if (w * JPW < NJB)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
