@@ -90,11 +90,19 @@ const char* gla_last_error(void);
  * For every segment p, starting from a ZERO state, computes
  *   o[t]                    = local output of token t (its segment's history only), dtype
  *   chunk_states[b,h,n]     = local state after chunk n (n = 0 .. T/chunk - 1 counts chunks
- *                             over the whole sequence), dtype, [B][H][T/chunk][dk][dv]
+ *                             over the whole sequence), dtype, [B][H][T/chunk] states of
+ *                             dk*dv elements in the TILED layout below
  *   seg_state[b,h,p]        = the segment's end state from a zero start, float32 [dk][dv]
  *   seg_logdecay[b,h,p,c]   = sum of g over the segment's tokens, float32
  * Inputs q, k, v (dtype), g (float32).  chunk is the tile length C of the chunkwise form.
  * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
+ *
+ * Tiled chunk-state layout (chunk_states only; every other state argument is row-major
+ * [dk][dv]): a state is (dk/16) x (dv/16) tiles of 16 x 16, tile (cb, jb) at element offset
+ * (cb * dv/16 + jb) * 256, element (16 cb + c, 16 jb + j) at (16 * (j / 4) + c) * 4 + j % 4
+ * within its tile.  A 64-lane wave holding a tile in registers writes or reads it as 512
+ * contiguous bytes; the layout is private to the four entry points (written by gla_chunk_fwd,
+ * updated by gla_segment_correct, read by gla_chunk_bwd and gla_segment_correct).
  */
 gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          void* o, void* chunk_states, float* seg_state, float* seg_logdecay,

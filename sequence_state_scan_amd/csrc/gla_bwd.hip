@@ -156,8 +156,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     if (urole) {
       const long roff = (long)(cb * 16 + n16) * DV + 4 * g4;
       if (n > 0) {
+        const E* tiles = cst + (chunk0 + n - 1) * SS + state_tile(cb, 0, NJB) + state_tile_row(n16, g4);
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_piece(cst + (chunk0 + n - 1) * SS + roff + jb * 16);
+        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_piece(tiles + jb * 256);
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {

@@ -356,50 +356,25 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
   return x;
 }
 
-// --------------------------------------------------------------------------------------------
-// Store of one 16x16 accumulator tile X (lane (n16, g4) holds X[4g4 + i][n16]) into row-major
-// memory at base (row stride ld), with 8-byte (bf16) or 16-byte (float) stores of 4 consecutive
-// columns per lane.  bf16: the tile is transposed on the matrix core, X^T = X^T . I with the
-// tile as the A operand of a 16x16x16 MFMA (exact, one nonzero product per output), so lane
-// (n16, g4) ends up holding row n16, columns 4g4..4g4+3.  Returns the tile rounded to the
-// element type in its accumulator layout (the A operand), for reuse as an MFMA operand.
-// float: the 4x4 quad transpose above.
-// --------------------------------------------------------------------------------------------
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ s16x4 identity_b_operand() {
-  // B[k = 4g4 + i][n = n16] = (k == n) for the 16x16x16 layout
-  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  s16x4 b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = (4 * g4 + i == n16) ? (short)0x3F80 : (short)0;
-  return b;
-}
-__device__ __forceinline__ bf16x4 store_tile(bf16* base, long ld, f32x4 x, s16x4 ident) {
-  bf16x4 xb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xb[i] = (bf16)x[i];
-  const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, xb), ident, zero4(), 0, 0, 0);
-  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  store4(base + (long)n16 * ld + 4 * g4, t);
-  return xb;
-}
-// The transpose of store_tile without the store: lane (n16, g4) gets row n16, columns 4g4.. of X^T.
-__device__ __forceinline__ bf16x4 transpose_tile(f32x4 x, s16x4 ident) {
-  bf16x4 xb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xb[i] = (bf16)x[i];
-  const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, xb), ident, zero4(), 0, 0, 0);
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (bf16)t[i];  // exact: t holds bf16 values
-  return r;
-}
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   bf16x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
   return r;
 }
+
+// --------------------------------------------------------------------------------------------
+// Chunk-state tiles.  A dk x dv chunk state is stored as (dk/16) x (dv/16) tiles of 16 x 16
+// elements, tile (cb, jb) at element offset (cb * (dv/16) + jb) * 256, and element (c, j) of a
+// tile at (16 * (j / 4) + c) * 4 + j % 4.  A wave holding a tile in either lane layout below reads
+// or writes it whole, 256 contiguous elements, with one instruction.
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ long state_tile(int cb, int jb, int njb) { return ((long)cb * njb + jb) * 256; }
+// lane (n16, g4) holding row n16, columns 4g4..4g4+3 of the tile
+__device__ __forceinline__ int state_tile_row(int n16, int g4) { return (16 * g4 + n16) * 4; }
+// lane (n16, g4) holding an accumulator tile X[4g4 + i][n16] after quad_transpose: row
+// 4g4 + (n16 & 3), columns (n16 & ~3) + i
+__device__ __forceinline__ int state_tile_qt(int n16, int g4) { return (16 * (n16 >> 2) + 4 * g4 + (n16 & 3)) * 4; }
 
 // --------------------------------------------------------------------------------------------
 // Wider stores of two adjacent 16-column blocks.  X and Y hold, in lane (n16, g4), row n16 and
@@ -419,11 +394,6 @@ __device__ __forceinline__ bf16x8 merge_pair(bf16x4 X, bf16x4 Y) {
   return __builtin_bit_cast(bf16x8, r);
 }
 __device__ __forceinline__ int pair_col(int g4) { return 8 * (g4 >> 1) + 16 * (g4 & 1); }
-__device__ __forceinline__ f32x4 store_tile(float* base, long ld, f32x4 x, s16x4) {
-  const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  store4(base + (long)(4 * g4 + (n16 & 3)) * ld + (n16 & ~3), quad_transpose(x));
-  return x;
-}
 
 // --------------------------------------------------------------------------------------------
 // Segmented scans across lanes: segments of W consecutive lanes (W a power of two, W <= 16), on

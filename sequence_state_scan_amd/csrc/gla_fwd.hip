@@ -62,7 +62,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const long tok0 = (long)bh * a.T + (long)p * L;
   const long chunk0 = (long)unit * nchunks;
   const int w = wave_id();
-  const s16x4 ident = identity_b_operand();
   typedef typename Mma<E>::frag frag;
 
   // the gate tile of q, k, g (the 16 lanes of a row hold 16 consecutive tokens of 8 channels: their
@@ -221,13 +220,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
         }
-        if constexpr (sizeof(E) == 2 && JPW == 2) {
-          *reinterpret_cast<bf16x8*>(cs + (long)(kb * 16 + n16) * DV + w * 32 + pair_col(g4)) =
-              merge_pair(transpose_tile(S[0][kb], ident), transpose_tile(S[1][kb], ident));
-        } else {
 #pragma unroll
-          for (int jj = 0; jj < JPW; ++jj) store_tile(cs + (long)kb * 16 * DV + (w * JPW + jj) * 16, DV, S[jj][kb], ident);
-        }
+        for (int jj = 0; jj < JPW; ++jj)
+          store4(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4), quad_transpose(S[jj][kb]));
       }
     }
     __syncthreads();
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
         for (int tT = 0; tT < NTT; ++tT) oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          cprev[jj][kb] = load_piece(cs + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3));
+          cprev[jj][kb] = load_piece(cs + state_tile(kb, jb, NJB) + state_tile_qt(n16, g4));
       }
     }
     // ---- a_t = exp(sum of g from the segment start to t); q * a -> LDS ----
@@ -382,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int c = kb * 16 + 4 * g4 + (n16 & 3);
-          store4(cs + (long)c * DV + jb * 16 + (n16 & ~3), widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
+          store4(cs + state_tile(kb, jb, NJB) + state_tile_qt(n16, g4), widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
         }
       }
     }

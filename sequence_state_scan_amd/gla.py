@@ -114,8 +114,18 @@ def _dims(q, v):
 
 # ------------------------------------------------------------------------------------ C calls
 
+def chunk_states_dense(cs):
+    """View of chunk states in the tiled layout of include/gla.h as ordinary row-major [dk][dv]
+    states (a copy; for inspection and tests, not used by any entry point)."""
+    *lead, dk, dv = cs.shape
+    L = len(lead)
+    t = cs.reshape(*lead, dk // 16, dv // 16, 4, 16, 4)  # tile row, tile column, j / 4, c, j % 4
+    return t.permute(*range(L), L, L + 3, L + 1, L + 2, L + 4).reshape(*lead, dk, dv)
+
+
 def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg_state=None, seg_logdecay=None):
-    """Local pass.  Returns (o_local, chunk_states [B,H,T/chunk,dk,dv] (local, q's dtype),
+    """Local pass.  Returns (o_local, chunk_states [B,H,T/chunk,dk,dv] (local, q's dtype, each
+    state in the tiled layout: chunk_states_dense gives the row-major view),
     seg_state [B,H,P,dk,dv], seg_logdecay [B,H,P,dk])."""
     B, H, T, dk, dv = _dims(q, v)
     o = torch.empty_like(v) if o is None else o

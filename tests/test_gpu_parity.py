@@ -45,10 +45,10 @@ def gpu_pipeline(d, chunk, P, K, bwd, h0=None, dhT=None):
     """Every step through the C ABI, keeping the intermediates.  Returns float64 numpy arrays."""
     q, k, v, g = d["q"], d["k"], d["v"], d["g"]
     o, cs, S_loc, ld = gla.gla_chunk_fwd(q, k, v, g, chunk, P)
-    res = {"o_local": o.clone(), "cs_local": cs.clone(), "S_local": S_loc, "logdecay": ld}
+    res = {"o_local": o.clone(), "cs_local": gla.chunk_states_dense(cs), "S_local": S_loc, "logdecay": ld}
     S_in, h_final = gla.gla_segment_scan(S_loc, ld, K, h_boundary=h0)
     gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=q, g=g, seg_in=S_in, o=o, chunk_states=cs)
-    res.update(S_in=S_in, h_final=h_final, o=o, cs=cs)
+    res.update(S_in=S_in, h_final=h_final, o=o, cs=gla.chunk_states_dense(cs))
     if bwd:
         dq, dk, dv, dg, D = gla.gla_chunk_bwd(q, k, v, g, d["do"], cs, S_in, chunk, P)
         res.update(dq=dq, dk_local=dk.clone(), dv_local=dv.clone(), dg_local=dg.clone(), D_local=D)
