@@ -235,6 +235,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         }
       }
       f32x4 xr[NTT];  // q dq - k dk at t = 16tT + n16, c = 16cb + 4g4 + i
+      f32x4 dqt[2], dkt[2];
 #pragma unroll
       for (int tT = 0; tT < NTT; ++tT) {
         const int t = tT * 16 + n16;
@@ -245,9 +246,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         f32x4 rl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) rl[i] = __builtin_amdgcn_rcpf(lam4[i]);
-        const long go = (t0 + t) * DK + cb * 16 + 4 * g4;
-        store4(dq + go, q_ * lam4);
-        store4(dk + go, k_ * rl);
+        if constexpr (sizeof(E) == 2) {
+          static_assert(NTT % 2 == 0, "token tiles pair up for bf16");
+          dqt[tT & 1] = q_ * lam4;
+          dkt[tT & 1] = k_ * rl;
+          if (tT & 1) {
+            // tiles tT - 1 and tT leave together, 16 bytes per lane: lane rows 0 and 2 store 8
+            // channels of token 16(tT - 1) + n16, rows 1 and 3 those of token 16 tT + n16
+            const long go = (t0 + 16 * (tT - 1 + (g4 & 1)) + n16) * DK + cb * 16 + 8 * (g4 >> 1);
+            *reinterpret_cast<bf16x8*>(dq + go) = merge_pair(to_bf16x4(dqt[0]), to_bf16x4(dqt[1]));
+            *reinterpret_cast<bf16x8*>(dk + go) = merge_pair(to_bf16x4(dkt[0]), to_bf16x4(dkt[1]));
+          }
+        } else {
+          const long go = (t0 + t) * DK + cb * 16 + 4 * g4;
+          store4(dq + go, q_ * lam4);
+          store4(dk + go, k_ * rl);
+        }
         xr[tT] = qb4 * q_ - kb4 * k_;
       }
       // dg[t][c] = sum_{t' >= t in the chunk} xr[t'][c] + carry[c]: suffix sums over the 16 tokens of
