@@ -25,7 +25,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
-constexpr int kWaves = 4;
 // LDS row padding in elements (keeps 16-byte alignment).  A row of 2^m + 8 elements puts 16
 // consecutive rows 4 banks apart: row-wise 8- and 16-byte accesses of 16 lanes to 16 rows, and the
 // transposing reads, run without bank conflicts (measured on gfx950 with the LDS conflict counter).
@@ -41,22 +40,9 @@ __device__ __forceinline__ int fresh_tid() {
   return x;
 }
 
-template <typename E> struct ElemPad { static constexpr int v = kPad; };
-
 // --------------------------------------------------------------------------------------------
 // Element loads and stores (4 or 8 consecutive elements <-> float registers)
 // --------------------------------------------------------------------------------------------
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
-}
 __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
@@ -81,30 +67,6 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 x) {
   *reinterpret_cast<bf16x4*>(p) = a;
 }
 
-// 8 rows x 8 columns of a row-major tensor with leading dimension ld -> v[row][col]
-template <typename E>
-__device__ __forceinline__ void load_blk(float (&v)[8][8], const E* p, long ld) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) load8(p + r * ld, v[r]);
-}
-// v[row][col] -> dst rows (row-major, leading dimension ld)
-template <typename E>
-__device__ __forceinline__ void store_blk_rows(E* dst, int ld, const float (&v)[8][8]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) store8(dst + r * ld, v[r]);
-}
-// v[row][col] -> dst[col][row] (the transposed block, leading dimension ld)
-template <typename E>
-__device__ __forceinline__ void store_blk_cols(E* dst, int ld, const float (&v)[8][8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float col[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) col[r] = v[r][c];
-    store8(dst + c * ld, col);
-  }
-}
-
 // --------------------------------------------------------------------------------------------
 // MFMA
 // --------------------------------------------------------------------------------------------
@@ -127,19 +89,6 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
-
-// acc[m][n] += sum_{k in [kb, ke)} X[m][k] * Y[n][k] for the 16x16 tile whose X rows start at X
-// and Y rows start at Y (row strides ldx, ldy).  kb, ke multiples of Mma<E>::KSTEP.
-template <typename E>
-__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const E* X, int ldx, const E* Y, int ldy,
-                                        int kb, int ke) {
-  const int l = lane_id();
-  const E* xp = X + (l & 15) * ldx + Mma<E>::KPL * (l >> 4);
-  const E* yp = Y + (l & 15) * ldy + Mma<E>::KPL * (l >> 4);
-#pragma unroll 4
-  for (int kk = kb; kk < ke; kk += Mma<E>::KSTEP) acc = Mma<E>::mma(Mma<E>::ld(xp + kk), Mma<E>::ld(yp + kk), acc);
-  return acc;
-}
 
 // Fragment of an operand Z[m][k] for the 16 rows m0..m0+15 at k-step kk, read from LDS.
 //   TR == false: Z stored k-contiguous, row m at P + m * ld (P points at row m0).
@@ -428,18 +377,6 @@ __device__ __forceinline__ float seg_scan_rev_incl(float x) {
   if constexpr (W > 8) x += row_shl<8>(x);
   return x;
 }
-// Value of x at the next lane of the segment (0 on the segment's last lane).
-template <int W>
-__device__ __forceinline__ float seg_next(float x) {
-  const float y = row_shl<1>(x);
-  return (W == 16 || (lane_id() & (W - 1)) != W - 1) ? y : 0.f;
-}
-// Value of x at the previous lane of the segment (0 on the segment's first lane).
-template <int W>
-__device__ __forceinline__ float seg_prev(float x) {
-  const float y = row_shr<1>(x);
-  return (W == 16 || (lane_id() & (W - 1)) != 0) ? y : 0.f;
-}
 // Value of x at the segment's last lane, on every lane of the segment.
 template <int W>
 __device__ __forceinline__ float seg_last(float x) {
@@ -448,51 +385,6 @@ __device__ __forceinline__ float seg_last(float x) {
   else
     return __shfl(x, W - 1, W);
 }
-
-// Raw 4-row x 8-column tile piece of a row-major tensor, held in registers for prefetching.
-template <typename E> struct Rows4x8;
-template <> struct Rows4x8<bf16> {
-  bf16x8 r[4];
-  __device__ __forceinline__ void load(const bf16* p, long ld) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const bf16x8*>(p + i * ld);
-  }
-  __device__ __forceinline__ float at(int i, int e) const { return (float)r[i][e]; }
-};
-template <> struct Rows4x8<float> {
-  float4 r[4][2];
-  __device__ __forceinline__ void load(const float* p, long ld) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i][0] = *reinterpret_cast<const float4*>(p + i * ld);
-      r[i][1] = *reinterpret_cast<const float4*>(p + i * ld + 4);
-    }
-  }
-  __device__ __forceinline__ float at(int i, int e) const {
-    const float4 v = r[i][e >> 2];
-    const int k = e & 3;
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-  }
-};
-
-// Raw 4-row x 4-column tile piece of a row-major tensor, held in registers for prefetching.
-template <typename E> struct Rows4x4;
-template <> struct Rows4x4<bf16> {
-  bf16x4 r[4];
-  __device__ __forceinline__ void load(const bf16* p, long ld) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const bf16x4*>(p + i * ld);
-  }
-  __device__ __forceinline__ float at(int i, int e) const { return (float)r[i][e]; }
-};
-template <> struct Rows4x4<float> {
-  f32x4 r[4];
-  __device__ __forceinline__ void load(const float* p, long ld) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const f32x4*>(p + i * ld);
-  }
-  __device__ __forceinline__ float at(int i, int e) const { return r[i][e]; }
-};
 
 // R rows of 4 consecutive elements of a row-major tensor (rows ld apart), held in registers for
 // prefetching.  With ld = 16 rows of the tensor this is a "strided item": lane n16 of a 16-lane row
@@ -634,43 +526,6 @@ struct GateTile8 {
   }
 };
 
-// Gate prefix sums of one 4-token x NE-channel item per lane (Rows: Rows4x8<float> or
-// Rows4x4<float>), the items of one channel group lying on NTG consecutive lanes in token order:
-// on return b[r][e] is the in-chunk inclusive running sum of g and lam[e] the chunk total.
-template <int NTG, int NE, class Rows>
-__device__ __forceinline__ void chunk_gate_prefix(const Rows& pg, bool has_item, float (&b)[4][NE], float (&lam)[NE]) {
-#pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    float run = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      run += has_item ? pg.at(r, e) : 0.f;
-      b[r][e] = run;
-    }
-    const float incl = seg_scan_incl<NTG>(run);
-    const float excl = seg_prev<NTG>(incl);
-    lam[e] = seg_last<NTG>(incl);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) b[r][e] += excl;
-  }
-}
-
-// Loader role of a thread when q and k items are loaded side by side: threads [0, RT) each own
-// one 4-token x 8-channel item of q (tokens 4tg.., channels 8cg..), threads [RT, 2RT) the same
-// item of k; the NTG items of one channel group lie on consecutive lanes.
-template <int RT, int NTG, int NI>
-struct LoaderRole {
-  bool krole, has_item;
-  int tg, cg;
-  __device__ __forceinline__ explicit LoaderRole(int tid) {
-    krole = tid >= RT;
-    const int rt = krole ? tid - RT : tid;
-    has_item = NI == RT || rt < NI;
-    tg = rt % NTG;
-    cg = rt / NTG;
-  }
-};
-
 // 8 consecutive elements (16 bytes for bf16, 32 for float) copied global -> registers -> LDS.
 template <typename E> struct Vec8;
 template <> struct Vec8<bf16> {
@@ -690,18 +545,6 @@ template <> struct Vec8<float> {
   }
 };
 
-// --------------------------------------------------------------------------------------------
-// Workgroup -> (unit, tile) mapping.  The dispatcher deals consecutive workgroup ids to the 8
-// XCDs in turn; this keeps all NT tiles of one unit (they read the same q/k/g chunk) on the
-// same XCD and therefore the same L2.  Grid size: round_up(n_units, 8) * NT.
-// --------------------------------------------------------------------------------------------
-__device__ __forceinline__ void xcd_map(int bid, int NT, int& unit, int& tile) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  unit = (slot / NT) * 8 + xcd;
-  tile = slot - (slot / NT) * NT;
-}
-
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
-__host__ __device__ constexpr int round_up(int a, int b) { return ceil_div(a, b) * b; }
 
 }  // namespace gla
