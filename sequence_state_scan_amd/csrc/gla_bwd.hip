@@ -31,9 +31,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
   typedef GateTile8<E, C, DK, NW * 64> GT;  // items of q, k, g: 16 tokens x 8 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDV = DV + kPad, LDQ = DK + kPad, LDT = C + kPad;
+  constexpr int LDV = lds_ld<E>(DV), LDQ = lds_ld<E>(DK), LDK = lds_ld_frag<E>(DK), LDT = lds_ld<E>(C);
   constexpr int DVH = DV < 128 ? DV : 128, NH = DV / DVH;  // d_v columns of U staged at a time
-  constexpr int LDU = DVH + kPad;
+  constexpr int LDU = lds_ld<E>(DVH);
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NJH = DVH / 16;
   constexpr int KS = Mma<E>::KSTEP;
   constexpr int KU = sizeof(E) == 2 ? 2 : 1;  // 16-wide d_v blocks per k-step of the MFMA
@@ -43,11 +43,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   typedef typename Piece4<E>::type piece;
 
   // LDS.  sV and sLam are dead once dq / dk are done; the U staging area then reuses them.
-  constexpr int SZ_V = C * LDV * (int)sizeof(E), SZ_Q = C * LDQ * (int)sizeof(E), SZ_T = C * LDT * (int)sizeof(E);
+  constexpr int SZ_V = C * LDV * (int)sizeof(E), SZ_Q = C * LDQ * (int)sizeof(E), SZ_K = C * LDK * (int)sizeof(E),
+                SZ_T = C * LDT * (int)sizeof(E);
   constexpr int SZ_U = DK * LDU * (int)sizeof(E);
   constexpr int SZ_VL = SZ_V + SZ_Q > SZ_U ? SZ_V + SZ_Q : SZ_U;  // V and exp(b), later the U staging
   constexpr int OFF_DO = 0, OFF_V = OFF_DO + SZ_V, OFF_LAM = OFF_V + SZ_V, OFF_Q = OFF_V + SZ_VL,
-                OFF_K = OFF_Q + SZ_Q, OFF_DAT = OFF_K + SZ_Q, OFF_AT = OFF_DAT + SZ_T, SMEM = OFF_AT + SZ_T;
+                OFF_K = OFF_Q + SZ_Q, OFF_DAT = OFF_K + SZ_K, OFF_AT = OFF_DAT + SZ_T, SMEM = OFF_AT + SZ_T;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __shared__ __attribute__((aligned(16))) float sLamE[DK];
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];  // per-set gate totals
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
           }
           const int off = GT::row(tid, r) * LDQ + 8 * x;
           store8(sQ + off, xq);
-          store8(sK + off, xk);
+          store8(sK + GT::row(tid, r) * LDK + 8 * x, xk);
           store8(sLam + off, eb);
         }
         if (GT::set_of(tid) == 0 && n16 == 0) {
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       const int tT = r / NTT, sT = r - (r / NTT) * NTT;
       f32x4 acc = zero4();
       if (sT <= tT) {
-        if (isA) acc = mma<E, false, false>(acc, sQ + tT * 16 * LDQ, LDQ, sK + sT * 16 * LDQ, LDQ, 0, DK);
+        if (isA) acc = mma<E, false, false>(acc, sQ + tT * 16 * LDQ, LDQ, sK + sT * 16 * LDK, LDK, 0, DK);
         else acc = mma<E, false, false>(acc, sdO + tT * 16 * LDV, LDV, sV + sT * 16 * LDV, LDV, 0, DV);
       }
       const int s = sT * 16 + n16;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       // Qbar^T fragments of this wave's rows are read once per k step for all row blocks
 #pragma unroll
       for (int ks = 0; ks < C / KS; ++ks) {
-        const typename Mma<E>::frag fk = frag_ld<E, true>(sK + cb * 16, LDQ, ks * KS);
+        const typename Mma<E>::frag fk = frag_ld<E, true>(sK + cb * 16, LDK, ks * KS);
         const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
 #pragma unroll
         for (int tT = 0; tT < NTT; ++tT) {
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         const f32x4 q_ = aq[tT], k_ = ak[tT];
         const f32x4 lam4 = load4(sLam + t * LDQ + cb * 16 + 4 * g4);
         const f32x4 qb4 = load4(sQ + t * LDQ + cb * 16 + 4 * g4);
-        const f32x4 kb4 = load4(sK + t * LDQ + cb * 16 + 4 * g4);
+        const f32x4 kb4 = load4(sK + t * LDK + cb * 16 + 4 * g4);
         f32x4 rl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) rl[i] = __builtin_amdgcn_rcpf(lam4[i]);
@@ -290,12 +291,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       if (urole) {
+        if constexpr (sizeof(E) == 2) {  // pairs of 16-column blocks, 16 bytes per lane
 #pragma unroll
-        for (int jl = 0; jl < NJH; ++jl) {
-          piece x;
+          for (int jp = 0; jp < NJH / 2; ++jp)
+            *reinterpret_cast<bf16x8*>(sU + (cb * 16 + n16) * LDU + jp * 32 + pair_col(g4)) =
+                merge_pair(to_bf16x4(U[h * NJH + 2 * jp]), to_bf16x4(U[h * NJH + 2 * jp + 1]));
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = (E)U[h * NJH + jl][i];
-          *reinterpret_cast<piece*>(sU + (cb * 16 + n16) * LDU + jl * 16 + 4 * g4) = x;
+          for (int jl = 0; jl < NJH; ++jl) {
+            piece x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (E)U[h * NJH + jl][i];
+            *reinterpret_cast<piece*>(sU + (cb * 16 + n16) * LDU + jl * 16 + 4 * g4) = x;
+          }
         }
         if (h == NH - 1) {
           // (5) U_{n-1}^T[j][c] = exp(lam) U_n^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         for (int ks = 0; ks < C / KS; ++ks)
           if ((ks + 1) * KS > sT * 16) fa[ks] = frag_ld<E, false>(sAT + sT * 16 * LDT, LDT, ks * KS);  // t >= s only
 #pragma unroll
-        for (int ks = 0; ks < DK / KS; ++ks) fkb[ks] = frag_ld<E, false>(sK + sT * 16 * LDQ, LDQ, ks * KS);
+        for (int ks = 0; ks < DK / KS; ++ks) fkb[ks] = frag_ld<E, false>(sK + sT * 16 * LDK, LDK, ks * KS);
         auto dv_tile = [&](int jl) {
           f32x4 acc = zero4();
 #pragma unroll

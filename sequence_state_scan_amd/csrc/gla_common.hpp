@@ -25,10 +25,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
-// LDS row padding in elements (keeps 16-byte alignment).  A row of 2^m + 8 elements puts 16
-// consecutive rows 4 banks apart: row-wise 8- and 16-byte accesses of 16 lanes to 16 rows, and the
-// transposing reads, run without bank conflicts (measured on gfx950 with the LDS conflict counter).
-constexpr int kPad = 8;
+// Leading dimension (elements) of a bf16 LDS tile with rows of D elements (D a multiple of 32).
+// Measured on gfx950 with the LDS bank-conflict counter, for a wave whose lane (n16, g4) touches
+// row n16 at column 8*g4 (16 bytes) or 4*g4 (8 bytes); conflict cycles per instruction:
+//   pad (mod 64)      16-B read   8-B read   16-B write   8-B write   transposing read
+//   8, 24, 40              4          0           0            4             2
+//   16, 48                 0          2           8           12             2
+// and 32 or 0 is worst.  lds_ld pads by 8: tiles written in 16-byte rows and read in 8-byte rows
+// or transposed.  lds_ld_frag pads by 16: tiles read mostly as 16-byte MFMA row fragments.
+template <typename E>
+__host__ __device__ constexpr int lds_ld(int D) { return D + 8; }
+template <typename E>
+__host__ __device__ constexpr int lds_ld_frag(int D) { return D + 16; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

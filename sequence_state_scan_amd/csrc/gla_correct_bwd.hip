@@ -25,7 +25,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   constexpr int NT = NW * 64;
   constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and k
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDV = DV + kPad, LDQ = DK + kPad;
+  constexpr int LDV = lds_ld<E>(DV), LDQ = lds_ld<E>(DK);
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NKB = DK / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   static_assert(NI <= NT, "one strided item of g and k per thread");

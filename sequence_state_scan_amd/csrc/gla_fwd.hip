@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   constexpr int NT = NW * 64;
   typedef GateTile8<E, C, DK, NW * 64> GT;  // items of q, k, g: 16 tokens x 8 channels
   constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
-  constexpr int LDQ = DK + kPad, LDKT = DK + kPad, LDV = DV + kPad, LDT = C + kPad;
+  constexpr int LDQ = lds_ld<E>(DK), LDKT = lds_ld<E>(DK), LDV = lds_ld<E>(DV), LDT = lds_ld<E>(C);
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   constexpr int KS = Mma<E>::KSTEP, NKS = C / KS;
@@ -260,7 +260,7 @@ template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_units) {
   constexpr int NT = NW * 64;
   constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and q
-  constexpr int LDQ = DK + kPad, LDR = DK + kPad;
+  constexpr int LDQ = lds_ld<E>(DK), LDR = lds_ld<E>(DK);
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
   static_assert(NI <= NT, "one strided item of g and q per thread");
