@@ -351,6 +351,18 @@ __device__ __forceinline__ bf16x8 merge_pair(bf16x4 X, bf16x4 Y) {
   return __builtin_bit_cast(bf16x8, r);
 }
 __device__ __forceinline__ int pair_col(int g4) { return 8 * (g4 >> 1) + 16 * (g4 & 1); }
+// The inverse, for a read-modify-write: the swap is its own inverse, so a piece loaded from
+// column pair_col(g4) gives back X and Y in the accumulator layout.
+__device__ __forceinline__ void unmerge_pair(bf16x8 m, bf16x4& X, bf16x4& Y) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 d = __builtin_bit_cast(u32x4, m);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(d[0], d[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(d[1], d[3], false, false);
+  const u32x2 x = {s0[0], s1[0]}, y = {s0[1], s1[1]};
+  X = __builtin_bit_cast(bf16x4, x);
+  Y = __builtin_bit_cast(bf16x4, y);
+}
 
 // --------------------------------------------------------------------------------------------
 // Segmented scans across lanes: segments of W consecutive lanes (W a power of two, W <= 16), on
@@ -473,7 +485,8 @@ struct GateTile8 {
   // chunk row (token) of block r of the thread's item
   static __device__ __forceinline__ int row(int tid, int r) { return 16 * (set_of(tid) * RI + r) + (tid & 15); }
 
-  // chunk_elem: element offset of the chunk's first token (token index * DK)
+  // chunk_elem: element offset of the chunk's first token (token index * DK); kp may be null
+  // (then k is not loaded)
   __device__ __forceinline__ void load(const float* gp, const E* qp, const E* kp, long chunk_elem, int tid) {
     if (!active(tid)) return;
     const long off = chunk_elem + (long)row(tid, 0) * DK + 8 * group_of(tid);
@@ -482,7 +495,7 @@ struct GateTile8 {
       g[r][0] = load4(gp + off + r * 16 * DK);
       g[r][1] = load4(gp + off + r * 16 * DK + 4);
       q[r].load(qp + off + r * 16 * DK);
-      k[r].load(kp + off + r * 16 * DK);
+      if (kp) k[r].load(kp + off + r * 16 * DK);
     }
   }
   __device__ __forceinline__ float gat(int r, int e) const { return g[r][e >> 2][e & 3]; }

@@ -250,26 +250,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 // With g <= 0, a_t only decreases: once every a_t of a chunk is exactly 0.0f, so are all later
 // ones (and the chunk-end decays), and the loop stops.
 //
-// One workgroup of NW waves per unit.  S_in is constant over the segment: wave w owns its d_v
-// column blocks j = 16w.., 16(w + NW).., held in fp32 registers in the store layout (4
-// consecutive j of one row c) for S_n += a_end S_in, and S_in^T sits in LDS in the element type
-// as the MFMA operand of o += (q * a) S_in, each fragment read once per chunk for all token
-// tiles.  Per live chunk every read (g, q, o, the chunk state) is issued first; q * a goes to
-// LDS, double-buffered by chunk parity so one barrier per chunk suffices.
+// One workgroup of NW waves per unit.  S_in is constant over the segment: wave w owns the JPW
+// adjacent d_v column blocks JPW w.., held in fp32 registers in the store layout (4 consecutive
+// j of one row c) for S_n += a_end S_in, and S_in^T sits in LDS in the element type as the MFMA
+// operand of o += (q * a) S_in, each fragment read once per chunk for all token tiles.  Per live
+// chunk every read (g, q, o, the chunk state) is issued first; o moves as merged pairs of
+// 16-column tiles (16 bytes per lane) in bf16; q * a goes to LDS, double-buffered by chunk parity,
+// so that besides the gate tile's set exchange one barrier per chunk suffices.
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_units) {
-  constexpr int NT = NW * 64;
-  constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and q
+  typedef GateTile8<E, C, DK, NW * 64> GT;  // items of g and q: 16 tokens x 8 channels
   constexpr int LDQ = lds_ld<E>(DK), LDR = lds_ld<E>(DK);
   constexpr int NJB = DV / 16, NKB = DK / 16, NTT = C / 16;
   constexpr int JPW = ceil_div(NJB, NW);
-  static_assert(NI <= NT, "one strided item of g and q per thread");
+  constexpr bool PAIRS = sizeof(E) == 2 && JPW == 2;  // output tiles leave as merged pairs
   static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
   typedef typename Piece4<E>::type piece;
 
   __shared__ __attribute__((aligned(16))) E sRT[DV * LDR];   // S_in^T  [j][c]
   __shared__ __attribute__((aligned(16))) E sQ[2][C * LDQ];  // q * a   [t][c]
   __shared__ float sAend[2][DK];                              // a at the chunk's last token
+  __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];  // per-set gate totals
 
   const int unit = blockIdx.x;
   if (unit >= n_units) return;
@@ -284,10 +285,8 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   const long chunk0 = (long)unit * nchunks;
   constexpr long SS = (long)DK * DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
-  const bool vrole = w < NJB;
-  // item of a thread: tokens 16r + n16 (r < RI), channels 4cg.. with cg = tid / 16
-  const bool has_item = NI == NT || tid < NI;
-  const int cg = tid >> 4;
+  const bool vrole = w * JPW < NJB;  // owns the column blocks JPW w ..
+  const int x8 = GT::group_of(tid);
 
   // ST[jj][kb][i] = S_in[16kb + 4g4 + (n16&3)][16jb + (n16&~3) + i]  (store layout, fp32);
   // its quad transpose, S_in[16kb + 4g4 + i][16jb + n16], is 4 consecutive c of row j of S_in^T
@@ -297,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   if (vrole) {
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
-      const int jb = w + jj * NW;
+      const int jb = w * JPW + jj;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         ST[jj][kb] = load4(sin + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3));
@@ -309,77 +308,96 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   }
   if (!__syncthreads_or(nonzero)) return;  // zero incoming state: nothing to add
 
-  float carry[4] = {0.f, 0.f, 0.f, 0.f};  // sum of g from the segment start to the end of the previous chunk
+  float carry[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // sum of g from the segment start to the previous chunk's end
   for (int n = 0; n < nchunks; ++n) {
     const long t0 = tok0 + (long)n * C;
     const int par = n & 1;
     E* const cs = cst + (chunk0 + n) * SS;
     // ---- every read of the chunk first ----
-    RowsRx4<float, RI> pg;
-    RowsRx4<E, RI> px;
-    if (has_item) {
-      const long off = (t0 + n16) * DK + cg * 4;
-      pg.load(g + off, 16 * DK);
-      px.load(q + off, 16 * DK);
-    }
+    GT pgt;
+    pgt.load(g, q, nullptr, t0 * DK, tid);
     piece oprev[JPW][NTT], cprev[JPW][NKB];
     if (vrole) {
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj) {
-        const int jb = w + jj * NW;
+      for (int tT = 0; tT < NTT; ++tT) {
+        if constexpr (PAIRS) {
+          unmerge_pair(*reinterpret_cast<const bf16x8*>(o + (t0 + tT * 16 + n16) * DV + w * 32 + pair_col(g4)),
+                       oprev[0][tT], oprev[1][tT]);
+        } else {
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4);
+          for (int jj = 0; jj < JPW; ++jj)
+            oprev[jj][tT] = load_piece(o + (t0 + tT * 16 + n16) * DV + (w * JPW + jj) * 16 + 4 * g4);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          cprev[jj][kb] = load_piece(cs + state_tile(kb, jb, NJB) + state_tile_qt(n16, g4));
-      }
+          cprev[jj][kb] = load_piece(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4));
     }
     // ---- a_t = exp(sum of g from the segment start to t); q * a -> LDS ----
     int live = 0;
     {
-      float b[RI][4], lam[4];
-      chunk_gate_prefix_strided<RI>(pg, has_item, b, lam);
+      float b[GT::RI][8], lam[8];
+      pgt.prefix(tid, sTot, b, lam);
+      if (GT::active(tid)) {
 #pragma unroll
-      for (int r = 0; r < RI; ++r) {
-        f32x4 x;
+        for (int r = 0; r < GT::RI; ++r) {
+          float xq[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float av = has_item ? __expf(carry[e] + b[r][e]) : 0.f;
-          live |= av != 0.f;
-          x[e] = px.at(r, e) * av;
+          for (int e = 0; e < 8; ++e) {
+            const float av = __expf(carry[e] + b[r][e]);
+            live |= av != 0.f;
+            xq[e] = pgt.q[r].at(e) * av;
+          }
+          store8(&sQ[par][GT::row(tid, r) * LDQ + 8 * x8], xq);
         }
-        if (has_item) store4(&sQ[par][(16 * r + n16) * LDQ + cg * 4], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) carry[e] += lam[e];
+        if (GT::set_of(tid) == 0 && n16 == 0) {
+          float ae[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ae[e] = __expf(carry[e]);
+          store8(&sAend[par][8 * x8], ae);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) carry[e] += lam[e];
-      if (has_item && n16 == 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sAend[par][cg * 4 + e] = __expf(carry[e]);
     }
     if (!__syncthreads_or(live)) break;  // every a_t of this chunk (and all later ones) is 0
     if (vrole) {
+      // o^T[j][t] += sum_c S_in^T[j][c] (q_t a_t)[c]
+      f32x4 acc[JPW][NTT];
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj) {
-        const int jb = w + jj * NW;
-        // o^T[j][t] += sum_c S_in^T[j][c] (q_t a_t)[c]
-        f32x4 acc[NTT];
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) acc[tT] = widen(oprev[jj][tT]);
+        for (int tT = 0; tT < NTT; ++tT) acc[jj][tT] = widen(oprev[jj][tT]);
 #pragma unroll
-        for (int kk = 0; kk < DK; kk += Mma<E>::KSTEP) {
-          const typename Mma<E>::frag x = frag_ld<E, false>(sRT + jb * 16 * LDR, LDR, kk);
+      for (int kk = 0; kk < DK; kk += Mma<E>::KSTEP) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          const typename Mma<E>::frag x = frag_ld<E, false>(sRT + (w * JPW + jj) * 16 * LDR, LDR, kk);
 #pragma unroll
           for (int tT = 0; tT < NTT; ++tT)
-            acc[tT] = Mma<E>::mma(x, frag_ld<E, false>(&sQ[par][tT * 16 * LDQ], LDQ, kk), acc[tT]);
+            acc[jj][tT] = Mma<E>::mma(x, frag_ld<E, false>(&sQ[par][tT * 16 * LDQ], LDQ, kk), acc[jj][tT]);
         }
+      }
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) store4(o + (t0 + tT * 16 + n16) * DV + jb * 16 + 4 * g4, acc[tT]);
+      for (int tT = 0; tT < NTT; ++tT) {
+        if constexpr (PAIRS) {
+          *reinterpret_cast<bf16x8*>(o + (t0 + tT * 16 + n16) * DV + w * 32 + pair_col(g4)) =
+              merge_pair(to_bf16x4(acc[0][tT]), to_bf16x4(acc[1][tT]));
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) store4(o + (t0 + tT * 16 + n16) * DV + (w * JPW + jj) * 16 + 4 * g4, acc[jj][tT]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int c = kb * 16 + 4 * g4 + (n16 & 3);
-          store4(cs + state_tile(kb, jb, NJB) + state_tile_qt(n16, g4), widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
+          store4(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4),
+                 widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
         }
-      }
     }
   }
 }
