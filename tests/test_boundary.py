@@ -103,3 +103,17 @@ def test_binding_has_no_cpu_fallback():
     q = torch.zeros(1, 1, 64, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gla.gla_chunk_fwd(q, q, q, torch.zeros(1, 1, 64, 32), chunk=32, P=1)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 256)])
+def test_chunk_state_tile_layout(dk, dv):
+    # the tiled chunk-state layout of include/gla.h, element by element: (c, j) of a state sits at
+    # (c // 16 * dv // 16 + j // 16) * 256 + (16 * (j % 16 // 4) + c % 16) * 4 + j % 4
+    rng = torch.Generator().manual_seed(1)
+    dense = torch.randn(2, 3, dk, dv, generator=rng)
+    tiled = torch.empty(2, 3, dk * dv)
+    for c in range(dk):
+        for j in range(dv):
+            off = (c // 16 * (dv // 16) + j // 16) * 256 + (16 * (j % 16 // 4) + c % 16) * 4 + j % 4
+            tiled[:, :, off] = dense[:, :, c, j]
+    assert torch.equal(gla.chunk_states_dense(tiled.reshape(2, 3, dk, dv)), dense)
