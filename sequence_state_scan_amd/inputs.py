@@ -28,6 +28,9 @@ Gate variants for stress cases (same draw, different map from x to g):
   "zero"          g = 0 (no decay at all)
   "strong"        -2 + 0.25*x clipped to <= 0 (about -2 per token: -64 over a 32-token chunk)
   "mixed"         even channels weak, odd channels strong
+  "scalar"        one decay per token and head (the LASP / TNL setting): logsigmoid(x[t, 0])/16 of
+                  the token's first draw, the same for every d_k channel (the kernels are unchanged:
+                  the gate is simply broadcast)
 """
 from __future__ import annotations
 
@@ -134,7 +137,10 @@ def _fill(seed, tensor_id, b, h, r0, rows, d, scale, gate, bf16, out):
     rng = np.random.default_rng(np.random.SeedSequence([seed, tensor_id, b, h, r0 // _ROWS]))
     x = rng.standard_normal((rows, d), dtype=np.float32)
     if tensor_id == 3:
-        out[...] = gate_from_normal(x, gate)
+        if gate == "scalar":
+            out[...] = gate_from_normal(x[:, :1], "logsigmoid16")
+        else:
+            out[...] = gate_from_normal(x, gate)
         return
     x *= scale
     if bf16:

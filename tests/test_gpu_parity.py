@@ -131,7 +131,7 @@ def test_fwdbwd_workload_h16():
 
 # ------------------------------------------------------------------------- stress and edge cases
 
-@pytest.mark.parametrize("gate", ["weak", "zero", "strong", "mixed"])
+@pytest.mark.parametrize("gate", ["weak", "zero", "strong", "mixed", "scalar"])
 @pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 64, 128, 32), ("f32", 32, 16, 16)])
 def test_gate_variants_with_boundary_states(gate, dtype, dk, dv, chunk):
     # B*H = 3 units per segment (not a multiple of the 8-way XCD grouping), h0 and dL/dS_T given

@@ -41,9 +41,13 @@ def test_gate_distribution():
     assert g.dtype == np.float32 and np.all(g <= 0)
     # logsigmoid(N(0,1)) has mean about -0.806; divided by 16
     assert abs(g.mean() - (-0.806 / 16)) < 2e-3
-    for variant in ("weak", "zero", "strong", "mixed"):
+    for variant in ("weak", "zero", "strong", "mixed", "scalar"):
         gv = inputs.generate(1, 1, 256, 8, 8, "f32", seed=1, gate=variant)["g"].numpy()
         assert np.all(gv <= 0), variant
+    # per-head scalar decay: one value per token, the same in every channel, drawn like the default
+    gs = inputs.generate(1, 2, 512, 16, 8, "f32", seed=2, gate="scalar")["g"].numpy()
+    assert np.all(gs == gs[..., :1]) and len(np.unique(gs[0, 0, :, 0])) > 500
+    assert abs(gs.mean() - (-0.806 / 16)) < 6e-3
     assert np.all(inputs.generate(1, 1, 8, 8, 8, "f32", gate="zero")["g"].numpy() == 0)
 
 
