@@ -7,7 +7,12 @@ Inputs are drawn once (seeded, synthetic) and stay resident in HBM; every output
 buffer is allocated before the timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--gate VARIANT]
-                  [--no-cpu-baseline] [--copy-calibration]
+                  [--no-cpu-baseline] [--copy-calibration] [--compare-orderings]
+
+--compare-orderings also times, on the same inputs, the two baseline orderings of the pages
+rendered on one GPU, and adds them under "orderings": the all-gather scan (LASP2's pattern,
+gla_segment_scan_allgather in place of the chain) and the serial chain (LASP1's pattern: no
+segment runs before the previous one is done, i.e. the recurrence over the whole sequence, P = 1).
 
 The roofline's "traffic" is the HBM bytes per launch of the dominant call as read by rocprofv3
 counters (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a device copy of
@@ -123,6 +128,82 @@ def cpu_baseline(w, gate, budget_s=15.0):
                       "value = tokens/(B*H)/time" % (w.B * w.H, tokens, tokens // w.L, spent)}
 
 
+def time_steps(torch, calls, steps, warmup, stream):
+    """Warm up, then time `steps` passes over `calls` with events on the launch stream.
+    Returns (ms per step, mean ms per call, wall seconds of the timed region)."""
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(steps):
+        for i, (_, fn) in enumerate(calls):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_call = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
+                for i, (name, _) in enumerate(calls)}
+    return start.elapsed_time(stop) / steps, per_call, wall
+
+
+def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
+    """The pages' baseline orderings on one GPU, same inputs and kernels: the all-gather scan in
+    place of the chain, and the serial chain (P = 1: every chunk after the previous one)."""
+    B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
+    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
+    ag = [
+        ("gla_segment_scan_allgather", lambda: gla.gla_segment_scan_allgather(buf["S_loc"], buf["ld"],
+                                                                               seg_carry=buf["S_in"],
+                                                                               h_out=buf["h_fin"])),
+        ("gla_segment_scan_allgather(reverse)", lambda: gla.gla_segment_scan_allgather(
+            buf["D"], buf["ld"], reverse=True, seg_carry=buf["G"], h_out=buf["dh0"])),
+    ]
+    ms_ag, pc_ag, _ = time_steps(torch, ag, 10, 2, stream)
+    # serial chain: one segment per (b, h); the scan is a copy and the corrections find a zero
+    # incoming state, so the step is the two local passes over the whole sequence
+    f32 = torch.float32
+    one = {n: torch.empty((B, H, 1, dk, dv), device=q.device, dtype=f32) for n in ("S", "S_in", "D", "G")}
+    ld1 = torch.empty((B, H, 1, dk), device=q.device, dtype=f32)
+    serial = [
+        ("gla_chunk_fwd(P=1)", lambda: gla.gla_chunk_fwd(q, k, v, g, C, 1, o=buf["o"], chunk_states=buf["cs"],
+                                                          seg_state=one["S"], seg_logdecay=ld1)),
+        ("gla_segment_scan(P=1)", lambda: gla.gla_segment_scan(one["S"], ld1, K, seg_carry=one["S_in"],
+                                                                h_out=buf["h_fin"])),
+        ("gla_segment_correct(FWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, 1, q=q, g=g,
+                                                                           seg_in=one["S_in"], o=buf["o"],
+                                                                           chunk_states=buf["cs"])),
+        ("gla_chunk_bwd(P=1)", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], one["S_in"], C, 1,
+                                                          dq=buf["dq"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"],
+                                                          seg_dstate=one["D"])),
+        ("gla_segment_scan(reverse, P=1)", lambda: gla.gla_segment_scan(one["D"], ld1, K, reverse=True,
+                                                                         seg_carry=one["G"], h_out=buf["dh0"])),
+        ("gla_segment_correct(BWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, 1, k=k, v=v, g=g,
+                                                                           seg_in=one["S_in"], seg_grad=one["G"],
+                                                                           chunk_states=buf["cs"], dk=buf["dk"],
+                                                                           dv=buf["dv"], dg=buf["dg"])),
+    ]
+    ms_ser, pc_ser, _ = time_steps(torch, serial, 2, 1, stream)
+    scans_chain = pc_chain["gla_segment_scan"] + pc_chain["gla_segment_scan(reverse)"]
+    res = {
+        "zeco_chain": {"ms_per_step": round(ms_chain, 4), "scan_ms": round(scans_chain, 4)},
+        "allgather_scan": {"ms_per_step": round(ms_chain - scans_chain + ms_ag, 4), "scan_ms": round(ms_ag, 4),
+                           "scan_calls_ms": {k_: round(v_, 4) for k_, v_ in pc_ag.items()}},
+        "serial_chain_P1": {"ms_per_step": round(ms_ser, 4),
+                            "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc_ser.items()}},
+    }
+    log("orderings (ms per fwd+bwd step): ZeCO chain scan %.3f | all-gather scan %.3f (scans %.3f vs %.3f) | "
+        "serial chain P=1 %.1f" % (ms_chain, res["allgather_scan"]["ms_per_step"], ms_ag, scans_chain, ms_ser))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +212,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--gate", default="logsigmoid16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compare-orderings", action="store_true",
+                    help="also time the all-gather scan and the serial chain (P = 1) on the same inputs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy %d bytes device to device (untimed), the reference for the byte counters"
                          % COPY_CALIBRATION_BYTES)
@@ -200,28 +283,7 @@ def main():
         log("copy calibration: %d bytes copied" % COPY_CALIBRATION_BYTES)
 
     stream = torch.cuda.current_stream(dev)  # the stream every call launches on
-    for _ in range(args.warmup):
-        for _, fn in calls:
-            fn()
-    torch.cuda.synchronize()
-
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-          for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for s in range(args.steps):
-        for i, (_, fn) in enumerate(calls):
-            ev[s][i][0].record(stream)
-            fn()
-            ev[s][i][1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(stop) / args.steps
-    per_call = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-                for i, (name, _) in enumerate(calls)}
+    ms_step, per_call, wall = time_steps(torch, calls, args.steps, args.warmup, stream)
     tokens = B * T
     value = tokens / (ms_step / 1e3)
 
@@ -247,6 +309,10 @@ def main():
                  "alg_flops": step_flops,
                  "mfma_frac": round(step_flops / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
+    orderings = None
+    if args.compare_orderings:
+        orderings = compare_orderings(torch, gla, w, x, buf, stream, ms_step, per_call)
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.time()
@@ -264,6 +330,8 @@ def main():
         "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},
         "wall_s_timed": round(wall, 3),
     }
+    if orderings is not None:
+        out["orderings"] = orderings
     print(json.dumps(out), flush=True)
 
 

@@ -133,6 +133,23 @@ gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay,
                             void* stream);
 
 /*
+ * gla_segment_scan_allgather -- the same results as gla_segment_scan in the all-gather order of
+ * the LASP2 baseline (mlsanity.com ZeCO page, "Key facts": LASP2 gathers every device's state
+ * where All-Scan passes one accumulated state along).  Every carry is formed directly from all
+ * the local states it depends on, with the decays between them summed in the log domain:
+ *   reverse == 0:  seg_carry[p] = sum_{q<p} exp(sum_{q<r<p} ld[r]) seg_state[q]
+ *                                 + exp(sum_{r<p} ld[r]) h_boundary;     h_out: the same at p = P
+ *   reverse == 1:  seg_carry[p] = sum_{q>p} exp(sum_{p<r<q} ld[r]) seg_state[q]
+ *                                 + exp(sum_{r>p} ld[r]) h_boundary;     h_out: the same at p = -1
+ * (ld = seg_logdecay, row-wise per d_k channel).  Equal to the chain up to rounding: the order of
+ * the sums and of the decay products differs.  O(P^2) state reads instead of O(P); no output
+ * waits for another.  Arguments, layouts and errors as gla_segment_scan, without K.
+ */
+gla_status gla_segment_scan_allgather(const float* seg_state, const float* seg_logdecay,
+                                      const float* h_boundary, float* seg_carry, float* h_out,
+                                      int B, int H, int P, int dk, int dv, int reverse, void* stream);
+
+/*
  * gla_segment_correct -- cumulative-decay correction of every segment's local results
  * (ZeCO's second pass over Q, K, V, pith.science referee report, major comment 1; the
  * atlas.scime.ai summary describes it as correcting local chunk states to global

@@ -133,6 +133,22 @@ gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay, c
                                                dk, dv, K, reverse, static_cast<hipStream_t>(stream)));
 }
 
+gla_status gla_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
+                                      float* seg_carry, float* h_out, int B, int H, int P, int dk, int dv, int reverse,
+                                      void* stream) {
+  const char* fn = "gla_segment_scan_allgather";
+  if (B < 1 || H < 1 || P < 1 || dk < 1 || dv < 1)
+    return fail(GLA_ERR_INVALID_ARG, "%s: B, H, P, dk and dv must be >= 1", fn);
+  if (reverse != 0 && reverse != 1) return fail(GLA_ERR_INVALID_ARG, "%s: reverse must be 0 or 1", fn);
+  if (!seg_state || !seg_logdecay || !seg_carry)
+    return fail(GLA_ERR_INVALID_ARG, "%s: seg_state, seg_logdecay and seg_carry must be non-null", fn);
+  if (seg_carry == seg_state) return fail(GLA_ERR_INVALID_ARG, "%s: seg_carry must not alias seg_state", fn);
+  const long long blocks = (long long)B * H * (P + 1) * (((long long)dk * dv + 255) / 256);
+  if (blocks > 0x7fffffffLL) return fail(GLA_ERR_INVALID_ARG, "%s: problem too large", fn);
+  return launched(fn, gla::launch_segment_scan_allgather(seg_state, seg_logdecay, h_boundary, seg_carry, h_out,
+                                                         B * H, P, dk, dv, reverse, static_cast<hipStream_t>(stream)));
+}
+
 gla_status gla_segment_correct(int mode, const void* q, const void* k, const void* v, const float* g,
                                const float* seg_in, const float* seg_grad, void* o, void* chunk_states, void* dk_,
                                void* dv_, float* dg, int B, int H, int T, int dk, int dv, int chunk, int P,

@@ -67,6 +67,9 @@ launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv);
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
                                int reverse, hipStream_t stream);
+hipError_t launch_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
+                                         float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int reverse,
+                                         hipStream_t stream);
 
 // Generic lookup over (dtype, chunk, D, tile): Launcher<E, C, D, TILE>::run.
 template <template <typename, int, int, int> class Launcher, class DL16, class DL32>

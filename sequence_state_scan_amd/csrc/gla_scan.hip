@@ -44,6 +44,60 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
   if (hout) hout[bh * st + off] = acc;
 }
 
+// The all-gather ordering of the same scan (the LASP2 pattern the ZeCO key-facts page compares
+// against, rendered on one GPU): every output combines the local states it depends on directly,
+// with no chain between outputs,
+//   forward: carry[p] = sum_{q<p} exp(sum_{q<r<p} ld[r]) state[q] + exp(sum_{r<p} ld[r]) h,
+//            h_out = the same with p = P
+//   reverse: carry[p] = sum_{q>p} exp(sum_{p<r<q} ld[r]) state[q] + exp(sum_{r>p} ld[r]) h,
+//            h_out = the same with p = -1
+// O(P^2) state reads instead of O(P), every output independent.  One lane per (output, element);
+// the decay exponent is accumulated in the log domain along the walk.
+__global__ __launch_bounds__(kThreads) void segment_scan_allgather_kernel(
+    const float* __restrict__ state, const float* __restrict__ logdecay, const float* __restrict__ hb,
+    float* __restrict__ carry, float* __restrict__ hout, int P, int dk, int dv, int reverse, int groups_per_out) {
+  const long st = (long)dk * dv;
+  long b = blockIdx.x;
+  const long grp = b % groups_per_out;
+  b /= groups_per_out;
+  const int oi = (int)(b % (P + 1));  // output index: 0..P-1 carries, P h_out
+  const long bh = b / (P + 1);
+  const long e = grp * kThreads + threadIdx.x;
+  if (e >= st) return;
+  if (oi == P && !hout) return;
+  const int r = (int)(e / dv);
+  float acc = 0.f, s = 0.f;
+  if (!reverse) {
+    const int p = oi;  // combines segments p-1, p-2, .., 0, then h
+    for (int q = p - 1; q >= 0; --q) {
+      const long u = bh * P + q;
+      acc = fmaf(expf(s), state[u * st + e], acc);
+      s += logdecay[u * dk + r];
+    }
+  } else {
+    const int p = oi == P ? -1 : oi;  // combines segments p+1, .., P-1, then h
+    for (int q = p + 1; q < P; ++q) {
+      const long u = bh * P + q;
+      acc = fmaf(expf(s), state[u * st + e], acc);
+      s += logdecay[u * dk + r];
+    }
+  }
+  if (hb) acc = fmaf(expf(s), hb[bh * st + e], acc);
+  if (oi == P) hout[bh * st + e] = acc;
+  else carry[(bh * P + oi) * st + e] = acc;
+}
+
+hipError_t launch_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
+                                         float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int reverse,
+                                         hipStream_t stream) {
+  const long st = (long)dk * dv;
+  const int groups = (int)((st + kThreads - 1) / kThreads);
+  const dim3 grid((unsigned)((long)BH * (P + 1) * groups));
+  hipLaunchKernelGGL(segment_scan_allgather_kernel, grid, dim3(kThreads), 0, stream, seg_state, seg_logdecay,
+                     h_boundary, seg_carry, h_out, P, dk, dv, reverse, groups);
+  return hipGetLastError();
+}
+
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
                                int reverse, hipStream_t stream) {

@@ -54,6 +54,8 @@ def load_library(path: str = LIB_PATH):
         lib.gla_chunk_fwd.restype = i
         lib.gla_segment_scan.argtypes = [fp, fp, fp, fp, fp] + [i] * 7 + [vp]
         lib.gla_segment_scan.restype = i
+        lib.gla_segment_scan_allgather.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
+        lib.gla_segment_scan_allgather.restype = i
         lib.gla_segment_correct.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, fp] + [i] * 8 + [vp]
         lib.gla_segment_correct.restype = i
         lib.gla_chunk_bwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, fp] + [i] * 8 + [vp]
@@ -155,6 +157,29 @@ def gla_segment_scan(seg_state, seg_logdecay, K: int, h_boundary=None, reverse: 
     return seg_carry, h_out
 
 
+def gla_segment_scan_allgather(seg_state, seg_logdecay, h_boundary=None, reverse: bool = False,
+                               seg_carry=None, h_out=None, want_h_out: bool = True):
+    """The same scan in the all-gather order (every carry combined directly from all the local
+    states it depends on).  Returns (seg_carry, h_out)."""
+    B, H, P, dk, dv = seg_state.shape
+    seg_carry = torch.empty_like(seg_state) if seg_carry is None else seg_carry
+    if h_out is None and want_h_out:
+        h_out = torch.empty((B, H, dk, dv), device=seg_state.device, dtype=torch.float32)
+    _check(load_library().gla_segment_scan_allgather(_f32(seg_state, "seg_state"), _f32(seg_logdecay, "seg_logdecay"),
+                                                     _f32(h_boundary, "h_boundary"), _f32(seg_carry, "seg_carry"),
+                                                     _f32(h_out, "h_out"), B, H, P, dk, dv, int(bool(reverse)),
+                                                     _stream(seg_state)))
+    return seg_carry, h_out
+
+
+def _scan(method: str, seg_state, seg_logdecay, K: int, h_boundary, reverse: bool):
+    if method == "chain":
+        return gla_segment_scan(seg_state, seg_logdecay, K, h_boundary=h_boundary, reverse=reverse)
+    if method == "allgather":
+        return gla_segment_scan_allgather(seg_state, seg_logdecay, h_boundary=h_boundary, reverse=reverse)
+    raise ValueError("unknown scan method %r" % method)
+
+
 def gla_segment_correct(mode: int, chunk: int, P: int, q=None, k=None, v=None, g=None, seg_in=None,
                         seg_grad=None, o=None, chunk_states=None, dk=None, dv=None, dg=None):
     """Cumulative-decay correction, in place: o and chunk_states for GLA_FWD; dk, dv, dg for
@@ -190,22 +215,23 @@ def gla_chunk_bwd(q, k, v, g, do, chunk_states, seg_in, chunk: int, P: int, dq=N
 
 # ------------------------------------------------------------------------------ method chains
 
-def zeco_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None):
+def zeco_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain"):
     """Local pass -> forward segment scan -> correction.  Returns a dict of tensors:
     o (global output), chunk_states (global state after every chunk), seg_in (state entering
-    each segment), h_final (state after the last token), seg_state / seg_logdecay (local pass)."""
+    each segment), h_final (state after the last token), seg_state / seg_logdecay (local pass).
+    scan: "chain" (gla_segment_scan) or "allgather" (gla_segment_scan_allgather)."""
     o, chunk_states, seg_state, seg_logdecay = gla_chunk_fwd(q, k, v, g, chunk, P)
-    seg_in, h_final = gla_segment_scan(seg_state, seg_logdecay, K, h_boundary=h0)
+    seg_in, h_final = _scan(scan, seg_state, seg_logdecay, K, h0, False)
     gla_segment_correct(GLA_FWD, chunk, P, q=q, g=g, seg_in=seg_in, o=o, chunk_states=chunk_states)
     return {"o": o, "chunk_states": chunk_states, "seg_in": seg_in, "h_final": h_final, "seg_state": seg_state,
             "seg_logdecay": seg_logdecay}
 
 
-def zeco_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=None):
+def zeco_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=None, scan: str = "chain"):
     """Local backward -> reverse segment scan -> gradient correction.  ``fwd`` is the dict
     zeco_forward returned.  Returns dq, dk, dv, dg, dh0 (and the intermediates)."""
     dq, dk, dv, dg, seg_dstate = gla_chunk_bwd(q, k, v, g, do, fwd["chunk_states"], fwd["seg_in"], chunk, P)
-    seg_grad, dh0 = gla_segment_scan(seg_dstate, fwd["seg_logdecay"], K, h_boundary=dhT, reverse=True)
+    seg_grad, dh0 = _scan(scan, seg_dstate, fwd["seg_logdecay"], K, dhT, True)
     gla_segment_correct(GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=fwd["seg_in"], seg_grad=seg_grad,
                         chunk_states=fwd["chunk_states"], dk=dk, dv=dv, dg=dg)
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dh0": dh0, "seg_dstate": seg_dstate, "seg_grad": seg_grad}

@@ -73,6 +73,16 @@ def test_segment_scan_host_checks(lib):
     assert lib.gla_segment_scan(*args(carry=FAKE)) == E  # carry aliases state
 
 
+def test_segment_scan_allgather_host_checks(lib):
+    E = gla.GLA_ERR_INVALID_ARG
+    other = ctypes.c_void_p(0x3000)
+    args = lambda rev=0, carry=other, P=4: (FAKE, FAKE, NUL, carry, NUL, 1, 1, P, 16, 16, rev, NUL)  # noqa
+    assert lib.gla_segment_scan_allgather(*args(rev=2)) == E
+    assert lib.gla_segment_scan_allgather(*args(P=0)) == E
+    assert lib.gla_segment_scan_allgather(*args(carry=NUL)) == E
+    assert lib.gla_segment_scan_allgather(*args(carry=FAKE)) == E  # carry aliases state
+
+
 def test_segment_correct_host_checks(lib):
     E = gla.GLA_ERR_INVALID_ARG
     def call(mode, q=FAKE, k=FAKE, o=FAKE, dk=FAKE, T=256, P=4):

@@ -176,6 +176,38 @@ def test_scan_is_bitwise_independent_of_K():
         assert maxrel(as_f64(outs[0][1]), ref_h) < 1e-5
 
 
+@pytest.mark.parametrize("P", [1, 2, 7, 64])
+def test_allgather_scan_matches_oracle_and_chain(P):
+    # the all-gather ordering of the scan: the oracle's chain to float32 rounding, for both
+    # directions, with and without boundary states
+    rng = np.random.default_rng(11 + P)
+    B, H, dk, dv = 2, 3, 32, 48
+    S = torch.from_numpy(rng.standard_normal((B, H, P, dk, dv)).astype(np.float32)).cuda()
+    ld = torch.from_numpy((-np.abs(rng.standard_normal((B, H, P, dk))) * 0.3).astype(np.float32)).cuda()
+    h = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32)).cuda()
+    for rev in (False, True):
+        for hb in (None, h):
+            c_ag, h_ag = gla.gla_segment_scan_allgather(S, ld, h_boundary=hb, reverse=rev)
+            c_ch, h_ch = gla.gla_segment_scan(S, ld, 4, h_boundary=hb, reverse=rev)
+            torch.cuda.synchronize()
+            ref_c, ref_h = oracle.segment_scan(as_f64(S), as_f64(ld), None if hb is None else as_f64(hb), reverse=rev)
+            for got, ref in ((c_ag, ref_c), (h_ag, ref_h), (c_ag, as_f64(c_ch)), (h_ag, as_f64(h_ch))):
+                assert maxrel(as_f64(got), ref) < 1e-5, (P, rev, hb is None)
+
+
+def test_allgather_pipeline_matches_chain_pipeline():
+    d = dev(inputs.generate(1, 2, 4096, 64, 128, "bf16", 12, True))
+    fc = gla.zeco_forward(d["q"], d["k"], d["v"], d["g"], 64, 8, 4)
+    bc = gla.zeco_backward(d["q"], d["k"], d["v"], d["g"], d["do"], fc, 64, 8, 4)
+    fa = gla.zeco_forward(d["q"], d["k"], d["v"], d["g"], 64, 8, 4, scan="allgather")
+    ba = gla.zeco_backward(d["q"], d["k"], d["v"], d["g"], d["do"], fa, 64, 8, 4, scan="allgather")
+    torch.cuda.synchronize()
+    for n in ("o", "h_final"):
+        assert maxrel(as_f64(fa[n]), as_f64(fc[n])) <= TOL["bf16"], n
+    for n in ("dq", "dk", "dv", "dg", "dh0"):
+        assert maxrel(as_f64(ba[n]), as_f64(bc[n])) <= TOL["bf16"], n
+
+
 def test_state_carry_across_calls():
     # running the second half with h0 = the first half's final state equals one call
     d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 8, False, "weak")
