@@ -16,8 +16,9 @@ namespace gla {
 
 // One workgroup of NW waves per unit.  G is constant over the segment and sits in registers,
 // rounded to the element type (the MFMA operand type), in two lane layouts: wave w holds the rows
-// c = 16w.. of G (all of d_v) for dk and dg, which contract G over d_v, and the columns
-// j = 16w.., 16(w + NW).. of G (all of d_k) for dv, which contracts it over d_k.  Per live chunk,
+// c = 16w.. of G (all of d_v) for dk and dg, which contract G over d_v, and the columns of the
+// adjacent blocks j = 16 JPW w.. of G (all of d_k) for dv, which contracts it over d_k.  In bf16,
+// dk and dv are read and written as merged pairs of 16-column tiles, 16 bytes per lane.  Per live chunk,
 // every read of g, k, V and of the outputs to update is issued first; the global state before the
 // chunk (for R_n) is read after the chunk is known to be live.
 template <typename E, int C, int DK, int DV, int NW>
@@ -28,6 +29,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   constexpr int LDV = lds_ld<E>(DV), LDQ = lds_ld<E>(DK);
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NKB = DK / 16;
   constexpr int JPW = ceil_div(NJB, NW);
+  constexpr bool PAIRS = sizeof(E) == 2;  // dk and dv move as merged pairs of 16-column tiles
   static_assert(NI <= NT, "one strided item of g and k per thread");
   static_assert(NCB <= NW, "one 16-row block of G per wave");
   static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
@@ -53,13 +55,14 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   constexpr long SS = (long)DK * DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
   const bool krole = w < NCB;            // holds rows 16w.. of G
-  const bool vrole = w < NJB;            // holds columns 16w.. (and 16(w + NW)..) of G
+  const bool vrole = w * JPW < NJB;      // holds the columns of G's blocks JPW w..
   // item of a thread: tokens 16r + n16 (r < RI), channels 4cg.. with cg = tid / 16 = 4w + g4: exactly
   // the (t, c) of the lane's dk accumulators below
   const bool has_item = NI == NT || tid < NI;
   const int cg = tid >> 4;
 
   // G rows: Gr[jb][i] = G[16w + n16][16jb + 4g4 + i];  G columns: Gt[jj][kb][i] = G[16kb + 4g4 + i][16jb + n16]
+  // with jb = JPW w + jj
   const float* gp = a.seg_grad + (long)unit * SS;
   piece Gr[NJB], Gt[JPW][NKB];
   int nonzero = 0;
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   }
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w + jj * NW;
+    const int jb = w * JPW + jj;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const f32x4 x = vrole ? quad_transpose(load4(gp + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3)))
@@ -107,18 +110,32 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
     if (krole) {
 #pragma unroll
       for (int tT = 0; tT < NTT; ++tT) {
-        const long go = (t0 + tT * 16 + n16) * DK + w * 16 + 4 * g4;
-        dkprev[tT] = load_piece(dk + go);
-        dgprev[tT] = load4(dg + go);
+        dgprev[tT] = load4(dg + (t0 + tT * 16 + n16) * DK + w * 16 + 4 * g4);
+        if constexpr (PAIRS) {
+          // token tiles tT - 1 and tT as one merged pair: lane rows 0 and 2 hold 8 channels of token
+          // 16(tT - 1) + n16, rows 1 and 3 those of token 16 tT + n16
+          if (tT & 1)
+            unmerge_pair(*reinterpret_cast<const bf16x8*>(dk + (t0 + 16 * (tT - 1 + (g4 & 1)) + n16) * DK + w * 16 +
+                                                          8 * (g4 >> 1)),
+                         dkprev[tT - 1], dkprev[tT]);
+        } else {
+          dkprev[tT] = load_piece(dk + (t0 + tT * 16 + n16) * DK + w * 16 + 4 * g4);
+        }
       }
     }
     piece dvprev[JPW][NTT];
     if (vrole) {
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj)
+      for (int sT = 0; sT < NTT; ++sT) {
+        if constexpr (PAIRS && JPW == 2) {
+          unmerge_pair(*reinterpret_cast<const bf16x8*>(dv + (t0 + sT * 16 + n16) * DV + w * 32 + pair_col(g4)),
+                       dvprev[0][sT], dvprev[1][sT]);
+        } else {
 #pragma unroll
-        for (int sT = 0; sT < NTT; ++sT)
-          dvprev[jj][sT] = load_piece(dv + (t0 + sT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4);
+          for (int jj = 0; jj < JPW; ++jj)
+            dvprev[jj][sT] = load_piece(dv + (t0 + sT * 16 + n16) * DV + (w * JPW + jj) * 16 + 4 * g4);
+        }
+      }
     }
     // ---- exp(r_t), r_t = sum of g over the tokens after t up to the segment's end; exp(r) k -> LDS ----
     float er[RI][4], lam[4];
@@ -164,6 +181,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
       part = sum_over_g4(part);
       // dk[t][c] += exp(r_t) (G v_t)[c];  dg[t][c] += E_n R_n + sum_{s < t in the chunk} k_s dk'_s
       f32x4 before;  // E_n R_n plus the sums of the earlier row blocks, c = 16w + 4g4 + i
+      f32x4 dkn[2];  // the new dk of the current pair of token tiles
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         before[i] = __expf(gcarry[i] + lam[i]) * __shfl(part, (l & ~15) | (4 * g4 + i));
@@ -181,20 +199,34 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
           before[i] += seg_last<16>(incl);
         }
         const long go = (t0 + t) * DK + w * 16 + 4 * g4;
-        store4(dk + go, widen(dkprev[tT]) + ddk);
         store4(dg + go, d);
+        if constexpr (PAIRS) {
+          dkn[tT & 1] = widen(dkprev[tT]) + ddk;
+          if (tT & 1)
+            *reinterpret_cast<bf16x8*>(dk + (t0 + 16 * (tT - 1 + (g4 & 1)) + n16) * DK + w * 16 + 8 * (g4 >> 1)) =
+                merge_pair(to_bf16x4(dkn[0]), to_bf16x4(dkn[1]));
+        } else {
+          store4(dk + go, widen(dkprev[tT]) + ddk);
+        }
       }
     }
     // ---- dv (columns of G) ----
     if (vrole) {
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj)
+      for (int sT = 0; sT < NTT; ++sT) {
+        // dv^T[j][s] += sum_c G^T[j][c] (exp(r_s) k_s)[c]
+        f32x4 acc[JPW];
 #pragma unroll
-        for (int sT = 0; sT < NTT; ++sT) {
-          // dv^T[j][s] += sum_c G^T[j][c] (exp(r_s) k_s)[c]
-          const f32x4 acc = mma_regX_e<E, NKB>(widen(dvprev[jj][sT]), Gt[jj], sEK + (sT * 16 + n16) * LDQ);
-          store4(dv + (t0 + sT * 16 + n16) * DV + (w + jj * NW) * 16 + 4 * g4, acc);
+        for (int jj = 0; jj < JPW; ++jj)
+          acc[jj] = mma_regX_e<E, NKB>(widen(dvprev[jj][sT]), Gt[jj], sEK + (sT * 16 + n16) * LDQ);
+        if constexpr (PAIRS && JPW == 2) {
+          *reinterpret_cast<bf16x8*>(dv + (t0 + sT * 16 + n16) * DV + w * 32 + pair_col(g4)) =
+              merge_pair(to_bf16x4(acc[0]), to_bf16x4(acc[1]));
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) store4(dv + (t0 + sT * 16 + n16) * DV + (w * JPW + jj) * 16 + 4 * g4, acc[jj]);
         }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) gcarry[e] += lam[e];
