@@ -15,7 +15,10 @@
 // c = 16w.. of U^T (all of d_v) in accumulator registers: they feed dq and dk, which contract U
 // and the chunk state over d_v.  dv contracts U over d_k instead, so once per chunk the waves
 // write exp(lam) U into LDS (as rows U[c][:], half of d_v at a time), and dv's tiles read it
-// back with the transposing load.  q, k, g, v and do are read from HBM once per chunk.
+// back with the transposing load.  q, k, g, v and do are read from HBM once per chunk (q, k, g as
+// gate tiles of 16 tokens x 8 channels); the chunk state arrives in U's lane layout, whole tiles
+// of the tiled chunk-state layout; dq, dk and dv leave as merged pairs of 16-column tiles, 16
+// bytes per lane.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 

@@ -18,10 +18,10 @@ namespace gla {
 
 // One workgroup of NW waves = one (batch*head, segment) unit, all of d_v.  The state S (float32,
 // dk x dv) lives in accumulator registers for the whole segment: wave w owns JPW adjacent
-// 16-column blocks (jb = JPW w ..), so in bf16 its output and state tiles leave as 32-column
-// pairs, 16 bytes per lane.  After every chunk the state is also written out (chunk_states,
-// element type E): the local chunk states the correction turns into global ones and the
-// backward reads.
+// 16-column blocks (jb = JPW w ..), so in bf16 its output tiles leave as 32-column pairs, 16 bytes
+// per lane.  After every chunk the state is also written out (chunk_states, element type E, each
+// 16x16 tile whole in the tiled chunk-state layout): the local chunk states the correction turns
+// into global ones and the backward reads.
 //
 // Per chunk: (1) every 16-lane row takes items of 16 tokens x 8 channels of q, k and g: the gate's
 // running sum comes from DPP scans across the 16 lanes (one token each) and the totals of the
