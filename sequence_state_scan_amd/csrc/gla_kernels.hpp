@@ -44,18 +44,14 @@ template <int... Vs> struct IntList {};
 using Bf16Chunks = IntList<32, 64>;
 using Bf16Dk = IntList<32, 64, 128>;
 using Bf16Dv = IntList<32, 64, 128, 256>;
-using Bf16Tiles = IntList<32, 64>;
 using F32Chunks = IntList<16, 32, 64>;
 using F32Dk = IntList<16, 32>;
 using F32Dv = IntList<16, 32>;
-using F32Tiles = IntList<16, 32>;
 
 template <typename F, int... Vs>
 inline bool dispatch_int(int v, IntList<Vs...>, F&& f) {
   return ((v == Vs ? (f(std::integral_constant<int, Vs>{}), true) : false) || ...);
 }
-
-inline int tile_of(int d) { return d < 64 ? d : 64; }
 
 // Per translation unit lookups; nullptr when no kernel exists for the shape.
 // dtype: 0 = f32, 1 = bf16.
@@ -70,26 +66,6 @@ hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay
 hipError_t launch_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                          float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int reverse,
                                          hipStream_t stream);
-
-// Generic lookup over (dtype, chunk, D, tile): Launcher<E, C, D, TILE>::run.
-template <template <typename, int, int, int> class Launcher, class DL16, class DL32>
-inline launch_fn lookup3(int dtype, int chunk, int d, int tile) {
-  launch_fn r = nullptr;
-  if (dtype == 1) {
-    dispatch_int(chunk, Bf16Chunks{}, [&](auto c) {
-      dispatch_int(d, DL16{}, [&](auto dd) {
-        dispatch_int(tile, Bf16Tiles{}, [&](auto t) { r = &Launcher<__bf16, c.value, dd.value, t.value>::run; });
-      });
-    });
-  } else if (dtype == 0) {
-    dispatch_int(chunk, F32Chunks{}, [&](auto c) {
-      dispatch_int(d, DL32{}, [&](auto dd) {
-        dispatch_int(tile, F32Tiles{}, [&](auto t) { r = &Launcher<float, c.value, dd.value, t.value>::run; });
-      });
-    });
-  }
-  return r;
-}
 
 // Generic lookup over (dtype, chunk, dk, dv): Launcher<E, C, DK, DV>::run.
 template <template <typename, int, int, int> class Launcher>
