@@ -173,21 +173,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       }
     }
     __syncthreads();
-    // ---- (2) dA[t][s] = dO[t] . V[s] and A[t][s] = Qbar[t] . Kbar[s], stored transposed, s <= t ----
-    for (int idx = w; idx < 2 * NTT * NTT; idx += NW) {
-      const bool isA = idx >= NTT * NTT;
-      const int r = isA ? idx - NTT * NTT : idx;
-      const int tT = r / NTT, sT = r - (r / NTT) * NTT;
-      f32x4 acc = zero4();
-      if (sT <= tT) {
+    // ---- (2) dA[t][s] = dO[t] . V[s] and A[t][s] = Qbar[t] . Kbar[s], stored transposed, s <= t.
+    // The tiles with sT <= tT are dealt to the waves longest first (the dA tiles contract over d_v,
+    // the A tiles over d_k) in snake order, so the SIMDs get about the same MFMA work; the all-zero
+    // tiles above the diagonal are only stored. ----
+    {
+      constexpr int NLT = NTT * (NTT + 1) / 2, NUT = NTT * (NTT - 1) / 2;
+      for (int i = 0;; ++i) {
+        const int slot = i * NW + ((i & 1) ? NW - 1 - w : w);
+        if (slot >= 2 * NLT) break;
+        const bool isA = slot >= NLT;
+        int j = isA ? slot - NLT : slot, tT = 0;  // j-th tile of the lower triangle, row-major
+        while (j > tT) j -= ++tT;
+        const int sT = j;
+        f32x4 acc = zero4();
         if (isA) acc = mma<E, false, false>(acc, sQ + tT * 16 * LDQ, LDQ, sK + sT * 16 * LDK, LDK, 0, DK);
         else acc = mma<E, false, false>(acc, sdO + tT * 16 * LDV, LDV, sV + sT * 16 * LDV, LDV, 0, DV);
-      }
-      const int s = sT * 16 + n16;
+        const int s = sT * 16 + n16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tT * 16 + 4 * g4 + i < s) acc[i] = 0.f;
-      store4((isA ? sAT : sdAT) + s * LDT + tT * 16 + 4 * g4, acc);
+        for (int q = 0; q < 4; ++q)
+          if (tT * 16 + 4 * g4 + q < s) acc[q] = 0.f;
+        store4((isA ? sAT : sdAT) + s * LDT + tT * 16 + 4 * g4, acc);
+      }
+      for (int z = w; z < 2 * NUT; z += NW) {
+        const bool isA = z >= NUT;
+        int j = isA ? z - NUT : z, tT = 0;  // j-th tile strictly above the diagonal
+        while (j >= NTT - 1 - tT) j -= NTT - 1 - tT++;
+        const int sT = tT + 1 + j;
+        store4((isA ? sAT : sdAT) + (sT * 16 + n16) * LDT + tT * 16 + 4 * g4, zero4());
+      }
     }
     __syncthreads();
     // ---- (3) exp(lam) U, dq, dk, dg ----
