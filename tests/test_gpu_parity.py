@@ -144,6 +144,18 @@ def test_one_chunk_per_segment_and_odd_counts(dtype, dk, dv, chunk, P):
     run_case(2, 1, chunk * P, dk, dv, chunk, P, 1, dtype, bwd=True, gate="weak", seed=6)
 
 
+SUPPORTED = ([("bf16", dk, dv, c) for dk in (32, 64, 128) for dv in (32, 64, 128, 256) for c in (32, 64)] +
+             [("f32", dk, dv, c) for dk in (16, 32) for dv in (16, 32) for c in (16, 32, 64)])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,chunk", SUPPORTED)
+def test_every_supported_shape(dtype, dk, dv, chunk):
+    # every compiled kernel instantiation, fwd+bwd through all steps, against the oracle: 4
+    # segments of 2 chunks, boundary states given
+    assert gla.load_library().gla_supported(gla.GLA_BF16 if dtype == "bf16" else gla.GLA_F32, dk, dv, chunk) == 1
+    run_case(1, 2, 8 * chunk, dk, dv, chunk, 4, 2, dtype, bwd=True, gate="weak", seed=21, carry=True)
+
+
 def test_chunk_size_invariance():
     d = dev(inputs.generate(1, 2, 2048, 128, 128, "bf16", 3, True, "weak"))
     a = gpu_pipeline(d, 32, 4, 4, True)
