@@ -51,7 +51,8 @@
  * Supported shapes (gla_supported() answers for a given combination):
  *   GLA_BF16: chunk in {32, 64}; dk in {32, 64, 128}; dv in {32, 64, 128, 256}
  *   GLA_F32:  chunk in {16, 32, 64}; dk in {16, 32}; dv in {16, 32}
- *   always:   B, H, P >= 1; T % P == 0; (T / P) % chunk == 0
+ *   always:   B, H, T, P >= 1 (an empty sequence is rejected with GLA_ERR_INVALID_ARG);
+ *             T % P == 0; (T / P) % chunk == 0
  */
 #ifndef GLA_H
 #define GLA_H

@@ -52,6 +52,7 @@ def test_chunk_fwd_host_checks(lib):
     assert _fwd(lib, T=250, P=4) == E          # T % P != 0
     assert _fwd(lib, T=256, P=8) == E          # segment 32 not a multiple of chunk 64
     assert _fwd(lib, B=0) == E
+    assert _fwd(lib, T=0) == E                 # empty sequence
     assert _fwd(lib, dtype=9) == E
     assert _fwd(lib, q=NUL) == E               # null input
     assert _fwd(lib, ss=NUL) == E              # null output
@@ -94,19 +95,21 @@ def test_segment_correct_host_checks(lib):
     assert call(gla.GLA_BWD, k=NUL) == E
     assert call(gla.GLA_BWD, dk=NUL) == E
     assert call(gla.GLA_FWD, T=100, P=4) == E
+    assert call(gla.GLA_BWD, T=0) == E         # empty sequence
 
 
 def test_chunk_bwd_host_checks(lib):
     E = gla.GLA_ERR_INVALID_ARG
-    def call(dq=ctypes.c_void_p(0x5000), dg=ctypes.c_void_p(0x6000), P=2):
+    def call(dq=ctypes.c_void_p(0x5000), dg=ctypes.c_void_p(0x6000), P=2, T=256):
         return lib.gla_chunk_bwd(FAKE, ctypes.c_void_p(0x1100), ctypes.c_void_p(0x1200), ctypes.c_void_p(0x1300),
                                  ctypes.c_void_p(0x1400), ctypes.c_void_p(0x1480), ctypes.c_void_p(0x1500), dq,
                                  ctypes.c_void_p(0x7000),
                                  ctypes.c_void_p(0x8000), dg, ctypes.c_void_p(0x9000),
-                                 1, 1, 256, 64, 64, 64, P, gla.GLA_BF16, NUL)
+                                 1, 1, T, 64, 64, 64, P, gla.GLA_BF16, NUL)
     assert call(dq=FAKE) == E      # dq aliases q
     assert call(dg=NUL) == E
     assert call(P=3) == E
+    assert call(T=0) == E          # empty sequence
 
 
 def test_binding_has_no_cpu_fallback():
