@@ -156,6 +156,29 @@ def test_every_supported_shape(dtype, dk, dv, chunk):
     run_case(1, 2, 8 * chunk, dk, dv, chunk, 4, 2, dtype, bwd=True, gate="weak", seed=21, carry=True)
 
 
+def _mixed_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dtype, dk, dv, chunk = SUPPORTED[int(rng.integers(len(SUPPORTED)))]
+        B, H, P = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 10))
+        per_seg = int(rng.integers(1, 6))
+        K = [k for k in (1, 2, 4, 8, 16) if dk % k == 0][int(rng.integers(0, 3))]
+        gate = ("logsigmoid16", "weak", "strong", "scalar")[int(rng.integers(4))]
+        if gate == "strong" and chunk > 32:
+            gate = "weak"  # the chunk form needs every chunk's decay above -87 (strong is about -2 per token)
+        cases.append((B, H, P * per_seg * chunk, dk, dv, chunk, P, K, dtype, gate, int(rng.integers(1000))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _mixed_cases())
+def test_mixed_configurations(case):
+    # a fixed sample of mixed shapes, segment counts, batch/head counts, dtypes and gates, fwd+bwd
+    # with boundary states, against the oracle step by step and against the plain recurrence
+    B, H, T, dk, dv, chunk, P, K, dtype, gate, seed = case
+    run_case(B, H, T, dk, dv, chunk, P, K, dtype, bwd=True, gate=gate, seed=seed, carry=True)
+
+
 def test_chunk_size_invariance():
     d = dev(inputs.generate(1, 2, 2048, 128, 128, "bf16", 3, True, "weak"))
     a = gpu_pipeline(d, 32, 4, 4, True)
