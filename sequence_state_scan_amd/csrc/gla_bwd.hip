@@ -220,18 +220,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       for (int tT = 0; tT < NTT; ++tT) aq[tT] = ak[tT] = zero4();
 #pragma unroll
       for (int j0 = 0; j0 < NJB; j0 += KU) {
-        piece sp[KU];
-        f32x4 ue[KU];
+        if constexpr (sizeof(E) == 2) {
+          // merged, the lane's pieces of blocks j0 and j0 + 1 are the 8 adjacent columns
+          // 16 j0 + pair_col(g4) + 0..7: the B fragment is one 16-byte read (two 8-byte reads
+          // per fragment run at about a third of the rate)
+          const bf16x8 xs = merge_pair(Sp[j0], Sp[j0 + 1]);
+          const bf16x8 xu = merge_pair(to_bf16x4(U[j0]), to_bf16x4(U[j0 + 1]));
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
-          sp[u] = Sp[j0 + u];
-          ue[u] = U[j0 + u];
-        }
+          for (int tT = 0; tT < NTT; ++tT) {
+            const int off = (tT * 16 + n16) * LDV + 16 * j0 + pair_col(g4);
+            aq[tT] = Mma<E>::mma(xs, *reinterpret_cast<const bf16x8*>(sdO + off), aq[tT]);
+            ak[tT] = Mma<E>::mma(xu, *reinterpret_cast<const bf16x8*>(sV + off), ak[tT]);
+          }
+        } else {
+          piece sp[1] = {Sp[j0]};
+          f32x4 ue[1] = {U[j0]};
 #pragma unroll
-        for (int tT = 0; tT < NTT; ++tT) {
-          const int t = tT * 16 + n16;
-          aq[tT] = mma_regX_e<E, KU>(aq[tT], sp, sdO + t * LDV + j0 * 16);
-          ak[tT] = mma_regX<E, KU>(ak[tT], ue, sV + t * LDV + j0 * 16);
+          for (int tT = 0; tT < NTT; ++tT) {
+            const int t = tT * 16 + n16;
+            aq[tT] = mma_regX_e<E, 1>(aq[tT], sp, sdO + t * LDV + j0 * 16);
+            ak[tT] = mma_regX<E, 1>(ak[tT], ue, sV + t * LDV + j0 * 16);
+          }
         }
       }
       // the carry into chunk n-1, rowsum(S_{n-1} * U_{n-1}) with U_{n-1} = exp(lam) U_n + Qbar^T dO, is
