@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       if (n > 0) {
         const E* tiles = cst + (chunk0 + n - 1) * SS + state_tile(cb, 0, NJB) + state_tile_row(n16, g4);
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_piece(tiles + jb * 256);
+        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = gld_nt(reinterpret_cast<const piece*>(tiles + jb * 256));
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {

@@ -75,6 +75,20 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 x) {
   *reinterpret_cast<bf16x4*>(p) = a;
 }
 
+// Streaming (nontemporal) global accesses.  Used only where one wave instruction covers whole
+// 128-byte lines: the rows of V and dO, and the chunk-state tiles (512 contiguous bytes).  There
+// the streaming policy raised throughput by a few percent on gfx950.  Accesses that cover half a
+// line per instruction (gate tiles, merged output pairs) were much slower with it, presumably
+// because the line is dropped before the other half arrives, so they keep the default policy.
+template <typename T>
+__device__ __forceinline__ T gld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void gst_nt(float* p, f32x4 x) { __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p)); }
+__device__ __forceinline__ void gst_nt(bf16* p, f32x4 x) {
+  bf16x4 a;
+  a[0] = (bf16)x[0]; a[1] = (bf16)x[1]; a[2] = (bf16)x[2]; a[3] = (bf16)x[3];
+  __builtin_nontemporal_store(a, reinterpret_cast<bf16x4*>(p));
+}
+
 // --------------------------------------------------------------------------------------------
 // MFMA
 // --------------------------------------------------------------------------------------------
@@ -551,7 +565,7 @@ struct GateTile8 {
 template <typename E> struct Vec8;
 template <> struct Vec8<bf16> {
   bf16x8 v;
-  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void load(const bf16* p) { v = gld_nt(reinterpret_cast<const bf16x8*>(p)); }
   __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
 };
 template <> struct Vec8<float> {

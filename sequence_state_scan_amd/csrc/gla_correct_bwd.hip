@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
       for (int jb = 0; jb < NJB; ++jb) {
         piece sp;
         if (n > 0) {
-          sp = load_piece(cst + (chunk0 + n - 1) * SS + state_tile(w, jb, NJB) + state_tile_row(n16, g4));
+          sp = gld_nt(reinterpret_cast<const piece*>(cst + (chunk0 + n - 1) * SS + state_tile(w, jb, NJB) + state_tile_row(n16, g4)));
         } else {
           const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
 #pragma unroll

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         }
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj)
-          store4(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4), quad_transpose(S[jj][kb]));
+          gst_nt(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4), quad_transpose(S[jj][kb]));
       }
     }
     __syncthreads();
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
       for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          cprev[jj][kb] = load_piece(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4));
+          cprev[jj][kb] = gld_nt(reinterpret_cast<const piece*>(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4)));
     }
     // ---- a_t = exp(sum of g from the segment start to t); q * a -> LDS ----
     int live = 0;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const int c = kb * 16 + 4 * g4 + (n16 & 3);
-          store4(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4),
+          gst_nt(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4),
                  widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
         }
     }
