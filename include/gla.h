@@ -99,11 +99,14 @@ const char* gla_last_error(void);
  * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
  *
  * Tiled chunk-state layout (chunk_states only; every other state argument is row-major
- * [dk][dv]): a state is (dk/16) x (dv/16) tiles of 16 x 16, tile (cb, jb) at element offset
- * (cb * dv/16 + jb) * 256, element (16 cb + c, 16 jb + j) at (16 * (j / 4) + c) * 4 + j % 4
- * within its tile.  A 64-lane wave holding a tile in registers writes or reads it as 512
- * contiguous bytes; the layout is private to the four entry points (written by gla_chunk_fwd,
- * updated by gla_segment_correct, read by gla_chunk_bwd and gla_segment_correct).
+ * [dk][dv]): a state is (dk/16) x (dv/16) tiles of 16 x 16.  Element (16 cb + c, 16 jb + j)
+ * belongs to lane index L = 16 * (j / 4) + c of tile (cb, jb), position j % 4.  When dv/16 is
+ * even, tiles (cb, 2m) and (cb, 2m + 1) are interleaved: the element sits at
+ * (cb * dv/16 + 2m) * 256 + 8 L + 4 (jb - 2m) + j % 4.  When dv/16 is odd (dv = 16) it sits at
+ * (cb * dv/16 + jb) * 256 + 4 L + j % 4.  A 64-lane wave holding a pair of tiles in registers
+ * writes or reads it as 1024 contiguous bytes (bf16); the layout is private to the four entry
+ * points (written by gla_chunk_fwd, updated by gla_segment_correct, read by gla_chunk_bwd and
+ * gla_segment_correct).
  */
 gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          void* o, void* chunk_states, float* seg_state, float* seg_logdecay,

@@ -160,9 +160,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     if (urole) {
       const long roff = (long)(cb * 16 + n16) * DV + 4 * g4;
       if (n > 0) {
-        const E* tiles = cst + (chunk0 + n - 1) * SS + state_tile(cb, 0, NJB) + state_tile_row(n16, g4);
+        const E* st = cst + (chunk0 + n - 1) * SS;
+        if constexpr (NJB % 2 == 0) {
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) Sp[jb] = gld_nt(reinterpret_cast<const piece*>(tiles + jb * 256));
+          for (int m = 0; m < NJB / 2; ++m) load_state_pair<E, NJB>(st, cb, m, state_lane_row(n16, g4), Sp[2 * m], Sp[2 * m + 1]);
+        } else {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_state_piece<E, NJB>(st, cb, jb, state_lane_row(n16, g4));
+        }
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {

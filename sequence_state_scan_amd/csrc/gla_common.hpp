@@ -333,19 +333,64 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
   return r;
 }
+__device__ __forceinline__ bf16x8 join_bf16x4(bf16x4 x, bf16x4 y) {
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // --------------------------------------------------------------------------------------------
 // Chunk-state tiles.  A dk x dv chunk state is stored as (dk/16) x (dv/16) tiles of 16 x 16
-// elements, tile (cb, jb) at element offset (cb * (dv/16) + jb) * 256, and element (c, j) of a
-// tile at (16 * (j / 4) + c) * 4 + j % 4.  A wave holding a tile in either lane layout below reads
-// or writes it whole, 256 contiguous elements, with one instruction.
+// elements.  Element (r, q) of a tile belongs to lane index L = 16 (q / 4) + r, position q % 4.
+// With dv/16 even, tiles (cb, 2m) and (cb, 2m + 1) are interleaved: lane index L of the pair holds
+// 8 consecutive elements, its 4 of tile 2m and then its 4 of tile 2m + 1, at element offset
+// (cb * dv/16 + 2m) * 256 + 8 L.  With dv/16 odd (only dv = 16) tile (cb, jb) holds its 4 at
+// (cb * dv/16 + jb) * 256 + 4 L.  A wave whose lanes hold both tiles of a pair in one of the lane
+// layouts below moves them with one 16-byte access per lane (bf16): 1024 contiguous bytes.
 // --------------------------------------------------------------------------------------------
-__device__ __forceinline__ long state_tile(int cb, int jb, int njb) { return ((long)cb * njb + jb) * 256; }
-// lane (n16, g4) holding row n16, columns 4g4..4g4+3 of the tile
-__device__ __forceinline__ int state_tile_row(int n16, int g4) { return (16 * g4 + n16) * 4; }
-// lane (n16, g4) holding an accumulator tile X[4g4 + i][n16] after quad_transpose: row
-// 4g4 + (n16 & 3), columns (n16 & ~3) + i
-__device__ __forceinline__ int state_tile_qt(int n16, int g4) { return (16 * (n16 >> 2) + 4 * g4 + (n16 & 3)) * 4; }
+template <int NJB>
+__device__ __forceinline__ long state_at(int cb, int jb, int L) {
+  if constexpr (NJB % 2 == 0) return (long)(cb * NJB + (jb & ~1)) * 256 + 8 * L + 4 * (jb & 1);
+  else return (long)(cb * NJB + jb) * 256 + 4 * L;
+}
+// lane index of lane (n16, g4) holding row n16, columns 4g4..4g4+3 of a tile
+__device__ __forceinline__ int state_lane_row(int n16, int g4) { return 16 * g4 + n16; }
+// lane index of lane (n16, g4) holding an accumulator tile X[4g4 + i][n16] after quad_transpose:
+// row 4g4 + (n16 & 3), columns (n16 & ~3) + i
+__device__ __forceinline__ int state_lane_qt(int n16, int g4) { return 16 * (n16 >> 2) + 4 * g4 + (n16 & 3); }
+
+// The lane's pieces of tiles (cb, 2m) and (cb, 2m + 1) (streaming loads; dv/16 even)
+template <typename E, int NJB>
+__device__ __forceinline__ void load_state_pair(const E* st, int cb, int m, int L, typename Piece4<E>::type& a,
+                                                typename Piece4<E>::type& b) {
+  typedef typename Piece4<E>::type piece;
+  static_assert(NJB % 2 == 0, "tiles pair up along dv");
+  if constexpr (sizeof(E) == 2) {
+    const bf16x8 x = gld_nt(reinterpret_cast<const bf16x8*>(st + state_at<NJB>(cb, 2 * m, L)));
+    a = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    b = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+  } else {
+    a = gld_nt(reinterpret_cast<const piece*>(st + state_at<NJB>(cb, 2 * m, L)));
+    b = gld_nt(reinterpret_cast<const piece*>(st + state_at<NJB>(cb, 2 * m + 1, L)));
+  }
+}
+template <typename E, int NJB>
+__device__ __forceinline__ typename Piece4<E>::type load_state_piece(const E* st, int cb, int jb, int L) {
+  return gld_nt(reinterpret_cast<const typename Piece4<E>::type*>(st + state_at<NJB>(cb, jb, L)));
+}
+template <typename E, int NJB>
+__device__ __forceinline__ void store_state_pair(E* st, int cb, int m, int L, f32x4 a, f32x4 b) {
+  static_assert(NJB % 2 == 0, "tiles pair up along dv");
+  if constexpr (sizeof(E) == 2) {
+    __builtin_nontemporal_store(join_bf16x4(to_bf16x4(a), to_bf16x4(b)),
+                                reinterpret_cast<bf16x8*>(st + state_at<NJB>(cb, 2 * m, L)));
+  } else {
+    gst_nt(st + state_at<NJB>(cb, 2 * m, L), a);
+    gst_nt(st + state_at<NJB>(cb, 2 * m + 1, L), b);
+  }
+}
+template <typename E, int NJB>
+__device__ __forceinline__ void store_state_piece(E* st, int cb, int jb, int L, f32x4 a) {
+  gst_nt(st + state_at<NJB>(cb, jb, L), a);
+}
 
 // --------------------------------------------------------------------------------------------
 // Wider stores of two adjacent 16-column blocks.  X and Y hold, in lane (n16, g4), row n16 and

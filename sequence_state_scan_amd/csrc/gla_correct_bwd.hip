@@ -166,17 +166,28 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
       // R_n = rowsum(S_{n-1} * G) for c = 16w + n16
       const long roff = (long)(w * 16 + n16) * DV + 4 * g4;
       float part = 0.f;
+      if (n > 0) {
+        const E* st = cst + (chunk0 + n - 1) * SS;
+        if constexpr (NJB % 2 == 0) {
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        piece sp;
-        if (n > 0) {
-          sp = gld_nt(reinterpret_cast<const piece*>(cst + (chunk0 + n - 1) * SS + state_tile(w, jb, NJB) + state_tile_row(n16, g4)));
+          for (int m = 0; m < NJB / 2; ++m) {
+            piece s0, s1;
+            load_state_pair<E, NJB>(st, w, m, state_lane_row(n16, g4), s0, s1);
+            part += piece_dot(s0, Gr[2 * m]) + piece_dot(s1, Gr[2 * m + 1]);
+          }
         } else {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) part += piece_dot(load_state_piece<E, NJB>(st, w, jb, state_lane_row(n16, g4)), Gr[jb]);
+        }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
           const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
+          piece sp;
 #pragma unroll
           for (int i = 0; i < 4; ++i) sp[i] = (E)x[i];
+          part += piece_dot(sp, Gr[jb]);
         }
-        part += piece_dot(sp, Gr[jb]);
       }
       part = sum_over_g4(part);
       // dk[t][c] += exp(r_t) (G v_t)[c];  dg[t][c] += E_n R_n + sum_{s < t in the chunk} k_s dk'_s

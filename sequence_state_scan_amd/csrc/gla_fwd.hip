@@ -220,9 +220,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
         }
+        if constexpr (JPW == 2) {  // the wave's two blocks are a pair of the tiled layout
+          store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), quad_transpose(S[0][kb]), quad_transpose(S[1][kb]));
+        } else {
 #pragma unroll
-        for (int jj = 0; jj < JPW; ++jj)
-          gst_nt(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4), quad_transpose(S[jj][kb]));
+          for (int jj = 0; jj < JPW; ++jj)
+            store_state_piece<E, NJB>(cs, kb, w * JPW + jj, state_lane_qt(n16, g4), quad_transpose(S[jj][kb]));
+        }
       }
     }
     __syncthreads();
@@ -330,10 +334,14 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj)
+      for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (JPW == 2) {
+          load_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), cprev[0][kb], cprev[1][kb]);
+        } else {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          cprev[jj][kb] = gld_nt(reinterpret_cast<const piece*>(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4)));
+          for (int jj = 0; jj < JPW; ++jj) cprev[jj][kb] = load_state_piece<E, NJB>(cs, kb, w * JPW + jj, state_lane_qt(n16, g4));
+        }
+      }
     }
     // ---- a_t = exp(sum of g from the segment start to t); q * a -> LDS ----
     int live = 0;
@@ -391,13 +399,17 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj)
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float ae = sAend[par][kb * 16 + 4 * g4 + (n16 & 3)];
+        if constexpr (JPW == 2) {
+          store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), widen(cprev[0][kb]) + ae * ST[0][kb],
+                                   widen(cprev[1][kb]) + ae * ST[1][kb]);
+        } else {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int c = kb * 16 + 4 * g4 + (n16 & 3);
-          gst_nt(cs + state_tile(kb, w * JPW + jj, NJB) + state_tile_qt(n16, g4),
-                 widen(cprev[jj][kb]) + sAend[par][c] * ST[jj][kb]);
+          for (int jj = 0; jj < JPW; ++jj)
+            store_state_piece<E, NJB>(cs, kb, w * JPW + jj, state_lane_qt(n16, g4), widen(cprev[jj][kb]) + ae * ST[jj][kb]);
         }
+      }
     }
   }
 }

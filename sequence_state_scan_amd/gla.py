@@ -121,8 +121,12 @@ def chunk_states_dense(cs):
     states (a copy; for inspection and tests, not used by any entry point)."""
     *lead, dk, dv = cs.shape
     L = len(lead)
-    t = cs.reshape(*lead, dk // 16, dv // 16, 4, 16, 4)  # tile row, tile column, j / 4, c, j % 4
-    return t.permute(*range(L), L, L + 3, L + 1, L + 2, L + 4).reshape(*lead, dk, dv)
+    if (dv // 16) % 2 == 1:
+        t = cs.reshape(*lead, dk // 16, dv // 16, 4, 16, 4)  # tile row, tile column, j / 4, c, j % 4
+        return t.permute(*range(L), L, L + 3, L + 1, L + 2, L + 4).reshape(*lead, dk, dv)
+    # tile row, pair of tile columns, j / 4 within the tile, c, tile of the pair, j % 4
+    t = cs.reshape(*lead, dk // 16, dv // 32, 4, 16, 2, 4)
+    return t.permute(*range(L), L, L + 3, L + 1, L + 4, L + 2, L + 5).reshape(*lead, dk, dv)
 
 
 def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg_state=None, seg_logdecay=None):

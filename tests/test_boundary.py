@@ -118,15 +118,22 @@ def test_binding_has_no_cpu_fallback():
         gla.gla_chunk_fwd(q, q, q, torch.zeros(1, 1, 64, 32), chunk=32, P=1)
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 256)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 16), (32, 64), (128, 256)])
 def test_chunk_state_tile_layout(dk, dv):
-    # the tiled chunk-state layout of include/gla.h, element by element: (c, j) of a state sits at
-    # (c // 16 * dv // 16 + j // 16) * 256 + (16 * (j % 16 // 4) + c % 16) * 4 + j % 4
+    # the tiled chunk-state layout of include/gla.h, element by element: (c, j) belongs to lane
+    # index L = 16 (j % 16 // 4) + c % 16 of tile (c // 16, j // 16); tiles pair up along dv when
+    # dv / 16 is even
     rng = torch.Generator().manual_seed(1)
     dense = torch.randn(2, 3, dk, dv, generator=rng)
-    tiled = torch.empty(2, 3, dk * dv)
+    tiled = torch.full((2, 3, dk * dv), float("nan"))
+    njb = dv // 16
     for c in range(dk):
         for j in range(dv):
-            off = (c // 16 * (dv // 16) + j // 16) * 256 + (16 * (j % 16 // 4) + c % 16) * 4 + j % 4
+            cb, jb, lane = c // 16, j // 16, 16 * (j % 16 // 4) + c % 16
+            if njb % 2 == 0:
+                off = (cb * njb + jb - jb % 2) * 256 + 8 * lane + 4 * (jb % 2) + j % 4
+            else:
+                off = (cb * njb + jb) * 256 + 4 * lane + j % 4
             tiled[:, :, off] = dense[:, :, c, j]
+    assert not torch.isnan(tiled).any()  # every offset is taken exactly once
     assert torch.equal(gla.chunk_states_dense(tiled.reshape(2, 3, dk, dv)), dense)
