@@ -16,9 +16,9 @@
 // and the chunk state over d_v.  dv contracts U over d_k instead, so once per chunk the waves
 // write exp(lam) U into LDS (as rows U[c][:], half of d_v at a time), and dv's tiles read it
 // back with the transposing load.  q, k, g, v and do are read from HBM once per chunk (q, k, g as
-// gate tiles of 16 tokens x 8 channels); the chunk state arrives in U's lane layout, whole tiles
-// of the tiled chunk-state layout; dq, dk and dv leave as merged pairs of 16-column tiles, 16
-// bytes per lane.
+// gate tiles of 16 tokens x 8 channels); the chunk state arrives in U's lane layout, a pair of
+// tiles of the tiled chunk-state layout per 16-byte load; dq, dk and dv leave as merged pairs of
+// 16-column tiles, 16 bytes per lane.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         const E* st = cst + (chunk0 + n - 1) * SS;
         if constexpr (NJB % 2 == 0) {
 #pragma unroll
-          for (int m = 0; m < NJB / 2; ++m) load_state_pair<E, NJB>(st, cb, m, state_lane_row(n16, g4), Sp[2 * m], Sp[2 * m + 1]);
+          for (int m = 0; m < NJB / 2; ++m)
+            load_state_pair<E, NJB>(st, cb, m, state_lane_row(n16, g4), Sp[2 * m], Sp[2 * m + 1]);
         } else {
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb) Sp[jb] = load_state_piece<E, NJB>(st, cb, jb, state_lane_row(n16, g4));

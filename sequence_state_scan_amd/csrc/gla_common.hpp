@@ -76,10 +76,11 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 x) {
 }
 
 // Streaming (nontemporal) global accesses.  Used only where one wave instruction covers whole
-// 128-byte lines: the rows of V and dO, and the chunk-state tiles (512 contiguous bytes).  There
-// the streaming policy raised throughput by a few percent on gfx950.  Accesses that cover half a
-// line per instruction (gate tiles, merged output pairs) were much slower with it, presumably
-// because the line is dropped before the other half arrives, so they keep the default policy.
+// 128-byte lines: the rows of V and dO, and the chunk-state tiles (512 or 1024 contiguous
+// bytes).  There the streaming policy raised throughput by a few percent on gfx950.  Accesses
+// that cover half a line per instruction (gate tiles, merged output pairs) were much slower with
+// it, presumably because the line is dropped before the other half arrives, so they keep the
+// default policy.
 template <typename T>
 __device__ __forceinline__ T gld_nt(const T* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void gst_nt(float* p, f32x4 x) { __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p)); }

@@ -177,7 +177,8 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
           }
         } else {
 #pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) part += piece_dot(load_state_piece<E, NJB>(st, w, jb, state_lane_row(n16, g4)), Gr[jb]);
+          for (int jb = 0; jb < NJB; ++jb)
+            part += piece_dot(load_state_piece<E, NJB>(st, w, jb, state_lane_row(n16, g4)), Gr[jb]);
         }
       } else {
 #pragma unroll

@@ -19,9 +19,10 @@ namespace gla {
 // One workgroup of NW waves = one (batch*head, segment) unit, all of d_v.  The state S (float32,
 // dk x dv) lives in accumulator registers for the whole segment: wave w owns JPW adjacent
 // 16-column blocks (jb = JPW w ..), so in bf16 its output tiles leave as 32-column pairs, 16 bytes
-// per lane.  After every chunk the state is also written out (chunk_states, element type E, each
-// 16x16 tile whole in the tiled chunk-state layout): the local chunk states the correction turns
-// into global ones and the backward reads.
+// per lane.  After every chunk the state is also written out (chunk_states, element type E, in the
+// tiled chunk-state layout; with two blocks per wave the pair of tiles of each 16-row block leaves
+// as 1024 contiguous bytes): the local chunk states the correction turns into global ones and the
+// backward reads.
 //
 // Per chunk: (1) every 16-lane row takes items of 16 tokens x 8 channels of q, k and g: the gate's
 // running sum comes from DPP scans across the 16 lanes (one token each) and the totals of the
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
           for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
         }
         if constexpr (JPW == 2) {  // the wave's two blocks are a pair of the tiled layout
-          store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), quad_transpose(S[0][kb]), quad_transpose(S[1][kb]));
+          store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), quad_transpose(S[0][kb]),
+                                   quad_transpose(S[1][kb]));
         } else {
 #pragma unroll
           for (int jj = 0; jj < JPW; ++jj)
@@ -339,7 +341,8 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
           load_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), cprev[0][kb], cprev[1][kb]);
         } else {
 #pragma unroll
-          for (int jj = 0; jj < JPW; ++jj) cprev[jj][kb] = load_state_piece<E, NJB>(cs, kb, w * JPW + jj, state_lane_qt(n16, g4));
+          for (int jj = 0; jj < JPW; ++jj)
+            cprev[jj][kb] = load_state_piece<E, NJB>(cs, kb, w * JPW + jj, state_lane_qt(n16, g4));
         }
       }
     }
