@@ -169,25 +169,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         static_assert(NKB % 2 == 0, "d_k a multiple of 32");
 #pragma unroll
         for (int pp = 0; pp < NKB / 2; ++pp) {
+          // merged, the lane's pieces of blocks 2pp and 2pp + 1 are the 8 adjacent rows
+          // 32 pp + pair_col(g4) + 0..7 of S: the Qbar fragment is one 16-byte read
           bf16x8 x[JPW];
 #pragma unroll
-          for (int jj = 0; jj < JPW; ++jj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              x[jj][i] = (bf16)S[jj][2 * pp][i];
-              x[jj][4 + i] = (bf16)S[jj][2 * pp + 1][i];
-            }
+          for (int jj = 0; jj < JPW; ++jj) x[jj] = merge_pair(to_bf16x4(S[jj][2 * pp]), to_bf16x4(S[jj][2 * pp + 1]));
 #pragma unroll
           for (int tT = 0; tT < NTT; ++tT) {
-            const E* yr = sQ + (tT * 16 + n16) * LDQ + 32 * pp + 4 * g4;
-            const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(yr);
-            const bf16x4 yhi = *reinterpret_cast<const bf16x4*>(yr + 16);
-            bf16x8 y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              y[i] = ylo[i];
-              y[4 + i] = yhi[i];
-            }
+            const bf16x8 y = *reinterpret_cast<const bf16x8*>(sQ + (tT * 16 + n16) * LDQ + 32 * pp + pair_col(g4));
 #pragma unroll
             for (int jj = 0; jj < JPW; ++jj) acc[jj][tT] = Mma<bf16>::mma(x[jj], y, acc[jj][tT]);
           }
