@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
           for (int tT = 0; tT < NTT; ++tT) {
             const int t = tT * 16 + n16;
             aq[tT] = mma_regX_e<E, 1>(aq[tT], sp, sdO + t * LDV + j0 * 16);
-            ak[tT] = mma_regX<E, 1>(ak[tT], ue, sV + t * LDV + j0 * 16);
+            ak[tT] = mma_regX<1>(ak[tT], ue, sV + t * LDV + j0 * 16);
           }
         }
       }

@@ -11,8 +11,9 @@
 //
 // Which physical k a slot holds only has to agree between A and B, so a state tile kept in
 // accumulator registers (lane holds S[4*g4 + i][n16] of each 16x16 block) can feed the A
-// operand directly: the lane's k-slots are taken as {16*kb + 4*g4 + i}, and the B operand
-// reads the same k from LDS (mma_regX below).
+// operand directly, and the B operand reads the same k from LDS.  In bf16 two such tiles are
+// merged first (merge_pair below): the lane's 8 k-slots are then 8 adjacent k, and the B
+// fragment is one 16-byte read.  fp32 takes the slots {16*kb + 4*g4 + i} (mma_regX).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -153,89 +154,31 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const E* X, int ldx, const E* Y,
   return acc;
 }
 
-// acc[m][n] += sum_k X[m][k] * Y[n][k] where X comes from NKB accumulator-layout register tiles:
-// R[kb][i] holds X[m = n16][k = 16*kb + 4*g4 + i].  Yrow points at Y's row n = n16 of this tile
-// (so the lane reads Y[n16][16*kb + 4*g4 + i]).
-template <typename E, int NKB>
-__device__ __forceinline__ f32x4 mma_regX(f32x4 acc, const f32x4 (&R)[NKB], const E* Yrow) {
+// fp32: acc[m][n] += sum_k X[m][k] * Y[n][k] where X comes from NKB accumulator-layout register
+// tiles: R[kb][i] holds X[m = n16][k = 16*kb + 4*g4 + i].  Yrow points at Y's row n = n16 of this
+// tile (so the lane reads Y[n16][16*kb + 4*g4 + i]).  (bf16 callers merge pairs of tiles with
+// merge_pair instead, so that their Y fragment is one 16-byte read.)
+template <int NKB>
+__device__ __forceinline__ f32x4 mma_regX(f32x4 acc, const f32x4 (&R)[NKB], const float* Yrow) {
   const int g4 = lane_id() >> 4;
-  if constexpr (sizeof(E) == 2) {
 #pragma unroll
-    for (int p = 0; p < NKB / 2; ++p) {
-      bf16x8 x, y;
-      const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 4 * g4);
-      const bf16x4 yhi = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 16 + 4 * g4);
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (bf16)R[2 * p][i];
-        x[4 + i] = (bf16)R[2 * p + 1][i];
-        y[i] = ylo[i];
-        y[4 + i] = yhi[i];
-      }
-      acc = Mma<bf16>::mma(x, y, acc);
-    }
-    if constexpr (NKB % 2 == 1) {
-      bf16x8 x, y;
-      const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 16 * (NKB - 1) + 4 * g4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (bf16)R[NKB - 1][i];
-        x[4 + i] = (bf16)0.f;
-        y[i] = ylo[i];
-        y[4 + i] = (bf16)0.f;
-      }
-      acc = Mma<bf16>::mma(x, y, acc);
-    }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc = Mma<float>::mma(R[kb][i], Yrow[16 * kb + 4 * g4 + i], acc);
-  }
+    for (int i = 0; i < 4; ++i) acc = Mma<float>::mma(R[kb][i], Yrow[16 * kb + 4 * g4 + i], acc);
   return acc;
 }
 
-// acc[tT] += X . Y_tT^T for NTT row blocks of Y at once, X from accumulator registers as in
-// mma_regX (lane supplies X[m = n16][k = 16kb + 4g4 + i]); the lane's Y row for block tT is
-// Y0 + tT * ldblk.  The k steps run outermost, so each X step is converted to the element type once.
-template <typename E, int NKB, int NTT>
-__device__ __forceinline__ void mma_regX_rows(f32x4 (&acc)[NTT], const f32x4 (&R)[NKB], const E* Y0, int ldblk) {
+// fp32: acc[tT] += X . Y_tT^T for NTT row blocks of Y at once, X from accumulator registers as in
+// mma_regX; the lane's Y row for block tT is Y0 + tT * ldblk.
+template <int NKB, int NTT>
+__device__ __forceinline__ void mma_regX_rows(f32x4 (&acc)[NTT], const f32x4 (&R)[NKB], const float* Y0, int ldblk) {
   const int g4 = lane_id() >> 4;
-  if constexpr (sizeof(E) == 2) {
 #pragma unroll
-    for (int p = 0; p < (NKB + 1) / 2; ++p) {
-      bf16x8 x;
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (bf16)R[2 * p][i];
-        x[4 + i] = 2 * p + 1 < NKB ? (bf16)R[2 * p + 1][i] : (bf16)0.f;
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int tT = 0; tT < NTT; ++tT) {
-        const E* Yrow = Y0 + tT * ldblk;
-        const bf16x4 ylo = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 4 * g4);
-        bf16x4 yhi;
-        if (2 * p + 1 < NKB) yhi = *reinterpret_cast<const bf16x4*>(Yrow + 32 * p + 16 + 4 * g4);
-        else yhi = bf16x4{};
-        bf16x8 y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y[i] = ylo[i];
-          y[4 + i] = yhi[i];
-        }
-        acc[tT] = Mma<bf16>::mma(x, y, acc[tT]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tT = 0; tT < NTT; ++tT)
-          acc[tT] = Mma<float>::mma(R[kb][i], (Y0 + tT * ldblk)[16 * kb + 4 * g4 + i], acc[tT]);
-  }
+      for (int tT = 0; tT < NTT; ++tT) acc[tT] = Mma<float>::mma(R[kb][i], (Y0 + tT * ldblk)[16 * kb + 4 * g4 + i], acc[tT]);
 }
 
 // Same as mma_regX, with X given as pieces already in the element type: R[kb] holds

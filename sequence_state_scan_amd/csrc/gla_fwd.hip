@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         }
       } else {
 #pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) mma_regX_rows<E, NKB, NTT>(acc[jj], S[jj], sQ + n16 * LDQ, 16 * LDQ);
+        for (int jj = 0; jj < JPW; ++jj) mma_regX_rows<NKB, NTT>(acc[jj], S[jj], sQ + n16 * LDQ, 16 * LDQ);
       }
       if constexpr (sizeof(E) == 2 && JPW == 2) {
 #pragma unroll
