@@ -256,6 +256,26 @@ def test_state_carry_across_calls():
     assert maxrel(as_f64(second["h_final"]), as_f64(full["h_final"])) <= TOL["bf16"]
 
 
+def test_gradient_carry_across_calls():
+    # streaming a sequence in two calls: the second half's backward first (no dh_T), then the first
+    # half's with dh_T = the second half's dh0; the gradients equal those of one call
+    d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 9, True, "weak")
+    x = {n: d[n].cuda() for n in ("q", "k", "v", "g", "do")}
+    half = lambda n, i: x[n][:, :, 1024 * i:1024 * (i + 1)].contiguous()
+    fwd = gla.zeco_forward(x["q"], x["k"], x["v"], x["g"], 64, 2, 2)
+    full = gla.zeco_backward(x["q"], x["k"], x["v"], x["g"], x["do"], fwd, 64, 2, 2)
+    f1 = gla.zeco_forward(half("q", 0), half("k", 0), half("v", 0), half("g", 0), 64, 1, 1)
+    f2 = gla.zeco_forward(half("q", 1), half("k", 1), half("v", 1), half("g", 1), 64, 1, 1, h0=f1["h_final"])
+    b2 = gla.zeco_backward(half("q", 1), half("k", 1), half("v", 1), half("g", 1), half("do", 1), f2, 64, 1, 1)
+    b1 = gla.zeco_backward(half("q", 0), half("k", 0), half("v", 0), half("g", 0), half("do", 0), f1, 64, 1, 1,
+                           dhT=b2["dh0"])
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dg"):
+        got = torch.cat([b1[n], b2[n]], dim=2)
+        assert maxrel(as_f64(got), as_f64(full[n])) <= TOL["bf16"], n
+    assert maxrel(as_f64(b1["dh0"]), as_f64(full["dh0"])) <= TOL["bf16"]
+
+
 def test_headline_workload_at_full_size():
     """64 segments of 16384 tokens, 4 heads, fwd+bwd, in the launch configuration the benchmark
     times.  The oracle runs head 0 in full (forward over all 1M tokens; exact backward over the last
