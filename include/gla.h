@@ -36,20 +36,27 @@
  *   - dtype selects the element type of q, k, v, o, do, dq, dk, dv: GLA_BF16 (bfloat16)
  *     or GLA_F32 (float32).  g, dg and every state are always float32.  bf16 products
  *     run on MFMA with float32 accumulation; f32 products on the f32 MFMA.
- *   - g must be <= 0 everywhere (a decay in (0, 1]).  gla_segment_correct relies on it to
- *     stop a segment's correction once every channel's cumulative decay has underflowed to
- *     exactly zero in float32.  Inside one chunk the kernels factor exp(b_t - b_s) as
- *     exp(b_t) * exp(-b_s) with b the in-chunk running sum of g, so each channel's decay
- *     over one chunk must stay above -87 (exp(87) is near the float32 limit); use a
- *     smaller chunk for stronger gates.
+ *   - g must be finite and <= 0 everywhere (a decay in (0, 1]); any such g is exact, however
+ *     strong the decay.  gla_segment_correct relies on g <= 0 to stop a segment's correction
+ *     once every channel's cumulative decay has underflowed to exactly zero in float32.  The
+ *     fast kernels factor exp(b_t - b_s) inside a chunk as exp(b_t) * exp(-b_s) (b the in-chunk
+ *     running sum of g) and take a chunk only if no channel decays by more than e^-40 over it;
+ *     a unit (b, h, segment) holding a stronger chunk is recomputed, in the same call, by
+ *     kernels that walk 16-token sub-blocks and sum the sub-block's own scores element by
+ *     element with exp(b_t - b_s), an exponent that is never positive.
  *   - stream is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
  *     it: no host synchronisation, no device-wide barrier.  The caller orders the calls.
- *   - Shapes, dtype, pointers and the supported-shape table are all checked on the host
- *     BEFORE any HIP call; a rejected call enqueues nothing.  A failed launch returns
- *     GLA_ERR_HIP.  gla_last_error() describes the last failure of the calling thread.
+ *   - Shapes, dtype, pointers, the workspace size and the supported-shape table are all checked
+ *     on the host BEFORE any HIP call; a rejected call enqueues nothing.  A failed launch
+ *     returns GLA_ERR_HIP.  gla_last_error() describes the last failure of the calling thread.
+ *   - gla_chunk_fwd and gla_chunk_bwd take a caller-owned device workspace of
+ *     gla_workspace_size() bytes (one int per unit: which units the exact kernels recompute).
+ *     The call writes it before reading it, so its contents on entry do not matter; it must
+ *     not be shared by calls that may run at the same time.
  *
  * Supported shapes (gla_supported() answers for a given combination):
- *   GLA_BF16: chunk in {32, 64}; dk in {32, 64, 128}; dv in {32, 64, 128, 256}
+ *   GLA_BF16: chunk in {16, 32, 64}; dk in {32, 64, 128}; dv in {32, 64, 128, 256}
+ *             (chunk 16 always runs the sub-block kernels: the bf16 MFMA contracts 32 tokens)
  *   GLA_F32:  chunk in {16, 32, 64}; dk in {16, 32}; dv in {16, 32}
  *   always:   B, H, T, P >= 1 (an empty sequence is rejected with GLA_ERR_INVALID_ARG);
  *             T % P == 0; (T / P) % chunk == 0
@@ -83,6 +90,14 @@ const char* gla_status_string(gla_status s);
 const char* gla_last_error(void);
 
 /*
+ * gla_workspace_size -- bytes of device workspace gla_chunk_fwd (which == GLA_FWD) or
+ * gla_chunk_bwd (which == GLA_BWD) needs for these arguments: one int per unit (b, h, segment),
+ * rounded up to 256 bytes.  Returns 0, with gla_last_error() set, if the arguments are rejected
+ * (the same checks as the call itself).  Any alignment of 4 bytes or more will do.
+ */
+size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype);
+
+/*
  * gla_chunk_fwd -- local pass (the first pass of ZeCO's Algorithm 1 as the pith.science referee
  * report describes it, including the HBM state store it makes, major comment 1; chunkwise
  * form: intra-chunk decay-masked attention plus the chunk state recurrence, with K/Lambda for
@@ -97,6 +112,7 @@ const char* gla_last_error(void);
  *   seg_logdecay[b,h,p,c]   = sum of g over the segment's tokens, float32
  * Inputs q, k, v (dtype), g (float32).  chunk is the tile length C of the chunkwise form.
  * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
+ * workspace: gla_workspace_size(GLA_FWD, ...) bytes of caller device memory (scratch).
  *
  * Tiled chunk-state layout (chunk_states only; every other state argument is row-major
  * [dk][dv]): a state is (dk/16) x (dv/16) tiles of 16 x 16.  Element (16 cb + c, 16 jb + j)
@@ -111,7 +127,7 @@ const char* gla_last_error(void);
 gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          void* o, void* chunk_states, float* seg_state, float* seg_logdecay,
                          int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
-                         void* stream);
+                         void* workspace, size_t workspace_size, void* stream);
 
 /*
  * gla_segment_scan -- decay-and-add scan over the P segments (All-Scan update,
@@ -195,12 +211,13 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
  *                    own outputs, float32 [dk][dv]
  * q, k, v, do, chunk_states and the outputs dq, dk_, dv_ share dtype.  Outputs are fully
  * overwritten and must not alias inputs.
+ * workspace: gla_workspace_size(GLA_BWD, ...) bytes of caller device memory (scratch).
  */
 gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                          const void* do_, const void* chunk_states, const float* seg_in,
                          void* dq, void* dk_, void* dv_, float* dg, float* seg_dstate,
                          int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
-                         void* stream);
+                         void* workspace, size_t workspace_size, void* stream);
 
 #ifdef __cplusplus
 }

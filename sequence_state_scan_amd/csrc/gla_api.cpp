@@ -36,14 +36,15 @@ bool in_list(int v, std::initializer_list<int> l) {
 
 bool shape_listed(int dtype, int dk, int dv, int chunk) {
   if (dtype == GLA_BF16)
-    return in_list(chunk, {32, 64}) && in_list(dk, {32, 64, 128}) && in_list(dv, {32, 64, 128, 256});
+    return in_list(chunk, {16, 32, 64}) && in_list(dk, {32, 64, 128}) && in_list(dv, {32, 64, 128, 256});
   if (dtype == GLA_F32)
     return in_list(chunk, {16, 32, 64}) && in_list(dk, {16, 32}) && in_list(dv, {16, 32});
   return false;
 }
 
 struct Kernels {
-  gla::launch_fn fwd, corr_fwd, bwd, corr_bwd;
+  gla::launch_fn fwd, corr_fwd, bwd, corr_bwd;  // fwd and bwd: the fast local kernels (null for bf16 chunk 16)
+  gla::launch_fn fwd_exact, bwd_exact;          // the exact sub-block kernels
 };
 
 bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
@@ -52,7 +53,16 @@ bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
   k->corr_fwd = gla::lookup_correct_fwd(dtype, chunk, dk, dv);
   k->bwd = gla::lookup_bwd(dtype, chunk, dk, dv);
   k->corr_bwd = gla::lookup_correct_bwd(dtype, chunk, dk, dv);
-  return k->fwd && k->corr_fwd && k->bwd && k->corr_bwd;
+  k->fwd_exact = gla::lookup_fwd_exact(dtype, dk, dv);
+  k->bwd_exact = gla::lookup_bwd_exact(dtype, dk, dv);
+  return (k->fwd != nullptr) == (k->bwd != nullptr) && k->corr_fwd && k->corr_bwd && k->fwd_exact && k->bwd_exact;
+}
+
+// Workspace of gla_chunk_fwd / gla_chunk_bwd: one int flag per unit (b, h, segment), rounded up
+// to 256 bytes.
+size_t workspace_bytes(int B, int H, int P) {
+  const size_t units = (size_t)B * H * P;
+  return (units * sizeof(int) + 255) / 256 * 256;
 }
 
 // Shape checks shared by the chunked entry points.
@@ -98,9 +108,21 @@ const char* gla_status_string(gla_status s) {
 
 const char* gla_last_error(void) { return g_last_error.c_str(); }
 
+size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype) {
+  if (which != GLA_FWD && which != GLA_BWD) {
+    fail(GLA_ERR_INVALID_ARG, "gla_workspace_size: unknown call %d", which);
+    return 0;
+  }
+  Kernels kern;
+  if (check_shape("gla_workspace_size", B, H, T, dk, dv, chunk, P, dtype, &kern) != GLA_OK) return 0;
+  ok();
+  return workspace_bytes(B, H, P);
+}
+
 gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g, void* o,
                          void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
-                         int dk, int dv, int chunk, int P, int dtype, void* stream) {
+                         int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
+                         void* stream) {
   const char* fn = "gla_chunk_fwd";
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
@@ -110,9 +132,21 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
                 "%s: q, k, v, g, o, chunk_states, seg_state and seg_logdecay must be non-null", fn);
   const void* ins[] = {q, k, v, g};
   for (const void* p : ins)
-    if (p == o || p == chunk_states) return fail(GLA_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
-  gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B * H, T, dk, dv, P};
-  return launched(fn, kern.fwd(&a, static_cast<hipStream_t>(stream)));
+    if (p == o || p == chunk_states || p == workspace)
+      return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
+  if (!workspace || workspace_size < workspace_bytes(B, H, P))
+    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
+                workspace_bytes(B, H, P), workspace ? workspace_size : (size_t)0);
+  gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, static_cast<int*>(workspace),
+                 B * H, T, dk, dv, P, chunk};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kern.fwd) {  // the fast kernel, then the exact one for the units it flagged
+    st = launched(fn, kern.fwd(&a, s));
+    if (st != GLA_OK) return st;
+  } else {
+    a.flags = nullptr;  // every unit
+  }
+  return launched(fn, kern.fwd_exact(&a, s));
 }
 
 gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
@@ -174,7 +208,7 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
 gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* do_,
                          const void* chunk_states, const float* seg_in, void* dq, void* dk_, void* dv_, float* dg,
                          float* seg_dstate, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
-                         void* stream) {
+                         void* workspace, size_t workspace_size, void* stream) {
   const char* fn = "gla_chunk_bwd";
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
@@ -183,11 +217,21 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
     return fail(GLA_ERR_INVALID_ARG, "%s: every pointer argument must be non-null", fn);
   const void* ins[] = {q, k, v, g, do_, chunk_states, seg_in};
   for (const void* p : ins)
-    if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate)
-      return fail(GLA_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
-  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate, B * H, T, dk, dv, P};
+    if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace)
+      return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
+  if (!workspace || workspace_size < workspace_bytes(B, H, P))
+    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
+                workspace_bytes(B, H, P), workspace ? workspace_size : (size_t)0);
+  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate, static_cast<int*>(workspace),
+                 B * H, T, dk, dv, P, chunk};
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return launched(fn, kern.bwd(&a, s));
+  if (kern.bwd) {  // the fast kernel, then the exact one for the units it flagged
+    st = launched(fn, kern.bwd(&a, s));
+    if (st != GLA_OK) return st;
+  } else {
+    a.flags = nullptr;  // every unit
+  }
+  return launched(fn, kern.bwd_exact(&a, s));
 }
 
 }  // extern "C"

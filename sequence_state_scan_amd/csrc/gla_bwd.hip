@@ -11,6 +11,9 @@
 // q dq - k dk equals rowsum(S_n * U_n) (the closed form of dg applied to that suffix), so no sum
 // ever runs over more than one chunk.
 //
+// A chunk in which some channel decays by more than kFastMinChunkLogDecay stops the unit: its flag
+// is set and the exact sub-block kernel (gla_exact.hip) recomputes the whole unit.
+//
 // One workgroup of NW waves walks each segment from its end.  Wave w keeps the 16 rows
 // c = 16w.. of U^T (all of d_v) in accumulator registers: they feed dq and dk, which contract U
 // and the chunk state over d_v.  dv contracts U over d_k instead, so once per chunk the waves
@@ -117,11 +120,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     prefetch_vd(n, tid);  // this chunk's V and dO
     // ---- (1) gate prefix sums, Qbar, Kbar, exp(b); V, dO -> LDS ----
+    int strong = 0;  // a channel decays by more than the factorisation takes in this chunk
     {
       float b[GT::RI][8], lam[8];
       pgt.prefix(tid, sTot, b, lam);
       if (GT::active(tid)) {
         const int x = GT::group_of(tid);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) strong |= lam[e] < kFastMinChunkLogDecay;
 #pragma unroll
         for (int r = 0; r < GT::RI; ++r) {
           float xq[8], xk[8], eb[8];
@@ -178,7 +184,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         }
       }
     }
-    __syncthreads();
+    if (__syncthreads_or(strong)) {  // the exact sub-block kernel redoes this unit
+      if (threadIdx.x == 0) a.flags[unit] = 1;
+      return;
+    }
     // ---- (2) dA[t][s] = dO[t] . V[s] and A[t][s] = Qbar[t] . Kbar[s], stored transposed, s <= t.
     // The tiles with sT <= tT are dealt to the waves longest first (the dA tiles contract over d_v,
     // the A tiles over d_k) in snake order, so the SIMDs get about the same MFMA work; the all-zero
@@ -392,6 +401,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[jb]);
   }
+  if (threadIdx.x == 0) a.flags[unit] = 0;
 }
 
 template <typename E, int C, int DK, int DV>

@@ -17,6 +17,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace gla {
 
@@ -570,5 +571,52 @@ template <> struct Vec8<float> {
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// --------------------------------------------------------------------------------------------
+// Exactness of the chunk factorisation.  The fast kernels factor exp(b_t - b_s) inside a chunk as
+// exp(b_t) * exp(-b_s) (K/Lambda).  They handle a chunk only when every channel's chunk decay is
+// at least kFastMinChunkLogDecay: exp(-b) then stays below exp(40) ~ 2.4e17 and exp(b) above
+// 4e-18, far from the float32 and bfloat16 limits.  A unit (b, h, segment) with any stronger chunk
+// is recorded in the per-unit flags and recomputed by the exact sub-block kernels.
+// --------------------------------------------------------------------------------------------
+constexpr float kFastMinChunkLogDecay = -40.f;
+
+// Broadcast lane S of each 16-lane row to the whole row (DPP row_newbcast).
+template <int S>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(S >= 0 && S < 16, "a lane of the row");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + S, 0xF, 0xF, false));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// acc[m][n] += sum_{k < 16} X[m][k] Y[n][k] (a contraction over one 16-token sub-block), with XTR /
+// YTR selecting the storage of X and Y as in frag_ld.  bf16 runs v_mfma_f32_16x16x32_bf16 with the
+// upper 16 k-slots zero: lanes g4 = 0, 1 supply k = 8 g4 .. 8 g4 + 7, lanes g4 = 2, 3 zeros (their
+// reads are pointed back at rows g4 - 2, inside the tile, and discarded).  The 16-deep
+// v_mfma_f32_16x16x16_bf16 is not used: when its result fed the next MFMA as the accumulator, the
+// upper two result registers read back stale now and then on gfx950.  f32 takes four
+// v_mfma_f32_16x16x4_f32.
+template <typename E, bool XTR, bool YTR>
+__device__ __forceinline__ f32x4 mma_k16(f32x4 acc, const E* X, int ldx, const E* Y, int ldy) {
+  if constexpr (sizeof(E) == 2) {
+    const int g4 = lane_id() >> 4, kk = -16 * (g4 >> 1);
+    bf16x8 x = frag_ld<E, XTR>(X, ldx, kk), y = frag_ld<E, YTR>(Y, ldy, kk);
+    if (g4 >= 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = y[e] = (E)0.f;
+    }
+    return Mma<bf16>::mma(x, y, acc);
+  } else {
+    return mma<E, XTR, YTR>(acc, X, ldx, Y, ldy, 0, 16);
+  }
+}
 
 }  // namespace gla

@@ -29,7 +29,8 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   constexpr int LDV = lds_ld<E>(DV), LDQ = lds_ld<E>(DK);
   constexpr int NJB = DV / 16, NCB = DK / 16, NTT = C / 16, NKB = DK / 16;
   constexpr int JPW = ceil_div(NJB, NW);
-  constexpr bool PAIRS = sizeof(E) == 2;  // dk and dv move as merged pairs of 16-column tiles
+  constexpr bool PAIRS = sizeof(E) == 2;  // dv moves as merged pairs of 16-column tiles
+  constexpr bool TPAIRS = PAIRS && NTT % 2 == 0;  // dk moves as merged pairs of 16-token tiles
   static_assert(NI <= NT, "one strided item of g and k per thread");
   static_assert(NCB <= NW, "one 16-row block of G per wave");
   static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
 #pragma unroll
       for (int tT = 0; tT < NTT; ++tT) {
         dgprev[tT] = load4(dg + (t0 + tT * 16 + n16) * DK + w * 16 + 4 * g4);
-        if constexpr (PAIRS) {
+        if constexpr (TPAIRS) {
           // token tiles tT - 1 and tT as one merged pair: lane rows 0 and 2 hold 8 channels of token
           // 16(tT - 1) + n16, rows 1 and 3 those of token 16 tT + n16
           if (tT & 1)
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
         }
         const long go = (t0 + t) * DK + w * 16 + 4 * g4;
         store4(dg + go, d);
-        if constexpr (PAIRS) {
+        if constexpr (TPAIRS) {
           dkn[tT & 1] = widen(dkprev[tT]) + ddk;
           if (tT & 1)
             *reinterpret_cast<bf16x8*>(dk + (t0 + 16 * (tT - 1 + (g4 & 1)) + n16) * DK + w * 16 + 8 * (g4 >> 1)) =
@@ -257,7 +258,7 @@ struct CorrectBwdLauncher {
 };
 
 launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv) {
-  return lookup_cdd<CorrectBwdLauncher>(dtype, chunk, dk, dv);
+  return lookup_cdd<CorrectBwdLauncher, Bf16CorrChunks>(dtype, chunk, dk, dv);
 }
 
 }  // namespace gla

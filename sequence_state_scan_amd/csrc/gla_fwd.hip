@@ -24,6 +24,10 @@ namespace gla {
 // as 1024 contiguous bytes): the local chunk states the correction turns into global ones and the
 // backward reads.
 //
+// A chunk in which some channel decays by more than kFastMinChunkLogDecay stops the unit: its flag
+// is set and the exact sub-block kernel (gla_exact.hip) recomputes the whole unit; otherwise the
+// flag is cleared at the end.
+//
 // Per chunk: (1) every 16-lane row takes items of 16 tokens x 8 channels of q, k and g: the gate's
 // running sum comes from DPP scans across the 16 lanes (one token each) and the totals of the
 // token-block sets meet in LDS, q and k are scaled and every tile is staged in LDS, and the next
@@ -91,6 +95,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     const long t0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     // ---- (1) gate prefix sums, Qbar, Kbar, Ktil, V -> LDS; request the next chunk ----
+    int strong = 0;  // a channel decays by more than the factorisation takes in this chunk
     {
       float b[GT::RI][8], lam[8];
       pgt.prefix(tid, sTot, b, lam);
@@ -98,7 +103,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
         const int x = GT::group_of(tid);
         float el[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
+        for (int e = 0; e < 8; ++e) {
+          el[e] = __expf(lam[e]);
+          strong |= lam[e] < kFastMinChunkLogDecay;
+        }
 #pragma unroll
         for (int r = 0; r < GT::RI; ++r) {
           float xq[8], xk[8], xkt[8];
@@ -128,7 +136,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the next chunk's loads after this chunk's staging
     if (n + 1 < nchunks) prefetch(n + 1, tid);
-    __syncthreads();
+    if (__syncthreads_or(strong)) {  // the exact sub-block kernel redoes this unit
+      if (threadIdx.x == 0) a.flags[unit] = 1;
+      return;
+    }
     // ---- (2) intra-chunk scores: A^T[s][t] = Kbar[s] . Qbar[t], kept for s <= t, stored as A[t][s] ----
     for (int idx = w; idx < NTT * NTT; idx += NW) {
       const int sT = idx / NTT, tT = idx - (idx / NTT) * NTT;
@@ -237,6 +248,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const int tid = threadIdx.x;
   if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
     store8(a.seg_logdecay + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
+  if (tid == 0) a.flags[unit] = 0;
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
@@ -430,7 +442,7 @@ launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv) {
   return lookup_cdd<FwdLocalLauncher>(dtype, chunk, dk, dv);
 }
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv) {
-  return lookup_cdd<CorrectFwdLauncher>(dtype, chunk, dk, dv);
+  return lookup_cdd<CorrectFwdLauncher, Bf16CorrChunks>(dtype, chunk, dk, dv);
 }
 
 }  // namespace gla

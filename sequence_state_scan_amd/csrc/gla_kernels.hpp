@@ -14,7 +14,8 @@ struct FwdArgs {  // gla_chunk_fwd
   void* o;
   void* chunk_states;  // [B][H][T/C][dk][dv], element type = dtype
   float *seg_state, *seg_logdecay;
-  int BH, T, Dk, Dv, P;
+  int* flags;  // [BH * P] per-unit flags in the workspace: 1 = recompute with the exact kernel
+  int BH, T, Dk, Dv, P, chunk;
 };
 
 struct BwdArgs {  // gla_chunk_bwd
@@ -25,7 +26,8 @@ struct BwdArgs {  // gla_chunk_bwd
   const float* seg_in;
   void *dq, *dk, *dv;
   float *dg, *seg_dstate;
-  int BH, T, Dk, Dv, P;
+  int* flags;  // as in FwdArgs
+  int BH, T, Dk, Dv, P, chunk;
 };
 
 struct CorrArgs {  // gla_segment_correct
@@ -41,7 +43,8 @@ typedef hipError_t (*launch_fn)(const void* args, hipStream_t stream);
 // Compile-time shape lists.  bf16: the MFMA K step is 32, so every contracted length
 // (chunk, d_k, d_v) is a multiple of 32.  f32 kernels exist for small heads only.
 template <int... Vs> struct IntList {};
-using Bf16Chunks = IntList<32, 64>;
+using Bf16Chunks = IntList<32, 64>;          // fast local kernels (the MFMA K step is 32 tokens)
+using Bf16CorrChunks = IntList<16, 32, 64>;  // corrections (their products contract over d_k, d_v)
 using Bf16Dk = IntList<32, 64, 128>;
 using Bf16Dv = IntList<32, 64, 128, 256>;
 using F32Chunks = IntList<16, 32, 64>;
@@ -59,6 +62,10 @@ launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_bwd(int dtype, int chunk, int dk, int dv);
 launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv);
+// The exact sub-block kernels (any chunk in {16, 32, 64}; chunk is an argument).  With flags
+// non-null only the units whose flag is 1 are processed, else every unit.
+launch_fn lookup_fwd_exact(int dtype, int dk, int dv);
+launch_fn lookup_bwd_exact(int dtype, int dk, int dv);
 
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
@@ -67,12 +74,28 @@ hipError_t launch_segment_scan_allgather(const float* seg_state, const float* se
                                          float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int reverse,
                                          hipStream_t stream);
 
+// Generic lookup over (dtype, dk, dv): Launcher<E, DK, DV>::run.
+template <template <typename, int, int> class Launcher>
+inline launch_fn lookup_dd(int dtype, int dk, int dv) {
+  launch_fn r = nullptr;
+  if (dtype == 1) {
+    dispatch_int(dk, Bf16Dk{}, [&](auto a) {
+      dispatch_int(dv, Bf16Dv{}, [&](auto b) { r = &Launcher<__bf16, a.value, b.value>::run; });
+    });
+  } else if (dtype == 0) {
+    dispatch_int(dk, F32Dk{}, [&](auto a) {
+      dispatch_int(dv, F32Dv{}, [&](auto b) { r = &Launcher<float, a.value, b.value>::run; });
+    });
+  }
+  return r;
+}
+
 // Generic lookup over (dtype, chunk, dk, dv): Launcher<E, C, DK, DV>::run.
-template <template <typename, int, int, int> class Launcher>
+template <template <typename, int, int, int> class Launcher, class Bf16C = Bf16Chunks>
 inline launch_fn lookup_cdd(int dtype, int chunk, int dk, int dv) {
   launch_fn r = nullptr;
   if (dtype == 1) {
-    dispatch_int(chunk, Bf16Chunks{}, [&](auto c) {
+    dispatch_int(chunk, Bf16C{}, [&](auto c) {
       dispatch_int(dk, Bf16Dk{}, [&](auto a) {
         dispatch_int(dv, Bf16Dv{}, [&](auto b) { r = &Launcher<__bf16, c.value, a.value, b.value>::run; });
       });

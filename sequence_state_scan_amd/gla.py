@@ -50,7 +50,10 @@ def load_library(path: str = LIB_PATH):
         lib.gla_status_string.restype = ctypes.c_char_p
         lib.gla_last_error.argtypes = []
         lib.gla_last_error.restype = ctypes.c_char_p
-        lib.gla_chunk_fwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, fp] + [i] * 8 + [vp]
+        sz = ctypes.c_size_t
+        lib.gla_workspace_size.argtypes = [i] * 9
+        lib.gla_workspace_size.restype = sz
+        lib.gla_chunk_fwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, fp] + [i] * 8 + [vp, sz, vp]
         lib.gla_chunk_fwd.restype = i
         lib.gla_segment_scan.argtypes = [fp, fp, fp, fp, fp] + [i] * 7 + [vp]
         lib.gla_segment_scan.restype = i
@@ -58,7 +61,7 @@ def load_library(path: str = LIB_PATH):
         lib.gla_segment_scan_allgather.restype = i
         lib.gla_segment_correct.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, fp] + [i] * 8 + [vp]
         lib.gla_segment_correct.restype = i
-        lib.gla_chunk_bwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, fp] + [i] * 8 + [vp]
+        lib.gla_chunk_bwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, fp] + [i] * 8 + [vp, sz, vp]
         lib.gla_chunk_bwd.restype = i
         if path == LIB_PATH:
             _lib = lib
@@ -105,13 +108,72 @@ def _f32(t, name):
     return _p(t)
 
 
+def _expect(t, name, shape, dtype, device, optional=False):
+    """Check one tensor argument against the shape, dtype and device the call implies.  The
+    kernels index every buffer from (B, H, T, dk, dv, P, chunk) alone, so a mismatch here would
+    read or write outside the buffer: it is rejected before anything reaches the library."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
 def _dims(q, v):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, T, d] tensors")
     B, H, T, dk = q.shape
     return B, H, T, dk, v.shape[-1]
+
+
+def _head_args(q, k, v, g, extra=()):
+    """(B, H, T, dk, dv) from q and v, after checking q, k, v, g and the (name, tensor, last dim)
+    triples of ``extra`` that share their [B, H, T] layout."""
+    B, H, T, dk, dv = _dims(q, v)
+    if not q.is_cuda:
+        raise ValueError("libgla works on device tensors only (got a %s tensor)" % q.device)
+    _dtype_code(q.dtype)
+    _expect(q, "q", (B, H, T, dk), q.dtype, q.device)
+    _expect(k, "k", (B, H, T, dk), q.dtype, q.device)
+    _expect(v, "v", (B, H, T, dv), q.dtype, q.device)
+    _expect(g, "g", (B, H, T, dk), torch.float32, q.device)
+    for name, t, d, dt in extra:
+        _expect(t, name, (B, H, T, d), dt, q.device)
+    return B, H, T, dk, dv
+
+
+def workspace_size(which: int, B: int, H: int, T: int, dk: int, dv: int, chunk: int, P: int, dtype) -> int:
+    """Bytes of workspace gla_chunk_fwd (which=GLA_FWD) or gla_chunk_bwd (GLA_BWD) needs."""
+    lib = load_library()
+    n = lib.gla_workspace_size(which, B, H, T, dk, dv, chunk, P, _dtype_code(dtype))
+    if n == 0:
+        raise GLAError(GLA_ERR_INVALID_ARG, "gla_workspace_size: %s" % lib.gla_last_error().decode())
+    return int(n)
+
+
+def _workspace(ws, which, B, H, T, dk, dv, chunk, P, dtype, device):
+    need = workspace_size(which, B, H, T, dk, dv, chunk, P, dtype)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError("workspace has %d bytes, the call needs %d" % (nbytes, need))
+    return ws, nbytes
 
 
 # ------------------------------------------------------------------------------------ C calls
@@ -129,31 +191,59 @@ def chunk_states_dense(cs):
     return t.permute(*range(L), L, L + 3, L + 1, L + 4, L + 2, L + 5).reshape(*lead, dk, dv)
 
 
-def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg_state=None, seg_logdecay=None):
+def _seg_shapes(B, H, T, dk, dv, chunk, P):
+    if P < 1 or chunk < 1 or T % P != 0 or (T // P) % chunk != 0:
+        raise ValueError("T=%d must split into P=%d segments of whole chunks of %d tokens" % (T, P, chunk))
+    return (B, H, T // chunk, dk, dv), (B, H, P, dk, dv), (B, H, P, dk)
+
+
+def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg_state=None, seg_logdecay=None,
+                  workspace=None):
     """Local pass.  Returns (o_local, chunk_states [B,H,T/chunk,dk,dv] (local, q's dtype, each
     state in the tiled layout: chunk_states_dense gives the row-major view),
-    seg_state [B,H,P,dk,dv], seg_logdecay [B,H,P,dk])."""
-    B, H, T, dk, dv = _dims(q, v)
+    seg_state [B,H,P,dk,dv], seg_logdecay [B,H,P,dk]).  ``workspace`` (a device tensor of at
+    least workspace_size(GLA_FWD, ...) bytes) is allocated when not given."""
+    B, H, T, dk, dv = _head_args(q, k, v, g)
+    cs_shape, st_shape, ld_shape = _seg_shapes(B, H, T, dk, dv, chunk, P)
+    dev, f32 = q.device, torch.float32
     o = torch.empty_like(v) if o is None else o
     if chunk_states is None:
-        chunk_states = torch.empty((B, H, T // chunk, dk, dv), device=q.device, dtype=q.dtype)
+        chunk_states = torch.empty(cs_shape, device=dev, dtype=q.dtype)
     if seg_state is None:
-        seg_state = torch.empty((B, H, P, dk, dv), device=q.device, dtype=torch.float32)
+        seg_state = torch.empty(st_shape, device=dev, dtype=f32)
     if seg_logdecay is None:
-        seg_logdecay = torch.empty((B, H, P, dk), device=q.device, dtype=torch.float32)
-    _check(load_library().gla_chunk_fwd(_p(q), _p(k), _p(v), _f32(g, "g"), _p(o), _p(chunk_states),
-                                        _f32(seg_state, "seg_state"), _f32(seg_logdecay, "seg_logdecay"),
-                                        B, H, T, dk, dv, chunk, P, _dtype_code(q.dtype), _stream(q)))
+        seg_logdecay = torch.empty(ld_shape, device=dev, dtype=f32)
+    _expect(o, "o", (B, H, T, dv), q.dtype, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(seg_state, "seg_state", st_shape, f32, dev)
+    _expect(seg_logdecay, "seg_logdecay", ld_shape, f32, dev)
+    ws, nbytes = _workspace(workspace, GLA_FWD, B, H, T, dk, dv, chunk, P, q.dtype, dev)
+    _check(load_library().gla_chunk_fwd(_p(q), _p(k), _p(v), _p(g), _p(o), _p(chunk_states), _p(seg_state),
+                                        _p(seg_logdecay), B, H, T, dk, dv, chunk, P, _dtype_code(q.dtype),
+                                        _p(ws), nbytes, _stream(q)))
     return o, chunk_states, seg_state, seg_logdecay
+
+
+def _scan_args(seg_state, seg_logdecay, h_boundary, seg_carry, h_out, want_h_out):
+    if not isinstance(seg_state, torch.Tensor) or seg_state.dim() != 5:
+        raise ValueError("seg_state must be a [B, H, P, dk, dv] tensor")
+    B, H, P, dk, dv = seg_state.shape
+    dev, f32 = seg_state.device, torch.float32
+    _expect(seg_state, "seg_state", (B, H, P, dk, dv), f32, dev)
+    _expect(seg_logdecay, "seg_logdecay", (B, H, P, dk), f32, dev)
+    _expect(h_boundary, "h_boundary", (B, H, dk, dv), f32, dev, optional=True)
+    seg_carry = torch.empty_like(seg_state) if seg_carry is None else seg_carry
+    _expect(seg_carry, "seg_carry", (B, H, P, dk, dv), f32, dev)
+    if h_out is None and want_h_out:
+        h_out = torch.empty((B, H, dk, dv), device=dev, dtype=f32)
+    _expect(h_out, "h_out", (B, H, dk, dv), f32, dev, optional=True)
+    return B, H, P, dk, dv, seg_carry, h_out
 
 
 def gla_segment_scan(seg_state, seg_logdecay, K: int, h_boundary=None, reverse: bool = False,
                      seg_carry=None, h_out=None, want_h_out: bool = True):
     """Decay-and-add scan over segments.  Returns (seg_carry, h_out)."""
-    B, H, P, dk, dv = seg_state.shape
-    seg_carry = torch.empty_like(seg_state) if seg_carry is None else seg_carry
-    if h_out is None and want_h_out:
-        h_out = torch.empty((B, H, dk, dv), device=seg_state.device, dtype=torch.float32)
+    B, H, P, dk, dv, seg_carry, h_out = _scan_args(seg_state, seg_logdecay, h_boundary, seg_carry, h_out, want_h_out)
     _check(load_library().gla_segment_scan(_f32(seg_state, "seg_state"), _f32(seg_logdecay, "seg_logdecay"),
                                            _f32(h_boundary, "h_boundary"), _f32(seg_carry, "seg_carry"),
                                            _f32(h_out, "h_out"), B, H, P, dk, dv, K, int(bool(reverse)),
@@ -165,10 +255,7 @@ def gla_segment_scan_allgather(seg_state, seg_logdecay, h_boundary=None, reverse
                                seg_carry=None, h_out=None, want_h_out: bool = True):
     """The same scan in the all-gather order (every carry combined directly from all the local
     states it depends on).  Returns (seg_carry, h_out)."""
-    B, H, P, dk, dv = seg_state.shape
-    seg_carry = torch.empty_like(seg_state) if seg_carry is None else seg_carry
-    if h_out is None and want_h_out:
-        h_out = torch.empty((B, H, dk, dv), device=seg_state.device, dtype=torch.float32)
+    B, H, P, dk, dv, seg_carry, h_out = _scan_args(seg_state, seg_logdecay, h_boundary, seg_carry, h_out, want_h_out)
     _check(load_library().gla_segment_scan_allgather(_f32(seg_state, "seg_state"), _f32(seg_logdecay, "seg_logdecay"),
                                                      _f32(h_boundary, "h_boundary"), _f32(seg_carry, "seg_carry"),
                                                      _f32(h_out, "h_out"), B, H, P, dk, dv, int(bool(reverse)),
@@ -188,10 +275,26 @@ def gla_segment_correct(mode: int, chunk: int, P: int, q=None, k=None, v=None, g
                         seg_grad=None, o=None, chunk_states=None, dk=None, dv=None, dg=None):
     """Cumulative-decay correction, in place: o and chunk_states for GLA_FWD; dk, dv, dg for
     GLA_BWD (which reads the global chunk_states)."""
+    if mode not in (GLA_FWD, GLA_BWD):
+        raise ValueError("mode must be GLA_FWD or GLA_BWD")
     ref_k = q if mode == GLA_FWD else k
     ref_v = o if mode == GLA_FWD else dv
-    B, H, T, d_k = ref_k.shape
-    d_v = ref_v.shape[-1]
+    if ref_k is None or ref_v is None:
+        raise ValueError("GLA_FWD needs q and o, GLA_BWD needs k and dv")
+    B, H, T, d_k, d_v = _dims(ref_k, ref_v)
+    dt, dev, f32 = ref_k.dtype, ref_k.device, torch.float32
+    cs_shape, st_shape, _ = _seg_shapes(B, H, T, d_k, d_v, chunk, P)
+    _expect(g, "g", (B, H, T, d_k), f32, dev)
+    _expect(seg_in, "seg_in", st_shape, f32, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, dt, dev)
+    if mode == GLA_FWD:
+        _expect(q, "q", (B, H, T, d_k), dt, dev)
+        _expect(o, "o", (B, H, T, d_v), dt, dev)
+    else:
+        for name, t, d in (("k", k, d_k), ("v", v, d_v), ("dk", dk, d_k), ("dv", dv, d_v)):
+            _expect(t, name, (B, H, T, d), dt, dev)
+        _expect(dg, "dg", (B, H, T, d_k), f32, dev)
+        _expect(seg_grad, "seg_grad", st_shape, f32, dev)
     _check(load_library().gla_segment_correct(mode, _p(q), _p(k), _p(v), _f32(g, "g"), _f32(seg_in, "seg_in"),
                                               _f32(seg_grad, "seg_grad"), _p(o), _p(chunk_states), _p(dk), _p(dv),
                                               _f32(dg, "dg"), B, H, T, d_k, d_v, chunk, P,
@@ -199,21 +302,30 @@ def gla_segment_correct(mode: int, chunk: int, P: int, q=None, k=None, v=None, g
 
 
 def gla_chunk_bwd(q, k, v, g, do, chunk_states, seg_in, chunk: int, P: int, dq=None, dk=None, dv=None,
-                  dg=None, seg_dstate=None):
+                  dg=None, seg_dstate=None, workspace=None):
     """Backward of every segment given the global chunk states and incoming segment states.
 
-    Returns (dq global, dk local, dv local, dg local, seg_dstate [B,H,P,dk,dv])."""
-    B, H, T, d_k, d_v = _dims(q, v)
+    Returns (dq global, dk local, dv local, dg local, seg_dstate [B,H,P,dk,dv]).  ``workspace`` as
+    in gla_chunk_fwd (GLA_BWD size)."""
+    B, H, T, d_k, d_v = _head_args(q, k, v, g, (("do", do, v.shape[-1], q.dtype),))
+    cs_shape, st_shape, _ = _seg_shapes(B, H, T, d_k, d_v, chunk, P)
+    dev, f32 = q.device, torch.float32
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     dg = torch.empty_like(g) if dg is None else dg
     if seg_dstate is None:
-        seg_dstate = torch.empty((B, H, P, d_k, d_v), device=q.device, dtype=torch.float32)
-    _check(load_library().gla_chunk_bwd(_p(q), _p(k), _p(v), _f32(g, "g"), _p(do), _p(chunk_states),
-                                        _f32(seg_in, "seg_in"), _p(dq), _p(dk), _p(dv), _f32(dg, "dg"),
-                                        _f32(seg_dstate, "seg_dstate"), B, H, T, d_k, d_v, chunk, P,
-                                        _dtype_code(q.dtype), _stream(q)))
+        seg_dstate = torch.empty(st_shape, device=dev, dtype=f32)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(seg_in, "seg_in", st_shape, f32, dev)
+    for name, t, d in (("dq", dq, d_k), ("dk", dk, d_k), ("dv", dv, d_v)):
+        _expect(t, name, (B, H, T, d), q.dtype, dev)
+    _expect(dg, "dg", (B, H, T, d_k), f32, dev)
+    _expect(seg_dstate, "seg_dstate", st_shape, f32, dev)
+    ws, nbytes = _workspace(workspace, GLA_BWD, B, H, T, d_k, d_v, chunk, P, q.dtype, dev)
+    _check(load_library().gla_chunk_bwd(_p(q), _p(k), _p(v), _p(g), _p(do), _p(chunk_states), _p(seg_in),
+                                        _p(dq), _p(dk), _p(dv), _p(dg), _p(seg_dstate), B, H, T, d_k, d_v, chunk,
+                                        P, _dtype_code(q.dtype), _p(ws), nbytes, _stream(q)))
     return dq, dk, dv, dg, seg_dstate
 
 

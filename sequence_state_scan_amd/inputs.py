@@ -27,6 +27,8 @@ Gate variants for stress cases (same draw, different map from x to g):
   "weak"          logsigmoid(x)/1024 (segments interact over thousands of tokens)
   "zero"          g = 0 (no decay at all)
   "strong"        -2 + 0.25*x clipped to <= 0 (about -2 per token: -64 over a 32-token chunk)
+  "strong5"       -5 + 0.25*x clipped to <= 0 (about -5 per token: -80 over 16 tokens, -320 over
+                  a 64-token chunk; every chunk then runs the exact sub-block kernels)
   "mixed"         even channels weak, odd channels strong
   "scalar"        one decay per token and head (the LASP / TNL setting): logsigmoid(x[t, 0])/16 of
                   the token's first draw, the same for every d_k channel (the kernels are unchanged:
@@ -104,6 +106,8 @@ def gate_from_normal(x: np.ndarray, gate: str) -> np.ndarray:
         g = np.zeros(x.shape, dtype=np.float64)
     elif gate == "strong":
         g = np.minimum(-2.0 + 0.25 * x.astype(np.float64), 0.0)
+    elif gate == "strong5":
+        g = np.minimum(-5.0 + 0.25 * x.astype(np.float64), 0.0)
     elif gate == "mixed":
         g = _logsigmoid64(x) / 1024.0
         strong = np.minimum(-2.0 + 0.25 * x.astype(np.float64), 0.0)

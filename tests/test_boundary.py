@@ -32,19 +32,23 @@ def test_status_strings(lib):
 
 
 def test_supported_shape_table(lib):
-    for dk, dv, c in [(128, 256, 64), (128, 128, 64), (64, 64, 32), (32, 32, 32), (128, 256, 32)]:
+    for dk, dv, c in [(128, 256, 64), (128, 128, 64), (64, 64, 32), (32, 32, 32), (128, 256, 32), (128, 256, 16),
+                      (32, 32, 16)]:
         assert lib.gla_supported(gla.GLA_BF16, dk, dv, c) == 1, (dk, dv, c)
     for dk, dv, c in [(16, 16, 16), (32, 32, 64), (16, 32, 32)]:
         assert lib.gla_supported(gla.GLA_F32, dk, dv, c) == 1, (dk, dv, c)
-    for dt, dk, dv, c in [(gla.GLA_BF16, 48, 64, 64), (gla.GLA_BF16, 128, 256, 16), (gla.GLA_BF16, 256, 256, 64),
+    for dt, dk, dv, c in [(gla.GLA_BF16, 48, 64, 64), (gla.GLA_BF16, 128, 256, 8), (gla.GLA_BF16, 256, 256, 64),
                           (gla.GLA_F32, 128, 128, 64), (gla.GLA_F32, 16, 16, 8), (7, 64, 64, 64)]:
         assert lib.gla_supported(dt, dk, dv, c) == 0, (dt, dk, dv, c)
 
 
+WS = ctypes.c_void_p(0xA000)  # a stand-in workspace pointer
+
+
 def _fwd(lib, B=1, H=1, T=256, dk=64, dv=64, chunk=64, P=1, dtype=gla.GLA_BF16, q=FAKE, o=ctypes.c_void_p(0x2000),
-         ss=FAKE):
+         ss=FAKE, ws=WS, wsb=1 << 20):
     return lib.gla_chunk_fwd(q, FAKE, FAKE, FAKE, o, ctypes.c_void_p(0x4000), ss, FAKE, B, H, T, dk, dv, chunk, P,
-                             dtype, NUL)
+                             dtype, ws, wsb, NUL)
 
 
 def test_chunk_fwd_host_checks(lib):
@@ -58,8 +62,13 @@ def test_chunk_fwd_host_checks(lib):
     assert _fwd(lib, ss=NUL) == E              # null output
     assert _fwd(lib, o=FAKE) == E              # o aliases q
     assert _fwd(lib, dk=48) == U               # valid but no kernel built
-    assert _fwd(lib, chunk=16) == U            # bf16 needs chunk >= 32
-    assert b"multiple" in lib.gla_last_error() or len(lib.gla_last_error()) > 0
+    assert _fwd(lib, dk=256) == U              # d_k above 128 has no kernel
+    assert _fwd(lib, chunk=8) == U             # no 8-token chunks
+    assert _fwd(lib, ws=NUL) == E              # the workspace is required
+    assert _fwd(lib, wsb=255) == E             # and must hold gla_workspace_size bytes
+    assert b"workspace" in lib.gla_last_error()
+    assert _fwd(lib, B=4, H=16, T=256 * 16, P=16, wsb=1023) == E  # 1024 bytes needed for 1024 units
+    assert _fwd(lib, ws=FAKE) == E             # the workspace aliases q
 
 
 def test_segment_scan_host_checks(lib):
@@ -105,11 +114,58 @@ def test_chunk_bwd_host_checks(lib):
                                  ctypes.c_void_p(0x1400), ctypes.c_void_p(0x1480), ctypes.c_void_p(0x1500), dq,
                                  ctypes.c_void_p(0x7000),
                                  ctypes.c_void_p(0x8000), dg, ctypes.c_void_p(0x9000),
-                                 1, 1, T, 64, 64, 64, P, gla.GLA_BF16, NUL)
+                                 1, 1, T, 64, 64, 64, P, gla.GLA_BF16, WS, 256, NUL)
     assert call(dq=FAKE) == E      # dq aliases q
     assert call(dg=NUL) == E
     assert call(P=3) == E
     assert call(T=0) == E          # empty sequence
+    ws_call = lambda ws, n: lib.gla_chunk_bwd(FAKE, ctypes.c_void_p(0x1100), ctypes.c_void_p(0x1200),  # noqa
+                                              ctypes.c_void_p(0x1300), ctypes.c_void_p(0x1400),
+                                              ctypes.c_void_p(0x1480), ctypes.c_void_p(0x1500),
+                                              ctypes.c_void_p(0x5000), ctypes.c_void_p(0x7000),
+                                              ctypes.c_void_p(0x8000), ctypes.c_void_p(0x6000),
+                                              ctypes.c_void_p(0x9000), 1, 1, 256, 64, 64, 64, 2, gla.GLA_BF16,
+                                              ws, n, NUL)
+    assert ws_call(NUL, 256) == E
+    assert ws_call(WS, 8) == E
+    assert ws_call(ctypes.c_void_p(0x1480), 256) == E  # the workspace aliases chunk_states
+
+
+def test_workspace_size(lib):
+    # one int flag per unit (b, h, segment), rounded up to 256 bytes, for either call
+    for B, H, T, P in [(1, 1, 256, 1), (1, 4, 1 << 20, 64), (3, 5, 64 * 77, 77), (8, 16, 4096, 64)]:
+        for which in (gla.GLA_FWD, gla.GLA_BWD):
+            n = lib.gla_workspace_size(which, B, H, T, 128, 256, 64 if T // P % 64 == 0 else 16, P, gla.GLA_BF16)
+            assert n == (4 * B * H * P + 255) // 256 * 256, (B, H, T, P)
+            assert n == gla.workspace_size(which, B, H, T, 128, 256, 64 if T // P % 64 == 0 else 16, P,
+                                           torch.bfloat16)
+    assert lib.gla_workspace_size(gla.GLA_FWD, 1, 1, 250, 64, 64, 64, 4, gla.GLA_BF16) == 0  # T % P
+    assert lib.gla_workspace_size(7, 1, 1, 256, 64, 64, 64, 4, gla.GLA_BF16) == 0            # unknown call
+    assert lib.gla_workspace_size(gla.GLA_BWD, 1, 1, 256, 48, 64, 64, 4, gla.GLA_BF16) == 0  # no kernel
+    with pytest.raises(gla.GLAError):
+        gla.workspace_size(gla.GLA_FWD, 1, 1, 250, 64, 64, 64, 4, torch.bfloat16)
+
+
+def test_binding_checks_every_tensor_against_the_call():
+    # the binding derives (B, H, T, dk, dv) from q and v and checks every other tensor against it
+    # before anything reaches the library (checked here on host tensors, one helper at a time)
+    q = torch.zeros(1, 2, 64, 32, dtype=torch.bfloat16)
+    gla._expect(q, "q", (1, 2, 64, 32), torch.bfloat16, q.device)
+    with pytest.raises(ValueError):
+        gla._expect(q, "k", (1, 2, 64, 16), torch.bfloat16, q.device)      # wrong d_k
+    with pytest.raises(TypeError):
+        gla._expect(q.float(), "k", (1, 2, 64, 32), torch.bfloat16, q.device)  # fp32 k next to bf16 q
+    with pytest.raises(ValueError):
+        gla._expect(q[:, :, ::2], "v", (1, 2, 32, 32), torch.bfloat16, q.device)  # not contiguous
+    with pytest.raises(ValueError):
+        gla._expect(None, "g", (1, 2, 64, 32), torch.float32, q.device)
+    gla._expect(None, "h_boundary", (1, 2, 32, 32), torch.float32, q.device, optional=True)
+    with pytest.raises(ValueError):
+        gla._expect(torch.zeros(1, 2, 64), "g", (1, 2, 64, 32), torch.float32, q.device)  # a per-head gate
+    assert gla._seg_shapes(1, 2, 256, 32, 64, 16, 4) == ((1, 2, 16, 32, 64), (1, 2, 4, 32, 64), (1, 2, 4, 32))
+    for T, P, C in [(250, 4, 16), (256, 3, 16), (256, 8, 64), (256, 0, 16)]:
+        with pytest.raises(ValueError):
+            gla._seg_shapes(1, 1, T, 32, 32, C, P)
 
 
 def test_binding_has_no_cpu_fallback():

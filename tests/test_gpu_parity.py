@@ -131,11 +131,36 @@ def test_fwdbwd_workload_h16():
 
 # ------------------------------------------------------------------------- stress and edge cases
 
-@pytest.mark.parametrize("gate", ["weak", "zero", "strong", "mixed", "scalar"])
-@pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 64, 128, 32), ("f32", 32, 16, 16)])
+@pytest.mark.parametrize("gate", ["weak", "zero", "strong", "strong5", "mixed", "scalar"])
+@pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 64, 128, 32), ("bf16", 64, 128, 64), ("bf16", 64, 128, 16),
+                                                ("f32", 32, 16, 16), ("f32", 32, 16, 32), ("f32", 32, 16, 64)])
 def test_gate_variants_with_boundary_states(gate, dtype, dk, dv, chunk):
-    # B*H = 3 units per segment (not a multiple of the 8-way XCD grouping), h0 and dL/dS_T given
+    # B*H = 3 units per segment (not a multiple of the 8-way XCD grouping), h0 and dL/dS_T given.
+    # strong (about -2 per token) and strong5 (about -5 per token, the survey's stress gate) decay
+    # far beyond what the chunk factorisation takes: those units run the exact sub-block kernels
     run_case(1, 3, 1024, dk, dv, chunk, 4, 2, dtype, bwd=True, gate=gate, seed=5, carry=True)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_strong_decay_at_the_headline_head_shape(chunk):
+    # g = min(-5 + x/4, 0) at d_k = 128, d_v = 256: the whole path, with boundary states, against the
+    # oracle (every chunk decays by e^-80 per 16 tokens or more)
+    run_case(1, 2, 2048, 128, 256, chunk, 4, 2, "bf16", bwd=True, gate="strong5", seed=13, carry=True)
+
+
+def test_fast_and_exact_units_in_one_call():
+    # a strong window inside some segments only: in one call the fast kernels take the other units
+    # and the exact kernels these (their flags set mid-segment, forward and backward)
+    B, H, T, dk, dv, chunk, P = 1, 3, 2048, 64, 128, 64, 4
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 17, True, "weak")
+    g = d["g"].clone()
+    g[0, 0, 300:340] = -3.0       # segment 0 of head 0, inside one chunk and across a chunk edge
+    g[0, 2, 1500:1530, ::3] = -4.0  # segment 2 of head 2, some channels only
+    d["g"] = g
+    x = dev(d)
+    gpu = gpu_pipeline(x, chunk, P, 2, True)
+    ref = oracle_pipeline(d, chunk, P, True)
+    check(gpu, ref, FWD_KEYS + BWD_KEYS, TOL["bf16"], "fast and exact units in one call")
 
 
 @pytest.mark.parametrize("dtype,dk,dv,chunk,P", [("bf16", 32, 32, 32, 8), ("bf16", 128, 256, 64, 3),
@@ -144,7 +169,7 @@ def test_one_chunk_per_segment_and_odd_counts(dtype, dk, dv, chunk, P):
     run_case(2, 1, chunk * P, dk, dv, chunk, P, 1, dtype, bwd=True, gate="weak", seed=6)
 
 
-SUPPORTED = ([("bf16", dk, dv, c) for dk in (32, 64, 128) for dv in (32, 64, 128, 256) for c in (32, 64)] +
+SUPPORTED = ([("bf16", dk, dv, c) for dk in (32, 64, 128) for dv in (32, 64, 128, 256) for c in (16, 32, 64)] +
              [("f32", dk, dv, c) for dk in (16, 32) for dv in (16, 32) for c in (16, 32, 64)])
 
 
@@ -164,9 +189,7 @@ def _mixed_cases(n=24, seed=2024):
         B, H, P = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 10))
         per_seg = int(rng.integers(1, 6))
         K = [k for k in (1, 2, 4, 8, 16) if dk % k == 0][int(rng.integers(0, 3))]
-        gate = ("logsigmoid16", "weak", "strong", "scalar")[int(rng.integers(4))]
-        if gate == "strong" and chunk > 32:
-            gate = "weak"  # the chunk form needs every chunk's decay above -87 (strong is about -2 per token)
+        gate = ("logsigmoid16", "weak", "strong", "scalar", "strong5")[int(rng.integers(5))]
         cases.append((B, H, P * per_seg * chunk, dk, dv, chunk, P, K, dtype, gate, int(rng.integers(1000))))
     return cases
 

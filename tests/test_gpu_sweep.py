@@ -3,7 +3,7 @@
 Each case draws together:
 - a compiled (dtype, d_k, d_v, chunk) instantiation;
 - B <= 3, H <= 5, P <= 11 segments of 1..6 chunks, and a scan block count K;
-- a gate recipe (the strong ones only with chunks of at most 32 tokens);
+- a gate recipe (the strong ones run the exact sub-block kernels);
 - whether boundary states h0 and dh_T are given.
 
 It runs 40 cases by default.  Set GLA_SWEEP to run more (GLA_SWEEP=2000 takes about four minutes
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 N = int(os.environ.get("GLA_SWEEP", "40"))
 SEED = int(os.environ.get("GLA_SWEEP_SEED", "7777"))
-GATES = ("logsigmoid16", "weak", "strong", "scalar", "zero", "mixed")
+GATES = ("logsigmoid16", "weak", "strong", "scalar", "zero", "mixed", "strong5")
 
 
 def _cases(n, seed):
@@ -32,8 +32,6 @@ def _cases(n, seed):
         per_seg = int(rng.integers(1, 7))
         K = [k for k in (1, 2, 4, 8, 16) if dk % k == 0][int(rng.integers(0, 3))]
         gate = GATES[int(rng.integers(len(GATES)))]
-        if gate in ("strong", "mixed") and chunk > 32:
-            gate = "weak"  # the chunk form needs every chunk's decay above -87 (strong is about -2 per token)
         out.append((B, H, P * per_seg * chunk, dk, dv, chunk, P, K, dtype, gate, int(rng.integers(1000)),
                     bool(rng.integers(2))))
     return out

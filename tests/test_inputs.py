@@ -41,9 +41,12 @@ def test_gate_distribution():
     assert g.dtype == np.float32 and np.all(g <= 0)
     # logsigmoid(N(0,1)) has mean about -0.806; divided by 16
     assert abs(g.mean() - (-0.806 / 16)) < 2e-3
-    for variant in ("weak", "zero", "strong", "mixed", "scalar"):
+    for variant in ("weak", "zero", "strong", "strong5", "mixed", "scalar"):
         gv = inputs.generate(1, 1, 256, 8, 8, "f32", seed=1, gate=variant)["g"].numpy()
         assert np.all(gv <= 0), variant
+    # the strong-decay stress gate: min(-5 + x/4, 0), about -5 per token
+    g5 = inputs.generate(1, 1, 4096, 16, 8, "f32", seed=3, gate="strong5")["g"].numpy()
+    assert abs(g5.mean() + 5.0) < 0.02 and g5.min() < -6.0
     # per-head scalar decay: one value per token, the same in every channel, drawn like the default
     gs = inputs.generate(1, 2, 512, 16, 8, "f32", seed=2, gate="scalar")["g"].numpy()
     assert np.all(gs == gs[..., :1]) and len(np.unique(gs[0, 0, :, 0])) > 500
