@@ -7,7 +7,12 @@ Inputs are drawn once (seeded, synthetic) and stay resident in HBM; every output
 buffer is allocated before the timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--gate VARIANT]
-                  [--no-cpu-baseline] [--copy-calibration] [--compare-orderings]
+                  [--no-cpu-baseline] [--no-extras] [--copy-calibration] [--compare-orderings]
+
+Besides the headline line, the default run adds (under "extras"): the same step with g = 0 (no
+decay, so the corrections never stop early: the full second pass), and the other fwd+bwd and
+forward workloads, each timed over 50 iterations with a 512 MiB scrub written between them
+(untimed) so that no input stays in the 256 MB last-level cache.
 
 --compare-orderings also times, on the same inputs, the two baseline orderings of the pages
 rendered on one GPU, and adds them under "orderings": the all-gather scan (LASP2's pattern,
@@ -89,18 +94,51 @@ def alg_bytes(w, part):
 
 
 def alg_flops(w, part):
-    """Algorithmic flops per token-head (the causal half of the intra-chunk products counted)."""
+    """Algorithmic flops (the causal half of the intra-chunk products counted).  part: "fwd" and
+    "bwd" are whole passes (local call plus correction); "chunk_fwd" and "chunk_bwd" the local
+    calls alone, whose kernels do not run the corrections' 2 dk dv / 4 dk dv per token-head."""
     th = w.B * w.H * w.T
     C, dk, dv = w.chunk, w.dk, w.dv
-    fwd = (C + 1) * (dk + dv) + 4 * dk * dv + (2 * dk * dv if w.P > 1 else 0)
-    bwd = (C + 1) * (3 * dk + 2 * dv) + 8 * dk * dv + (4 * dk * dv if w.P > 1 else 0)
-    return th * (fwd if part == "fwd" else bwd)
+    seg = w.P > 1
+    per = {
+        "chunk_fwd": (C + 1) * (dk + dv) + 4 * dk * dv,
+        "chunk_bwd": (C + 1) * (3 * dk + 2 * dv) + 8 * dk * dv,
+    }
+    per["fwd"] = per["chunk_fwd"] + (2 * dk * dv if seg else 0)
+    per["bwd"] = per["chunk_bwd"] + (4 * dk * dv if seg else 0)
+    return th * per[part]
 
 
-def cpu_baseline(w, gate, budget_s=15.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rate(oracle, a, w, threads, budget_s, min_tokens):
+    """Time the oracle's fwd+bwd on the first n tokens of one head, n grown until one run takes at
+    least 2/3 of budget_s (or covers the head).  Returns (seconds, tokens)."""
+    n = min_tokens
+    while True:
+        t1 = min(n, w.T)
+        sl = {k: v[:, :, :t1] for k, v in a.items()}
+        t0 = time.perf_counter()
+        oracle.gla_fwd(sl["q"], sl["k"], sl["v"], sl["g"], threads=threads)
+        oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["do"], threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s * 2 / 3 or t1 >= w.T:
+            return dt, t1
+        n = max(n + min_tokens, int(n * budget_s / max(dt, 1e-3)) // min_tokens * min_tokens)
+
+
+def cpu_baseline(w, gate, budget_s=15.0, budget_1t_s=5.0):
     """The oracle (plain float64 recurrence, fwd+bwd) on a bounded sample of the workload: head 0,
-    the first n segments, n grown until one run takes at least 2/3 of budget_s (or covers the head)."""
-    import numpy as np
+    the first n tokens (whole segments), timed with every host thread and again with one."""
     import oracle
     from sequence_state_scan_amd import inputs
     from sequence_state_scan_amd.inputs import as_f64
@@ -109,23 +147,15 @@ def cpu_baseline(w, gate, budget_s=15.0):
     threads = oracle.max_threads()
     h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, 0, w.dtype, 0, True, gate)
     a = {n: as_f64(t) for n, t in h.items()}
-    n, spent, tokens = 1, 0.0, 0
-    while True:
-        t1 = min(n * w.L, w.T)
-        sl = {k: v[:, :, :t1] for k, v in a.items()}
-        t0 = time.perf_counter()
-        oracle.gla_fwd(sl["q"], sl["k"], sl["v"], sl["g"])
-        oracle.gla_bwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["do"])
-        dt = time.perf_counter() - t0
-        spent, tokens = dt, t1
-        if dt >= budget_s * 2 / 3 or t1 >= w.T:
-            break
-        n = max(n + 1, int(n * budget_s / max(dt, 1e-3)))
-    # tokens of the workload per second: one head of `tokens` tokens is tokens / H workload tokens
+    spent, tokens = _oracle_rate(oracle, a, w, threads, budget_s, w.L)
+    spent1, tokens1 = _oracle_rate(oracle, a, w, 1, budget_1t_s, min(w.L, 1024))
+    # tokens of the workload per second: one head of `tokens` tokens is tokens / (B*H) workload tokens
     value = (tokens / (w.B * w.H)) / spent
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "head 0 of %d, first %d tokens (%d segments), fwd+bwd float64 token recurrence, %.2fs; "
-                      "value = tokens/(B*H)/time" % (w.B * w.H, tokens, tokens // w.L, spent)}
+            "cpu_model": cpu_model(), "value_1thread": (tokens1 / (w.B * w.H)) / spent1,
+            "sample": "head 0 of %d, first %d tokens, fwd+bwd float64 token recurrence, %.2fs on %d threads "
+                      "(1 thread: first %d tokens, %.2fs); value = tokens/(B*H)/time"
+                      % (w.B * w.H, tokens, spent, threads, tokens1, spent1)}
 
 
 def time_steps(torch, calls, steps, warmup, stream):
@@ -174,7 +204,7 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
     ld1 = torch.empty((B, H, 1, dk), device=q.device, dtype=f32)
     serial = [
         ("gla_chunk_fwd(P=1)", lambda: gla.gla_chunk_fwd(q, k, v, g, C, 1, o=buf["o"], chunk_states=buf["cs"],
-                                                          seg_state=one["S"], seg_logdecay=ld1)),
+                                                          seg_state=one["S"], seg_logdecay=ld1, workspace=buf["ws"])),
         ("gla_segment_scan(P=1)", lambda: gla.gla_segment_scan(one["S"], ld1, K, seg_carry=one["S_in"],
                                                                 h_out=buf["h_fin"])),
         ("gla_segment_correct(FWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, 1, q=q, g=g,
@@ -182,7 +212,7 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
                                                                            chunk_states=buf["cs"])),
         ("gla_chunk_bwd(P=1)", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], one["S_in"], C, 1,
                                                           dq=buf["dq"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"],
-                                                          seg_dstate=one["D"])),
+                                                          seg_dstate=one["D"], workspace=buf["ws"])),
         ("gla_segment_scan(reverse, P=1)", lambda: gla.gla_segment_scan(one["D"], ld1, K, reverse=True,
                                                                          seg_carry=one["G"], h_out=buf["dh0"])),
         ("gla_segment_correct(BWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, 1, k=k, v=v, g=g,
@@ -204,6 +234,107 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
     return res
 
 
+def path_buffers(torch, gla, w, dev, edt):
+    """Every output and intermediate of one fwd+bwd step, and the two calls' workspaces, allocated
+    before anything is timed."""
+    B, H, T, dk, dv, C, P = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P
+    f32 = torch.float32
+    st = (B, H, P, dk, dv)
+    ws = max(gla.workspace_size(gla.GLA_FWD, B, H, T, dk, dv, C, P, edt),
+             gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, C, P, edt))
+    return {
+        "o": torch.empty((B, H, T, dv), device=dev, dtype=edt),
+        "cs": torch.empty((B, H, T // C, dk, dv), device=dev, dtype=edt),
+        "S_loc": torch.empty(st, device=dev, dtype=f32), "ld": torch.empty((B, H, P, dk), device=dev, dtype=f32),
+        "S_in": torch.empty(st, device=dev, dtype=f32), "h_fin": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
+        "dq": torch.empty((B, H, T, dk), device=dev, dtype=edt), "dk": torch.empty((B, H, T, dk), device=dev, dtype=edt),
+        "dv": torch.empty((B, H, T, dv), device=dev, dtype=edt), "dg": torch.empty((B, H, T, dk), device=dev, dtype=f32),
+        "D": torch.empty(st, device=dev, dtype=f32), "G": torch.empty(st, device=dev, dtype=f32),
+        "dh0": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
+        "ws": torch.empty(ws, device=dev, dtype=torch.uint8),
+    }
+
+
+def path_calls(gla, w, x, buf, bwd=True):
+    """The calls of one step: the forward chain, and with bwd the backward chain."""
+    C, P, K = w.chunk, w.P, w.K
+    q, k, v, g = x["q"], x["k"], x["v"], x["g"]
+    calls = [
+        ("gla_chunk_fwd", lambda: gla.gla_chunk_fwd(q, k, v, g, C, P, o=buf["o"], chunk_states=buf["cs"],
+                                                     seg_state=buf["S_loc"], seg_logdecay=buf["ld"],
+                                                     workspace=buf["ws"])),
+        ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
+                                                           h_out=buf["h_fin"])),
+        ("gla_segment_correct(FWD)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, P, q=q, g=g, seg_in=buf["S_in"],
+                                                                      o=buf["o"], chunk_states=buf["cs"])),
+    ]
+    if bwd:
+        do = x["do"]
+        calls += [
+            ("gla_chunk_bwd", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], buf["S_in"], C, P, dq=buf["dq"],
+                                                         dk=buf["dk"], dv=buf["dv"], dg=buf["dg"], seg_dstate=buf["D"],
+                                                         workspace=buf["ws"])),
+            ("gla_segment_scan(reverse)", lambda: gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True,
+                                                                        seg_carry=buf["G"], h_out=buf["dh0"])),
+            ("gla_segment_correct(BWD)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, P, k=k, v=v, g=g,
+                                                                          seg_in=buf["S_in"], seg_grad=buf["G"],
+                                                                          chunk_states=buf["cs"], dk=buf["dk"],
+                                                                          dv=buf["dv"], dg=buf["dg"])),
+        ]
+    return calls
+
+
+def time_scrubbed(torch, calls, iters, warmup, stream, scrub):
+    """Time each of `iters` steps on its own, with `scrub` (a large buffer) overwritten between them
+    outside the timed events, so that no input is left in the last-level cache.  Returns
+    (mean ms, median ms, mean ms per call)."""
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(iters)]
+    for it in range(iters):
+        scrub.add_(1)
+        for i, (_, fn) in enumerate(calls):
+            ev[it][i][0].record(stream)
+            fn()
+            ev[it][i][1].record(stream)
+    torch.cuda.synchronize()
+    steps = sorted(sum(ev[it][i][0].elapsed_time(ev[it][i][1]) for i in range(len(calls))) for it in range(iters))
+    per_call = {name: sum(ev[it][i][0].elapsed_time(ev[it][i][1]) for it in range(iters)) / iters
+                for i, (name, _) in enumerate(calls)}
+    return sum(steps) / iters, steps[iters // 2], per_call
+
+
+def other_workloads(torch, gla, inputs, dev, stream, names, iters=50, warmup=5):
+    """The remaining fwd+bwd and forward workloads at full size, each step timed alone with a
+    512 MiB scrub between steps."""
+    scrub = torch.zeros(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+    out = {}
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        d = inputs.generate_workload(w, bwd=w.bwd)
+        x = {n: t.to(dev) for n, t in d.items()}
+        del d
+        buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
+        calls = path_calls(gla, w, x, buf, bwd=w.bwd)
+        mean, med, per_call = time_scrubbed(torch, calls, iters, warmup, stream, scrub)
+        ab = alg_bytes(w, "fwd") + (alg_bytes(w, "bwd") if w.bwd else 0)
+        af = alg_flops(w, "fwd") + (alg_flops(w, "bwd") if w.bwd else 0)
+        out[name] = {
+            "pass": "fwd+bwd" if w.bwd else "fwd", "tokens_per_s": round(w.B * w.T / (mean / 1e3), 1),
+            "ms_mean": round(mean, 4), "ms_median": round(med, 4), "iters": iters,
+            "hbm_frac": round(ab / (mean / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(af / (mean / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_bytes": ab,
+            "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},
+        }
+        log("%s: %.4f ms mean (%.4f median), %.3f of HBM peak" % (name, mean, med, out[name]["hbm_frac"]))
+        del x, buf, calls
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +343,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--gate", default="logsigmoid16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline step (no g = 0 step, no other workloads)")
     ap.add_argument("--compare-orderings", action="store_true",
                     help="also time the all-gather scan and the serial chain (P = 1) on the same inputs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -241,38 +374,8 @@ def main():
     log("inputs %s drawn and uploaded in %.1fs" % (w.name, time.time() - t))
 
     B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
-    f32, edt = torch.float32, x["q"].dtype
-    buf = {
-        "o": torch.empty_like(x["v"]),
-        "cs": torch.empty((B, H, T // C, dk, dv), device=dev, dtype=edt),
-        "S_loc": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
-        "ld": torch.empty((B, H, P, dk), device=dev, dtype=f32),
-        "S_in": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
-        "h_fin": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
-        "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
-        "dg": torch.empty_like(x["g"]),
-        "D": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
-        "G": torch.empty((B, H, P, dk, dv), device=dev, dtype=f32),
-        "dh0": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
-    }
-    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
-
-    calls = [
-        ("gla_chunk_fwd", lambda: gla.gla_chunk_fwd(q, k, v, g, C, P, o=buf["o"], chunk_states=buf["cs"],
-                                                     seg_state=buf["S_loc"], seg_logdecay=buf["ld"])),
-        ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
-                                                           h_out=buf["h_fin"])),
-        ("gla_segment_correct(FWD)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, P, q=q, g=g, seg_in=buf["S_in"],
-                                                                      o=buf["o"], chunk_states=buf["cs"])),
-        ("gla_chunk_bwd", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], buf["S_in"], C, P, dq=buf["dq"],
-                                                     dk=buf["dk"], dv=buf["dv"], dg=buf["dg"], seg_dstate=buf["D"])),
-        ("gla_segment_scan(reverse)", lambda: gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True,
-                                                                    seg_carry=buf["G"], h_out=buf["dh0"])),
-        ("gla_segment_correct(BWD)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, P, k=k, v=v, g=g,
-                                                                      seg_in=buf["S_in"], seg_grad=buf["G"],
-                                                                      chunk_states=buf["cs"], dk=buf["dk"],
-                                                                      dv=buf["dv"], dg=buf["dg"])),
-    ]
+    buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
+    calls = path_calls(gla, w, x, buf)
 
     if args.copy_calibration:
         src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -290,9 +393,9 @@ def main():
     # the dominant call and its roofline (algorithmic bytes of that call / its mean duration)
     dom = max(per_call, key=per_call.get)
     if dom == "gla_chunk_bwd":
-        dom_bytes, dom_flops = alg_bytes(w, "chunk_bwd"), alg_flops(w, "bwd")
+        dom_bytes, dom_flops = alg_bytes(w, "chunk_bwd"), alg_flops(w, "chunk_bwd")
     elif dom == "gla_chunk_fwd":
-        dom_bytes, dom_flops = alg_bytes(w, "fwd"), alg_flops(w, "fwd")
+        dom_bytes, dom_flops = alg_bytes(w, "fwd"), alg_flops(w, "chunk_fwd")
     else:
         dom_bytes, dom_flops = None, None
     roof = None
@@ -313,6 +416,24 @@ def main():
     if args.compare_orderings:
         orderings = compare_orderings(torch, gla, w, x, buf, stream, ms_step, per_call)
 
+    extras = None
+    if not args.no_extras and w.name == inputs.HEADLINE:
+        # the same step with g = 0: no decay, so both corrections run over every chunk
+        x0 = dict(x)
+        x0["g"] = torch.zeros_like(x["g"])
+        ms0, pc0, _ = time_steps(torch, path_calls(gla, w, x0, buf), 10, 3, stream)
+        del x0
+        log("g = 0: %.4f ms per step" % ms0)
+        extras = {"no_decay_step": {
+            "gate": "zero", "ms_per_step": round(ms0, 4), "tokens_per_s": round(tokens / (ms0 / 1e3), 1),
+            "hbm_frac": round(step_bytes / (ms0 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0.items()}}}
+        del x, buf, calls
+        torch.cuda.empty_cache()
+        extras["workloads"] = other_workloads(torch, gla, inputs, dev, stream,
+                                              [n for n in inputs.WORKLOADS if n != w.name and
+                                               inputs.WORKLOADS[n].dtype == "bf16"])
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.time()
@@ -332,6 +453,8 @@ def main():
     }
     if orderings is not None:
         out["orderings"] = orderings
+    if extras is not None:
+        out["extras"] = extras
     print(json.dumps(out), flush=True)
 
 
