@@ -130,6 +130,21 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_size, void* stream);
 
 /*
+ * gla_chunk_fwd_noalloc -- gla_chunk_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, results and checks without the workspace, which here is a library-owned device
+ * array of 256 KiB on each GPU (one int per unit), looked up once per device and kept until the
+ * process ends.  The call allocates nothing.  B*H*P above 65536 is rejected with
+ * GLA_ERR_INVALID_ARG before any HIP call.  The array's contents are written before they are
+ * read, so nothing needs clearing between calls; calls that may run at the same time on one GPU
+ * (two streams, two threads) share the array and race.
+ */
+gla_status gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 void* o, void* chunk_states, float* seg_state, float* seg_logdecay,
+                                 int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                                 void* stream);
+
+/*
  * gla_segment_scan -- decay-and-add scan over the P segments (All-Scan update,
  * pith.science "What carries the argument"), on each of K blocks of dk/K state rows
  * independently (the results do not depend on K, bit for bit).

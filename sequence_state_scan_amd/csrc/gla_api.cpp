@@ -12,19 +12,27 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local gla_status g_last_status = GLA_OK;
+
+gla_status vfail(gla_status s, const char* fmt, va_list ap) {
+  char buf[512];
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  g_last_error = buf;
+  g_last_status = s;
+  return s;
+}
 
 gla_status fail(gla_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vfail(s, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return s;
 }
 
 gla_status ok() {
   g_last_error.clear();
+  g_last_status = GLA_OK;
   return GLA_OK;
 }
 
@@ -88,6 +96,17 @@ gla_status launched(const char* fn, hipError_t e) {
 }
 
 }  // namespace
+
+namespace gla {
+gla_status set_error(gla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(s, fmt, ap);
+  va_end(ap);
+  return s;
+}
+gla_status last_status() { return g_last_status; }
+}  // namespace gla
 
 extern "C" {
 

@@ -3,6 +3,8 @@
 #pragma once
 #include <hip/hip_runtime_api.h>
 
+#include "gla.h"
+
 #include <type_traits>
 #include <utility>
 
@@ -39,6 +41,13 @@ struct CorrArgs {  // gla_segment_correct
 };
 
 typedef hipError_t (*launch_fn)(const void* args, hipStream_t stream);
+
+// Units (b, h, segment) the static scratch of gla_chunk_fwd_noalloc holds flags for (256 KiB).
+constexpr int kStaticUnits = 65536;
+
+// The calling thread's last-error record of the C ABI (gla_last_error): set it, and read its status.
+gla_status set_error(gla_status s, const char* fmt, ...);
+gla_status last_status();
 
 // Compile-time shape lists.  bf16: the MFMA K step is 32, so every contracted length
 // (chunk, d_k, d_v) is a multiple of 32.  f32 kernels exist for small heads only.

@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH):
         lib.gla_workspace_size.restype = sz
         lib.gla_chunk_fwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, fp] + [i] * 8 + [vp, sz, vp]
         lib.gla_chunk_fwd.restype = i
+        lib.gla_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, vp, vp, fp, fp] + [i] * 8 + [vp]
+        lib.gla_chunk_fwd_noalloc.restype = i
         lib.gla_segment_scan.argtypes = [fp, fp, fp, fp, fp] + [i] * 7 + [vp]
         lib.gla_segment_scan.restype = i
         lib.gla_segment_scan_allgather.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
@@ -221,6 +223,22 @@ def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg
     _check(load_library().gla_chunk_fwd(_p(q), _p(k), _p(v), _p(g), _p(o), _p(chunk_states), _p(seg_state),
                                         _p(seg_logdecay), B, H, T, dk, dv, chunk, P, _dtype_code(q.dtype),
                                         _p(ws), nbytes, _stream(q)))
+    return o, chunk_states, seg_state, seg_logdecay
+
+
+def gla_chunk_fwd_noalloc(q, k, v, g, chunk: int, P: int, o, chunk_states, seg_state, seg_logdecay):
+    """gla_chunk_fwd without a workspace (the library's static one): every output is the caller's
+    and must be given; nothing is allocated."""
+    B, H, T, dk, dv = _head_args(q, k, v, g)
+    cs_shape, st_shape, ld_shape = _seg_shapes(B, H, T, dk, dv, chunk, P)
+    dev, f32 = q.device, torch.float32
+    _expect(o, "o", (B, H, T, dv), q.dtype, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(seg_state, "seg_state", st_shape, f32, dev)
+    _expect(seg_logdecay, "seg_logdecay", ld_shape, f32, dev)
+    _check(load_library().gla_chunk_fwd_noalloc(_p(q), _p(k), _p(v), _p(g), _p(o), _p(chunk_states), _p(seg_state),
+                                                _p(seg_logdecay), B, H, T, dk, dv, chunk, P, _dtype_code(q.dtype),
+                                                _stream(q)))
     return o, chunk_states, seg_state, seg_logdecay
 
 
