@@ -345,6 +345,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step (no g = 0 step, no other workloads)")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="time the step with the sequences split over this many streams (zeco_step_streams)")
+    ap.add_argument("--stagger", action="store_true",
+                    help="with --streams: each group waits for the previous group's local pass")
     ap.add_argument("--compare-orderings", action="store_true",
                     help="also time the all-gather scan and the serial chain (P = 1) on the same inputs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -376,6 +380,11 @@ def main():
     B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
     buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
     calls = path_calls(gla, w, x, buf)
+    if args.streams > 1:
+        sbuf = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, args.streams)
+        calls = [("zeco_step_streams(%d)" % args.streams,
+                  lambda: gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, args.streams,
+                                                out=sbuf, stagger=args.stagger))]
 
     if args.copy_calibration:
         src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
@@ -391,7 +400,7 @@ def main():
     value = tokens / (ms_step / 1e3)
 
     # the dominant call and its roofline (algorithmic bytes of that call / its mean duration)
-    dom = max(per_call, key=per_call.get)
+    dom = max(per_call, key=per_call.get) if args.streams == 1 else None
     if dom == "gla_chunk_bwd":
         dom_bytes, dom_flops = alg_bytes(w, "chunk_bwd"), alg_flops(w, "chunk_bwd")
     elif dom == "gla_chunk_fwd":
@@ -428,6 +437,15 @@ def main():
             "gate": "zero", "ms_per_step": round(ms0, 4), "tokens_per_s": round(tokens / (ms0 / 1e3), 1),
             "hbm_frac": round(step_bytes / (ms0 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0.items()}}}
+        if args.streams == 1:
+            # the same step with the heads split over two streams (the scans and corrections of one
+            # half can run beside the local passes of the other)
+            sbuf = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, 2)
+            ms2, _, _ = time_steps(torch, [("two streams", lambda: gla.zeco_step_streams(
+                x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, 2, out=sbuf))], 10, 3, stream)
+            del sbuf
+            log("two streams: %.4f ms per step" % ms2)
+            extras["two_stream_step"] = {"ms_per_step": round(ms2, 4), "tokens_per_s": round(tokens / (ms2 / 1e3), 1)}
         del x, buf, calls
         torch.cuda.empty_cache()
         extras["workloads"] = other_workloads(torch, gla, inputs, dev, stream,
@@ -445,7 +463,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C, "P": P, "K": K,
-                   "segment_tokens": w.L, "gate": args.gate},
+                   "segment_tokens": w.L, "gate": args.gate, "streams": args.streams,
+                   "stagger": bool(args.stagger)},
         "roofline": roof, "cpu_baseline": cpu,
         "step_roofline": step_roof,
         "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},

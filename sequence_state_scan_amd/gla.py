@@ -369,3 +369,98 @@ def zeco_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=Non
     gla_segment_correct(GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=fwd["seg_in"], seg_grad=seg_grad,
                         chunk_states=fwd["chunk_states"], dk=dk, dv=dv, dg=dg)
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dh0": dh0, "seg_dstate": seg_dstate, "seg_grad": seg_grad}
+
+
+# ------------------------------------------------------------------------ several streams at once
+
+_streams = {}
+
+
+def _side_streams(device, n):
+    """n streams of default priority on ``device``, created once and reused."""
+    key = (device.index, n)
+    if key not in _streams:
+        _streams[key] = [torch.cuda.Stream(device=device) for _ in range(n)]
+    return _streams[key]
+
+
+def _rows(t, lo, hi):
+    """Sequences lo..hi-1 of a [B, H, ...] tensor, as a contiguous [hi-lo, 1, ...] view."""
+    if t is None:
+        return None
+    flat = t.view(t.shape[0] * t.shape[1], 1, *t.shape[2:])
+    return flat[lo:hi]
+
+
+def zeco_step_streams(q, k, v, g, do, chunk: int, P: int, K: int, n_streams: int = 2, h0=None, dhT=None,
+                      out=None, stagger: bool = False):
+    """The whole fwd+bwd path with the B*H sequences cut into ``n_streams`` groups, each group's six
+    calls (local pass, scan, correction; local backward, reverse scan, correction) in order on a
+    stream of its own.  The streams fork from torch's current stream and join back into it, so
+    the result is ordered like any other call on the current stream.  While one group runs its
+    scans and corrections, another group's local passes can use the CUs they leave free (every unit
+    is computed exactly as in the one-stream chain, so the results are identical bit for bit).
+
+    ``out``: optional dict of preallocated buffers (as returned by a previous call) to reuse.
+    ``stagger``: each group's chain waits for the previous group's local pass, so that a group's
+    scan and correction run while the next group's local pass does (the overlap the ZeCO pages
+    measure; on one GPU it serialises the local passes of the groups, which costs more than the
+    scans it hides).
+    Returns a dict: o, h_final, dq, dk, dv, dg, dh0 and the intermediates."""
+    B, H, T, dk_, dv_ = _head_args(q, k, v, g, (("do", do, v.shape[-1], q.dtype),))
+    cs_shape, st_shape, ld_shape = _seg_shapes(B, H, T, dk_, dv_, chunk, P)
+    dev, f32, edt = q.device, torch.float32, q.dtype
+    if out is None:
+        out = {
+            "o": torch.empty_like(v), "chunk_states": torch.empty(cs_shape, device=dev, dtype=edt),
+            "seg_state": torch.empty(st_shape, device=dev, dtype=f32),
+            "seg_logdecay": torch.empty(ld_shape, device=dev, dtype=f32),
+            "seg_in": torch.empty(st_shape, device=dev, dtype=f32),
+            "h_final": torch.empty((B, H, dk_, dv_), device=dev, dtype=f32),
+            "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+            "dg": torch.empty_like(g), "seg_dstate": torch.empty(st_shape, device=dev, dtype=f32),
+            "seg_grad": torch.empty(st_shape, device=dev, dtype=f32),
+            "dh0": torch.empty((B, H, dk_, dv_), device=dev, dtype=f32),
+        }
+    BH = B * H
+    n = max(1, min(n_streams, BH))
+    bounds = [BH * i // n for i in range(n + 1)]
+    if "workspaces" not in out or len(out["workspaces"]) != n:
+        out["workspaces"] = []
+        for i in range(n):
+            sz = max(workspace_size(GLA_FWD, bounds[i + 1] - bounds[i], 1, T, dk_, dv_, chunk, P, edt),
+                     workspace_size(GLA_BWD, bounds[i + 1] - bounds[i], 1, T, dk_, dv_, chunk, P, edt))
+            out["workspaces"].append(torch.empty(sz, device=dev, dtype=torch.uint8))
+    main = torch.cuda.current_stream(dev)
+    streams = _side_streams(dev, n)
+    local_done = None
+    for i, st in enumerate(streams):
+        lo, hi = bounds[i], bounds[i + 1]
+        r = {name: _rows(t, lo, hi) for name, t in out.items() if isinstance(t, torch.Tensor)}
+        x = {name: _rows(t, lo, hi) for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("do", do),
+                                                     ("h0", h0), ("dhT", dhT))}
+        ws = out["workspaces"][i]
+        st.wait_stream(main)
+        if stagger and local_done is not None:
+            st.wait_event(local_done)
+        with torch.cuda.stream(st):
+            gla_chunk_fwd(x["q"], x["k"], x["v"], x["g"], chunk, P, o=r["o"], chunk_states=r["chunk_states"],
+                          seg_state=r["seg_state"], seg_logdecay=r["seg_logdecay"], workspace=ws)
+            if stagger:
+                local_done = torch.cuda.Event()
+                local_done.record(st)
+            gla_segment_scan(r["seg_state"], r["seg_logdecay"], K, h_boundary=x["h0"], seg_carry=r["seg_in"],
+                             h_out=r["h_final"])
+            gla_segment_correct(GLA_FWD, chunk, P, q=x["q"], g=x["g"], seg_in=r["seg_in"], o=r["o"],
+                                chunk_states=r["chunk_states"])
+            gla_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["do"], r["chunk_states"], r["seg_in"], chunk, P,
+                          dq=r["dq"], dk=r["dk"], dv=r["dv"], dg=r["dg"], seg_dstate=r["seg_dstate"], workspace=ws)
+            gla_segment_scan(r["seg_dstate"], r["seg_logdecay"], K, h_boundary=x["dhT"], reverse=True,
+                             seg_carry=r["seg_grad"], h_out=r["dh0"])
+            gla_segment_correct(GLA_BWD, chunk, P, k=x["k"], v=x["v"], g=x["g"], seg_in=r["seg_in"],
+                                seg_grad=r["seg_grad"], chunk_states=r["chunk_states"], dk=r["dk"], dv=r["dv"],
+                                dg=r["dg"])
+    for st in streams:
+        main.wait_stream(st)
+    return out
+

@@ -37,6 +37,19 @@ def maxrel(x, r):
     return float(num / den)
 
 
+def elemrel(x, r):
+    """Element-wise relative error with a floor: max_i |x_i - r_i| / (|r_i| + 1e-3 max|r|).  Unlike
+    maxrel it does not let a local error hide where the tensor is small (reported, not gated)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if not r.size:
+        return 0.0
+    floor = 1e-3 * np.max(np.abs(r))
+    if floor == 0.0:
+        return float(np.max(np.abs(x - r)))
+    return float(np.max(np.abs(x - r) / (np.abs(r) + floor)))
+
+
 def dev(d):
     return {k: v.to("cuda") for k, v in d.items()}
 
@@ -75,7 +88,7 @@ def oracle_pipeline(d, chunk, P, bwd, h0=None, dhT=None):
 
 def check(gpu, ref, keys, tol, label):
     errs = {n: maxrel(gpu[n], ref[n]) for n in keys}
-    say(label, " ".join("%s=%.2e" % (n, e) for n, e in errs.items()))
+    say(label, " ".join("%s=%.2e(el %.1e)" % (n, e, elemrel(gpu[n], ref[n])) for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, "%s: max relative error above %.0e: %s" % (label, tol, bad)
 
@@ -266,6 +279,31 @@ def test_allgather_pipeline_matches_chain_pipeline():
         assert maxrel(as_f64(ba[n]), as_f64(bc[n])) <= TOL["bf16"], n
 
 
+@pytest.mark.parametrize("n_streams", [2, 3])
+def test_multi_stream_schedule(n_streams):
+    # the sequences split over several streams, each group's six calls on its own stream: bit for
+    # bit the one-stream chain, and the oracle's results (boundary states given, one group of
+    # sequences taking the exact kernels through a strongly decaying stretch)
+    B, H, T, dk, dv, chunk, P, K = 2, 3, 2048, 64, 128, 64, 4, 2
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 19, True, "logsigmoid16")
+    d["g"][1, 2, 700:760] = -3.0
+    rng = np.random.default_rng(3)
+    h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    x = dev(d)
+    got = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], chunk, P, K, n_streams,
+                                h0=h0.cuda(), dhT=dhT.cuda())
+    one = gpu_pipeline(x, chunk, P, K, True, h0.cuda(), dhT.cuda())
+    torch.cuda.synchronize()
+    names = {"o": "o", "h_final": "h_final", "dq": "dq", "dk": "dk", "dv": "dv", "dg": "dg", "dh0": "dh0",
+             "seg_in": "S_in", "seg_grad": "G"}
+    for a_, b_ in names.items():
+        assert np.array_equal(as_f64(got[a_]), one[b_]), a_
+    ref = oracle_pipeline(d, chunk, P, True, h0.numpy(), dhT.numpy())
+    check({k_: one[k_] for k_ in ("o", "h_final", "dq", "dk", "dv", "dg", "dh0")}, ref,
+          ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL["bf16"], "%d streams" % n_streams)
+
+
 def test_state_carry_across_calls():
     # running the second half with h0 = the first half's final state equals one call
     d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 8, False, "weak")
@@ -301,8 +339,9 @@ def test_gradient_carry_across_calls():
 
 def test_headline_workload_at_full_size():
     """64 segments of 16384 tokens, 4 heads, fwd+bwd, in the launch configuration the benchmark
-    times.  The oracle runs head 0 in full (forward over all 1M tokens; exact backward over the last
-    two segments, started from the oracle's own state at that point), and the homogeneity identity
+    times.  The oracle runs head 0 in full, forward and backward over all 1M tokens, and every
+    output and gradient of that head is compared element by element on every segment; G[61] is
+    checked against the oracle's backward over the last two segments.  The homogeneity identity
     sum<dq,q> = sum<dk,k> = sum<dv,v> = sum<do,o> is checked on every head."""
     w = inputs.WORKLOADS[inputs.HEADLINE]
     t = time.time()
@@ -322,30 +361,44 @@ def test_headline_workload_at_full_size():
         rel = float(((dot(x[xn], b[dn]) - ref).abs() / ref.abs()).max())
         say("homogeneity %s: %.2e" % (xn, rel))
         assert rel <= TOL["bf16"], xn
-    # oracle on head 0
+    # oracle on head 0, every token
     h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, 0, w.dtype, 0, True)
     a = {n: as_f64(t) for n, t in h.items()}
+    del h
     L = w.L
     t62 = (w.P - 2) * L
     t = time.time()
-    o_head, S62 = oracle.gla_fwd(a["q"][:, :, :t62], a["k"][:, :, :t62], a["v"][:, :, :t62], a["g"][:, :, :t62])
-    o_tail, hT = oracle.gla_fwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:], S62)
+    o_ref, hT, hs = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"], states_every=L)
+    S62 = hs[:, :, w.P - 3]  # the state after 62 segments
+    del hs
     say("oracle forward over %d tokens: %.1fs" % (w.T, time.time() - t))
-    o_ref = np.concatenate([o_head, o_tail], axis=2)
-    del o_head, o_tail
-    errs = {
-        "o": maxrel(as_f64(f["o"][:1, :1]), o_ref),
-        "h_final": maxrel(as_f64(f["h_final"][:1, :1]), hT),
-        "S_in[62]": maxrel(as_f64(f["seg_in"][:1, :1, w.P - 2]), S62),
-    }
+    errs, el = {}, {}
+
+    def cmp(name, got, r):
+        errs[name] = maxrel(got, r)
+        el[name] = elemrel(got, r)
+
+    cmp("o", as_f64(f["o"][:1, :1]), o_ref)
     del o_ref
+    cmp("h_final", as_f64(f["h_final"][:1, :1]), hT)
+    cmp("S_in[62]", as_f64(f["seg_in"][:1, :1, w.P - 2]), S62)
     t = time.time()
-    gb = oracle.gla_bwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:],
-                        a["do"][:, :, t62:], S62)
-    say("oracle backward over the last two segments: %.1fs" % (time.time() - t))
+    gb = oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"])
+    say("oracle backward over %d tokens: %.1fs" % (w.T, time.time() - t))
     for n in ("dq", "dk", "dv", "dg"):
-        errs[n] = maxrel(as_f64(b[n][:1, :1, t62:]), gb[n])
-    errs["G[61]"] = maxrel(as_f64(b["seg_grad"][:1, :1, w.P - 3]), gb["dh0"])
-    say("headline workload, head 0: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+        got = as_f64(b[n][:1, :1])
+        cmp(n, got, gb[n])
+        # and segment by segment, so that no segment's error hides behind a larger one elsewhere
+        seg = max(maxrel(got[:, :, p * L:(p + 1) * L], gb[n][:, :, p * L:(p + 1) * L]) for p in range(w.P))
+        errs[n + "[worst segment]"] = seg
+        del got
+    cmp("dh0", as_f64(b["dh0"][:1, :1]), gb["dh0"])
+    del gb
+    gb2 = oracle.gla_bwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:],
+                         a["do"][:, :, t62:], S62)
+    cmp("G[61]", as_f64(b["seg_grad"][:1, :1, w.P - 3]), gb2["dh0"])
+    say("headline workload, head 0, every token: " +
+        " ".join("%s=%.2e" % kv for kv in errs.items()) + " | element-wise: " +
+        " ".join("%s=%.1e" % kv for kv in el.items()))
     bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
     assert not bad, bad
