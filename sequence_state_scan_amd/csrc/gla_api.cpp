@@ -53,6 +53,7 @@ bool shape_listed(int dtype, int dk, int dv, int chunk) {
 struct Kernels {
   gla::launch_fn fwd, corr_fwd, bwd, corr_bwd;  // fwd and bwd: the fast local kernels (null for bf16 chunk 16)
   gla::launch_fn fwd_exact, bwd_exact;          // the exact sub-block kernels
+  gla::launch_fn fwd_state, bwd_state;          // the state passes over sub-segments (with the fast kernels)
 };
 
 bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
@@ -63,14 +64,56 @@ bool find_kernels(int dtype, int dk, int dv, int chunk, Kernels* k) {
   k->corr_bwd = gla::lookup_correct_bwd(dtype, chunk, dk, dv);
   k->fwd_exact = gla::lookup_fwd_exact(dtype, dk, dv);
   k->bwd_exact = gla::lookup_bwd_exact(dtype, dk, dv);
-  return (k->fwd != nullptr) == (k->bwd != nullptr) && k->corr_fwd && k->corr_bwd && k->fwd_exact && k->bwd_exact;
+  k->fwd_state = gla::lookup_fwd_state(dtype, chunk, dk, dv);
+  k->bwd_state = gla::lookup_bwd_state(dtype, chunk, dk, dv);
+  return (k->fwd != nullptr) == (k->bwd != nullptr) && (k->fwd != nullptr) == (k->fwd_state != nullptr) &&
+         (k->fwd != nullptr) == (k->bwd_state != nullptr) && k->corr_fwd && k->corr_bwd && k->fwd_exact &&
+         k->bwd_exact;
 }
 
-// Workspace of gla_chunk_fwd / gla_chunk_bwd: one int flag per unit (b, h, segment), rounded up
-// to 256 bytes.
-size_t workspace_bytes(int B, int H, int P) {
-  const size_t units = (size_t)B * H * P;
-  return (units * sizeof(int) + 255) / 256 * 256;
+// Sub-segments per segment.  One workgroup runs a (b, h, segment) unit, and at most one fits on a
+// CU, so with fewer than 256 units most of the chip would idle: each segment is then cut into S
+// sub-segments (a power of two, each of at least 2 chunks) until B*H*P*S reaches 256.  A state
+// pass gives every sub-segment's end state (backward: its state gradient), the segment scan
+// combines them inside each segment, and the local pass starts every sub-segment from its true
+// incoming state (gradient), so its outputs are the ones the unsplit segment would give.  Only
+// the fast kernels split (bf16 chunk 16 runs unsplit).
+constexpr long long kFillUnits = 256;
+int split_factor(int B, int H, int T, int P, int chunk, const Kernels& k) {
+  if (!k.fwd) return 1;
+  const long long units = (long long)B * H * P;
+  const int nch = T / P / chunk;
+  int S = 1;
+  while (units * S < kFillUnits && nch % (2 * S) == 0 && nch / (2 * S) >= 2) S *= 2;
+  return S;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of gla_chunk_fwd / gla_chunk_bwd, in this order: one int flag per unit (b, h, segment,
+// sub-segment); with S > 1 the sub-segments' states from the state pass, their summed log-gates,
+// and the scan's incoming states (forward) or gradients (backward), all float32.
+struct Workspace {
+  size_t flags, sub_state, sub_ld, carry, total;
+};
+Workspace workspace_layout(int B, int H, int P, int dk, int dv, int S) {
+  const size_t u = (size_t)B * H * P * S;
+  Workspace w{};
+  w.flags = 0;
+  size_t off = align256(u * sizeof(int));
+  if (S > 1) {
+    w.sub_state = off;
+    off += align256(u * dk * dv * sizeof(float));
+    w.sub_ld = off;
+    off += align256(u * dk * sizeof(float));
+    w.carry = off;
+    off += align256(u * dk * dv * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+size_t workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int P, const Kernels& k) {
+  return workspace_layout(B, H, P, dk, dv, split_factor(B, H, T, P, chunk, k)).total;
 }
 
 // Shape checks shared by the chunked entry points.
@@ -135,13 +178,23 @@ size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int ch
   Kernels kern;
   if (check_shape("gla_workspace_size", B, H, T, dk, dv, chunk, P, dtype, &kern) != GLA_OK) return 0;
   ok();
-  return workspace_bytes(B, H, P);
+  return workspace_bytes(B, H, T, dk, dv, chunk, P, kern);
 }
 
 gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* g, void* o,
                          void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
                          int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
                          void* stream) {
+  return gla::chunk_fwd_capped(q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P,
+                               dtype, workspace, workspace_size, 0, stream);
+}
+
+}  // extern "C"
+
+gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, void* o,
+                                 void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
+                                 int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
+                                 int max_split, void* stream) {
   const char* fn = "gla_chunk_fwd";
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
@@ -153,12 +206,30 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
   for (const void* p : ins)
     if (p == o || p == chunk_states || p == workspace)
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
-  if (!workspace || workspace_size < workspace_bytes(B, H, P))
+  int S = split_factor(B, H, T, P, chunk, kern);
+  if (max_split > 0 && S > max_split) S = max_split;
+  const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
+  if (!workspace || workspace_size < lay.total)
     return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
-                workspace_bytes(B, H, P), workspace ? workspace_size : (size_t)0);
-  gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, static_cast<int*>(workspace),
-                 B * H, T, dk, dv, P, chunk};
+                lay.total, workspace ? workspace_size : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, reinterpret_cast<int*>(ws + lay.flags),
+                 B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S > 1) {
+    // state pass over the sub-segments, then the scan over them inside each segment: the state
+    // entering each sub-segment (zero at the segment's start) and, as its end value, the segment's
+    // local end state
+    a.sub_state = reinterpret_cast<float*>(ws + lay.sub_state);
+    a.sub_ld = reinterpret_cast<float*>(ws + lay.sub_ld);
+    float* carry = reinterpret_cast<float*>(ws + lay.carry);
+    st = launched(fn, kern.fwd_state(&a, s));
+    if (st != GLA_OK) return st;
+    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, nullptr, carry, seg_state, B * H * P, S, dk,
+                                               dv, 1, 0, s));
+    if (st != GLA_OK) return st;
+    a.init = carry;
+  }
   if (kern.fwd) {  // the fast kernel, then the exact one for the units it flagged
     st = launched(fn, kern.fwd(&a, s));
     if (st != GLA_OK) return st;
@@ -167,6 +238,8 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
   }
   return launched(fn, kern.fwd_exact(&a, s));
 }
+
+extern "C" {
 
 gla_status gla_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                             float* seg_carry, float* h_out, int B, int H, int P, int dk, int dv, int K,
@@ -238,12 +311,29 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
   for (const void* p : ins)
     if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace)
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
-  if (!workspace || workspace_size < workspace_bytes(B, H, P))
+  const int S = split_factor(B, H, T, P, chunk, kern);
+  const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
+  if (!workspace || workspace_size < lay.total)
     return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
-                workspace_bytes(B, H, P), workspace ? workspace_size : (size_t)0);
-  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate, static_cast<int*>(workspace),
-                 B * H, T, dk, dv, P, chunk};
+                lay.total, workspace ? workspace_size : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate,
+                 reinterpret_cast<int*>(ws + lay.flags), B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S > 1) {
+    // state-gradient pass over the sub-segments, then the reverse scan over them inside each
+    // segment: the gradient w.r.t. the state leaving each sub-segment from the rest of its segment
+    // and, as its end value, the segment's gradient w.r.t. its incoming state
+    a.sub_state = reinterpret_cast<float*>(ws + lay.sub_state);
+    a.sub_ld = reinterpret_cast<float*>(ws + lay.sub_ld);
+    float* carry = reinterpret_cast<float*>(ws + lay.carry);
+    st = launched(fn, kern.bwd_state(&a, s));
+    if (st != GLA_OK) return st;
+    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, nullptr, carry, seg_dstate, B * H * P, S, dk,
+                                               dv, 1, 1, s));
+    if (st != GLA_OK) return st;
+    a.init = carry;
+  }
   if (kern.bwd) {  // the fast kernel, then the exact one for the units it flagged
     st = launched(fn, kern.bwd(&a, s));
     if (st != GLA_OK) return st;

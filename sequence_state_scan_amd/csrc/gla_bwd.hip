@@ -79,11 +79,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   E* __restrict__ dk = static_cast<E*>(a.dk);
   E* __restrict__ dv = static_cast<E*>(a.dv);
   float* __restrict__ dg = a.dg;
-  const int L = a.T / a.P;
-  const int nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments per segment, this one, its segment
+  const int L = a.T / a.P, Ls = L / NS;
+  const int nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const long chunk0 = tok0 / C;  // global chunk index of the sub-segment's first chunk
   constexpr long SS = (long)DK * DV;  // one state
   const int w = wave_id();
   const int cb = w;                   // this wave's 16-row block of U^T (waves w >= NCB hold none)
@@ -109,10 +110,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   };
 
   f32x4 U[NJB];  // U[jb][i] = U[16cb + n16][16jb + 4g4 + i]
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
   // carry into the current chunk: rowsum(S_n * U_n) for c = 16cb + 4g4 + i (nothing after the last chunk)
   float cin[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.init && sub < NS - 1 && urole) {
+    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment), and its
+    // carry rowsum(S * U) with S the global state after the sub-segment's last chunk
+    const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+    float part = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      U[jb] = load4(a.init + (long)unit * SS + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4);
+      part += piece_dot(load_state_piece<E, NJB>(cst + (chunk0 + nchunks - 1) * SS, cb, jb, state_lane_row(n16, g4)),
+                        U[jb]);
+    }
+    part = sum_over_g4(part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
+  } else {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
+  }
 
   prefetch(nchunks - 1, threadIdx.x);
   for (int n = nchunks - 1; n >= 0; --n) {
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     piece Sp[NJB];
     if (urole) {
       const long roff = (long)(cb * 16 + n16) * DV + 4 * g4;
-      if (n > 0) {
+      if (n > 0 || sub > 0) {  // the stored global state after the previous chunk
         const E* st = cst + (chunk0 + n - 1) * SS;
         if constexpr (NJB % 2 == 0) {
 #pragma unroll
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-          const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
+          const f32x4 x = load4(a.seg_in + (long)seg * SS + roff + jb * 16);  // the segment's incoming state
 #pragma unroll
           for (int i = 0; i < 4; ++i) Sp[jb][i] = (E)x[i];
         }
@@ -394,8 +411,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       __syncthreads();
     }
   }
-  // D = gradient w.r.t. the state entering the segment (from this segment's outputs)
-  if (urole) {
+  // D = gradient w.r.t. the state entering the segment (from this segment's outputs); with
+  // sub-segments the reverse scan over them gives it
+  if (urole && NS == 1) {
     float* dst = a.seg_dstate + (long)unit * SS;
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
@@ -404,15 +422,131 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   if (threadIdx.x == 0) a.flags[unit] = 0;
 }
 
+// State-gradient pass over sub-segments: from a zero gradient at the sub-segment's end, walking
+// its chunks back, U_{n-1} = diag(exp(lam)) U_n + Qbar^T dO (Qbar = q exp(b)); the result is the
+// gradient w.r.t. the state entering the sub-segment from its own outputs.  Every factor is
+// exp(<= 0).  Wave w holds rows 16w .. of U, in bwd_kernel's lane layout.
+template <typename E, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_units) {
+  constexpr int NT = NW * 64;
+  typedef GateTile8<E, C, DK, NW * 64> GT;
+  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
+  constexpr int LDV = lds_ld<E>(DV), LDQ = lds_ld<E>(DK);
+  constexpr int NJB = DV / 16, NCB = DK / 16;
+  constexpr int KS = Mma<E>::KSTEP;
+  static_assert(NCB <= NW, "one 16-row block of U per wave");
+
+  __shared__ __attribute__((aligned(16))) E sdO[C * LDV];  // dO   [t][j]
+  __shared__ __attribute__((aligned(16))) E sQ[C * LDQ];   // Qbar [t][c]
+  __shared__ __attribute__((aligned(16))) float sLamE[DK];
+  __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
+
+  const int unit = blockIdx.x;
+  if (unit >= n_units) return;
+  const E* __restrict__ q = static_cast<const E*>(a.q);
+  const E* __restrict__ dO = static_cast<const E*>(a.dO);
+  const int NS = a.S, sub = unit % NS, seg = unit / NS;
+  const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const int w = wave_id(), cb = w;
+  const bool urole = cb < NCB;
+
+  GT pgt;
+  auto prefetch = [&](int n, int tid) { pgt.load(a.g, q, nullptr, (tok0 + (long)n * C) * DK, tid); };
+  f32x4 U[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
+  float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // the sub-segment's summed log-gates
+
+  prefetch(nchunks - 1, threadIdx.x);
+  for (int n = nchunks - 1; n >= 0; --n) {
+    const int tid = fresh_tid(), l = tid & 63, n16 = l & 15;
+    Vec8<E> pd[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pd[i].load(dO + (tok0 + (long)n * C + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+    }
+    {
+      float b[GT::RI][8], lam[8];
+      pgt.prefix(tid, sTot, b, lam);
+      if (GT::active(tid)) {
+        const int x = GT::group_of(tid);
+#pragma unroll
+        for (int r = 0; r < GT::RI; ++r) {
+          float xq[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[e] = pgt.q[r].at(e) * __expf(b[r][e]);
+          store8(sQ + GT::row(tid, r) * LDQ + 8 * x, xq);
+        }
+        if (GT::set_of(tid) == 0 && n16 == 0) {
+          float el[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            el[e] = __expf(lam[e]);
+            ldsum[e] += lam[e];
+          }
+          store8(sLamE + 8 * x, el);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int pc = tid + NT * i;
+        if (NVP % NT == 0 || pc < NVP) pd[i].store(sdO + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (n > 0) prefetch(n - 1, tid);
+    __syncthreads();
+    if (urole) {
+      // U^T[j][c] = exp(lam_c) U^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]
+      const float le = sLamE[cb * 16 + n16];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) U[jb] *= le;
+#pragma unroll
+      for (int ks = 0; ks < C / KS; ++ks) {
+        const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) U[jb] = Mma<E>::mma(frag_ld<E, true>(sdO + jb * 16, LDV, ks * KS), fq, U[jb]);
+      }
+    }
+    __syncthreads();
+  }
+  if (urole) {
+    float* dst = a.sub_state + (long)unit * DK * DV;
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[jb]);
+  }
+  const int tid = threadIdx.x;
+  if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
+    store8(a.sub_ld + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
+}
+
 template <typename E, int C, int DK, int DV>
 struct BwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
-    const int n_units = a.BH * a.P;
+    const int n_units = a.BH * a.P * a.S;
     hipLaunchKernelGGL((bwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
+
+template <typename E, int C, int DK, int DV>
+struct BwdStateLauncher {
+  static hipError_t run(const void* pa, hipStream_t s) {
+    const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
+    const int n_units = a.BH * a.P * a.S;
+    hipLaunchKernelGGL((bwd_state_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    return hipGetLastError();
+  }
+};
+
+launch_fn lookup_bwd_state(int dtype, int chunk, int dk, int dv) {
+  return lookup_cdd<BwdStateLauncher>(dtype, chunk, dk, dv);
+}
 
 launch_fn lookup_bwd(int dtype, int chunk, int dk, int dv) { return lookup_cdd<BwdLauncher>(dtype, chunk, dk, dv); }
 

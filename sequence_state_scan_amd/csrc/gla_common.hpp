@@ -489,8 +489,8 @@ struct GateTile8 {
   // chunk row (token) of block r of the thread's item
   static __device__ __forceinline__ int row(int tid, int r) { return 16 * (set_of(tid) * RI + r) + (tid & 15); }
 
-  // chunk_elem: element offset of the chunk's first token (token index * DK); kp may be null
-  // (then k is not loaded)
+  // chunk_elem: element offset of the chunk's first token (token index * DK); qp or kp may be
+  // null (then q or k is not loaded)
   __device__ __forceinline__ void load(const float* gp, const E* qp, const E* kp, long chunk_elem, int tid) {
     if (!active(tid)) return;
     const long off = chunk_elem + (long)row(tid, 0) * DK + 8 * group_of(tid);
@@ -498,7 +498,7 @@ struct GateTile8 {
     for (int r = 0; r < RI; ++r) {
       g[r][0] = load4(gp + off + r * 16 * DK);
       g[r][1] = load4(gp + off + r * 16 * DK + 4);
-      q[r].load(qp + off + r * 16 * DK);
+      if (qp) q[r].load(qp + off + r * 16 * DK);
       if (kp) k[r].load(kp + off + r * 16 * DK);
     }
   }

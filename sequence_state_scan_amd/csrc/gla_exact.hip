@@ -141,10 +141,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
   const int C = a.chunk, NSB = C / kSB;
-  const int L = a.T / a.P, nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments, as in fwd_local_kernel
+  const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const long chunk0 = tok0 / C;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
   const int R = tid >> 4, t = n16;
   const bool gact = R < NGR, vrole = w * JPW < NJB;
@@ -153,7 +154,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) S[jj][kb] = zero4();
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (a.init && sub > 0 && vrole)  // the state entering the sub-segment
+        S[jj][kb] = quad_transpose(load4(a.init + (long)unit * DK * DV + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV +
+                                         (w * JPW + jj) * 16 + (n16 & ~3)));
+      else
+        S[jj][kb] = zero4();
+    }
   f32x4 ldsum = zero4();  // log cumulative decay of the segment, channels 4R ..
 
   for (int n = 0; n < nchunks; ++n) {
@@ -254,16 +261,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
     }
   }
   // ---- segment results: local end state (float32) and log cumulative decay ----
-  if (vrole) {
-    float* st = a.seg_state + (long)unit * DK * DV;
+  if (NS == 1) {
+    if (vrole) {
+      float* st = a.seg_state + (long)unit * DK * DV;
 #pragma unroll
-    for (int jj = 0; jj < JPW; ++jj)
+      for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + (w * JPW + jj) * 16 + (n16 & ~3),
-               quad_transpose(S[jj][kb]));
+        for (int kb = 0; kb < NKB; ++kb)
+          store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + (w * JPW + jj) * 16 + (n16 & ~3),
+                 quad_transpose(S[jj][kb]));
+    }
+    if (gact && t == 0) store4(a.seg_logdecay + (long)unit * DK + 4 * R, ldsum);
+  } else if (sub == NS - 1) {
+    // the end state comes from the scan over the sub-segments; the log decay is their sum
+    for (int c = tid; c < DK; c += NW * 64) {
+      float sum = 0.f;
+      for (int s2 = 0; s2 < NS; ++s2) sum += a.sub_ld[((long)seg * NS + s2) * DK + c];
+      a.seg_logdecay[(long)seg * DK + c] = sum;
+    }
   }
-  if (gact && t == 0) store4(a.seg_logdecay + (long)unit * DK + 4 * R, ldsum);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -305,18 +321,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   E* __restrict__ dk = static_cast<E*>(a.dk);
   E* __restrict__ dv = static_cast<E*>(a.dv);
   const int C = a.chunk, NSB = C / kSB;
-  const int L = a.T / a.P, nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments, as in bwd_kernel
+  const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const long chunk0 = tok0 / C;
   constexpr long SS = (long)DK * DV;
   const int w = wave_id();
   const bool urole = w < NCB;  // holds U rows 16w .. and the gate rows 4w .. 4w + 3
 
   f32x4 U[NJB];  // U[jb][i] = U[16w + n16][16jb + 4g4 + i]
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
   f32x4 cin = zero4();  // rowsum(S_after * U_after) for c = 16w + 4g4 + i
+  if (a.init && sub < NS - 1 && urole) {
+    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment), and the
+    // carry rowsum(S * U) with S the global state after the sub-segment's last chunk
+    const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) U[jb] = load4(a.init + (long)unit * SS + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
+    f32x4 Se[NJB];
+    load_state_rows<E, NJB>(cst + (chunk0 + nchunks - 1) * SS, w, Se);
+    float part = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) part += piece_dot(Se[jb], U[jb]);
+    part = sum_over_g4(part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
+  } else {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
+  }
 
   for (int n = nchunks - 1; n >= 0; --n) {
     const long tc0 = tok0 + (long)n * C;
@@ -402,12 +435,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       if (urole) {
         // the stored state before the chunk, advanced through the chunk's earlier sub-blocks
         f32x4 Sf[NJB];
-        if (n > 0) {
+        if (n > 0 || sub > 0) {
           load_state_rows<E, NJB>(cst + (chunk0 + n - 1) * SS, w, Sf);
         } else {
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb)
-            Sf[jb] = load4(a.seg_in + (long)unit * SS + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
+            Sf[jb] = load4(a.seg_in + (long)seg * SS + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
         }
         for (int i = 0; i < j; ++i) {
           const float le = sLamE[i][16 * w + n16];
@@ -478,8 +511,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       __syncthreads();
     }
   }
-  // D = gradient w.r.t. the state entering the segment (from this segment's outputs)
-  if (urole) {
+  // D = gradient w.r.t. the state entering the segment (from this segment's outputs); with
+  // sub-segments the reverse scan over them gives it
+  if (urole && NS == 1) {
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
     float* dst = a.seg_dstate + (long)unit * SS;
 #pragma unroll
@@ -491,7 +525,7 @@ template <typename E, int DK, int DV>
 struct FwdExactLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
-    const int n_units = a.BH * a.P;
+    const int n_units = a.BH * a.P * a.S;
     hipLaunchKernelGGL((fwd_exact_kernel<E, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
@@ -501,7 +535,7 @@ template <typename E, int DK, int DV>
 struct BwdExactLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
-    const int n_units = a.BH * a.P;
+    const int n_units = a.BH * a.P * a.S;
     hipLaunchKernelGGL((bwd_exact_kernel<E, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sLamE[DK];  // exp(lam) per channel
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];  // per-set gate totals
 
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x;  // (b, h, segment, sub-segment)
   if (unit >= n_units) return;
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
@@ -61,11 +61,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   const float* __restrict__ g = a.g;
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
-  const int L = a.T / a.P;
-  const int nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
-  const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments per segment, this one, its segment
+  const int L = a.T / a.P, Ls = L / NS;
+  const int nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const long chunk0 = tok0 / C;  // global chunk index of the sub-segment's first chunk
   const int w = wave_id();
   typedef typename Mma<E>::frag frag;
 
@@ -84,10 +85,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   };
 
   f32x4 S[JPW][NKB];  // S[jj][kb][i] = S[16kb + 4g4 + i][16jb + n16]
+  if (a.init && sub > 0 && w * JPW < NJB) {
+    // the state entering the sub-segment (from its segment's start), row-major float32: each lane
+    // reads 4 consecutive columns of a row and the quad transpose turns them into its rows
+    const float* ci = a.init + (long)unit * DK * DV;
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
-  for (int jj = 0; jj < JPW; ++jj)
+    for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) S[jj][kb] = zero4();
+      for (int kb = 0; kb < NKB; ++kb)
+        S[jj][kb] = quad_transpose(load4(ci + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + (w * JPW + jj) * 16 + (n16 & ~3)));
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) S[jj][kb] = zero4();
+  }
   float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // log cumulative decay of the segment (set 0, n16 == 0)
 
   prefetch(0, threadIdx.x);
@@ -235,20 +248,147 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   }
 
   // ---- segment results: local end state (float32) and log cumulative decay ----
-  float* st = a.seg_state + (long)unit * DK * DV;
-  const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
+  const int tid = threadIdx.x;
+  if (NS == 1) {
+    float* st = a.seg_state + (long)unit * DK * DV;
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
-  for (int jj = 0; jj < JPW; ++jj) {
-    const int jb = w * JPW + jj;
-    if (w * JPW < NJB)
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jb = w * JPW + jj;
+      if (w * JPW < NJB)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
+    }
+    if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
+      store8(a.seg_logdecay + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
+  } else if (sub == NS - 1) {
+    // the segment's end state comes from the scan over its sub-segments; its log decay is the sum
+    // of the sub-segments' (from the state pass)
+    for (int c = tid; c < DK; c += NT) {
+      float sum = 0.f;
+      for (int s2 = 0; s2 < NS; ++s2) sum += a.sub_ld[((long)seg * NS + s2) * DK + c];
+      a.seg_logdecay[(long)seg * DK + c] = sum;
+    }
+  }
+  if (tid == 0) a.flags[unit] = 0;
+}
+
+// State pass over sub-segments: the state at the end of every sub-segment from a zero start,
+// S = diag(exp(lam)) S + Ktil^T V per chunk (no outputs), and the sub-segment's summed log-gates.
+// Every factor is exp(<= 0), so no chunk needs the exact kernels here.  Layout and per-chunk
+// staging as in fwd_local_kernel; only k, g and v are read.
+template <typename E, int C, int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_units) {
+  constexpr int NT = NW * 64;
+  typedef GateTile8<E, C, DK, NW * 64> GT;
+  constexpr int NVP = C * DV / 8, VPT = ceil_div(NVP, NT);
+  constexpr int LDKT = lds_ld<E>(DK), LDV = lds_ld<E>(DV);
+  constexpr int NJB = DV / 16, NKB = DK / 16;
+  constexpr int JPW = ceil_div(NJB, NW);
+  constexpr int KS = Mma<E>::KSTEP, NKS = C / KS;
+  static_assert(JPW == 1 || NJB % NW == 0, "a wave owns JPW column blocks, or none");
+
+  __shared__ __attribute__((aligned(16))) E sKt[C * LDKT];  // Ktil [s][c]
+  __shared__ __attribute__((aligned(16))) E sV[C * LDV];    // V    [s][j]
+  __shared__ __attribute__((aligned(16))) float sLamE[DK];
+  __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
+
+  const int unit = blockIdx.x;
+  if (unit >= n_units) return;
+  const E* __restrict__ k = static_cast<const E*>(a.k);
+  const E* __restrict__ v = static_cast<const E*>(a.v);
+  const int S = a.S, sub = unit % S, seg = unit / S;
+  const int L = a.T / a.P, Ls = L / S, nchunks = Ls / C;
+  const int bh = seg / a.P, p = seg - bh * a.P;
+  const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
+  const int w = wave_id();
+  typedef typename Mma<E>::frag frag;
+
+  GT pgt;
+  Vec8<E> pv[VPT];
+  auto prefetch = [&](int n, int tid) {
+    const long t0 = tok0 + (long)n * C;
+    pgt.load(a.g, nullptr, k, t0 * DK, tid);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pv[i].load(v + (t0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+    }
+  };
+
+  f32x4 S_[JPW][NKB];
+#pragma unroll
+  for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) S_[jj][kb] = zero4();
+  float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  prefetch(0, threadIdx.x);
+  for (int n = 0; n < nchunks; ++n) {
+    const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
+    {
+      float b[GT::RI][8], lam[8];
+      pgt.prefix(tid, sTot, b, lam);
+      if (GT::active(tid)) {
+        const int x = GT::group_of(tid);
+#pragma unroll
+        for (int r = 0; r < GT::RI; ++r) {
+          float xkt[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xkt[e] = pgt.k[r].at(e) * __expf(lam[e] - b[r][e]);
+          store8(sKt + GT::row(tid, r) * LDKT + 8 * x, xkt);
+        }
+        if (GT::set_of(tid) == 0 && n16 == 0) {
+          float el[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            el[e] = __expf(lam[e]);
+            ldsum[e] += lam[e];
+          }
+          store8(sLamE + 8 * x, el);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int pc = tid + NT * i;
+        if (NVP % NT == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 1 < nchunks) prefetch(n + 1, tid);
+    __syncthreads();
+    if (w * JPW < NJB) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 lamE = load4(sLamE + kb * 16 + 4 * g4);
+        frag fk[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) fk[ks] = frag_ld<E, true>(sKt + kb * 16, LDKT, ks * KS);
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          S_[jj][kb] *= lamE;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            S_[jj][kb] = Mma<E>::mma(fk[ks], frag_ld<E, true>(sV + (w * JPW + jj) * 16, LDV, ks * KS), S_[jj][kb]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* st = a.sub_state + (long)unit * DK * DV;
+  const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
+  if (w * JPW < NJB) {
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + jb * 16 + (n16 & ~3), quad_transpose(S[jj][kb]));
+        store4(st + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV + (w * JPW + jj) * 16 + (n16 & ~3),
+               quad_transpose(S_[jj][kb]));
   }
   const int tid = threadIdx.x;
   if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
-    store8(a.seg_logdecay + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
-  if (tid == 0) a.flags[unit] = 0;
+    store8(a.sub_ld + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
@@ -422,8 +562,18 @@ template <typename E, int C, int DK, int DV>
 struct FwdLocalLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
-    const int n_units = a.BH * a.P;
+    const int n_units = a.BH * a.P * a.S;
     hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    return hipGetLastError();
+  }
+};
+
+template <typename E, int C, int DK, int DV>
+struct FwdStateLauncher {
+  static hipError_t run(const void* pa, hipStream_t s) {
+    const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
+    const int n_units = a.BH * a.P * a.S;
+    hipLaunchKernelGGL((fwd_state_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };
@@ -440,6 +590,9 @@ struct CorrectFwdLauncher {
 
 launch_fn lookup_fwd_local(int dtype, int chunk, int dk, int dv) {
   return lookup_cdd<FwdLocalLauncher>(dtype, chunk, dk, dv);
+}
+launch_fn lookup_fwd_state(int dtype, int chunk, int dk, int dv) {
+  return lookup_cdd<FwdStateLauncher>(dtype, chunk, dk, dv);
 }
 launch_fn lookup_correct_fwd(int dtype, int chunk, int dk, int dv) {
   return lookup_cdd<CorrectFwdLauncher, Bf16CorrChunks>(dtype, chunk, dk, dv);

@@ -16,8 +16,15 @@ struct FwdArgs {  // gla_chunk_fwd
   void* o;
   void* chunk_states;  // [B][H][T/C][dk][dv], element type = dtype
   float *seg_state, *seg_logdecay;
-  int* flags;  // [BH * P] per-unit flags in the workspace: 1 = recompute with the exact kernel
+  int* flags;  // [BH * P * S] per-unit flags in the workspace: 1 = recompute with the exact kernel
   int BH, T, Dk, Dv, P, chunk;
+  // Each segment is cut into S sub-segments of T/(P S) tokens, one workgroup each (S = 1: none).
+  // init: [BH * P * S][Dk][Dv] state entering each sub-segment, counted from its segment's start
+  // (read for sub-segments s > 0); sub_state / sub_ld: the state pass's outputs, the state at the
+  // end of each sub-segment from a zero start and the sub-segment's summed log-gates.
+  int S;
+  const float* init;
+  float *sub_state, *sub_ld;
 };
 
 struct BwdArgs {  // gla_chunk_bwd
@@ -30,7 +37,20 @@ struct BwdArgs {  // gla_chunk_bwd
   float *dg, *seg_dstate;
   int* flags;  // as in FwdArgs
   int BH, T, Dk, Dv, P, chunk;
+  // Sub-segments as in FwdArgs.  init: [BH * P * S][Dk][Dv] gradient w.r.t. the state leaving each
+  // sub-segment from the later sub-segments of its segment (read for s < S - 1); sub_state, sub_ld:
+  // the state-gradient pass's outputs, each sub-segment's gradient w.r.t. its incoming state from
+  // its own outputs, and its summed log-gates.
+  int S;
+  const float* init;
+  float *sub_state, *sub_ld;
 };
+
+// gla_chunk_fwd with the sub-segment split capped at max_split (0: no cap), the workspace already
+// checked to hold workspace_size bytes for that cap.
+gla_status chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, void* o, void* chunk_states,
+                            float* seg_state, float* seg_logdecay, int B, int H, int T, int dk, int dv, int chunk,
+                            int P, int dtype, void* workspace, size_t workspace_size, int max_split, void* stream);
 
 struct CorrArgs {  // gla_segment_correct
   const void *q, *k, *v;
@@ -75,6 +95,9 @@ launch_fn lookup_correct_bwd(int dtype, int chunk, int dk, int dv);
 // non-null only the units whose flag is 1 are processed, else every unit.
 launch_fn lookup_fwd_exact(int dtype, int dk, int dv);
 launch_fn lookup_bwd_exact(int dtype, int dk, int dv);
+// The state passes over sub-segments (forward: sub_state, sub_ld; backward: sub_state).
+launch_fn lookup_fwd_state(int dtype, int chunk, int dk, int dv);
+launch_fn lookup_bwd_state(int dtype, int chunk, int dk, int dv);
 
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,

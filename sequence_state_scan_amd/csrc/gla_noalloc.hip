@@ -60,6 +60,7 @@ extern "C" gla_status gla_chunk_fwd_noalloc(const void* q, const void* k, const 
   void* ws = nullptr;
   const gla_status st = scratch_ptr(&ws);
   if (st != GLA_OK) return st;
-  return gla_chunk_fwd(q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P, dtype, ws,
-                       sizeof(int) * (size_t)gla::kStaticUnits, stream);
+  // no sub-segments: the scratch holds the per-unit flags only
+  return gla::chunk_fwd_capped(q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P, dtype,
+                               ws, sizeof(int) * (size_t)gla::kStaticUnits, 1, stream);
 }

@@ -68,6 +68,8 @@ def test_chunk_fwd_host_checks(lib):
     assert _fwd(lib, wsb=255) == E             # and must hold gla_workspace_size bytes
     assert b"workspace" in lib.gla_last_error()
     assert _fwd(lib, B=4, H=16, T=256 * 16, P=16, wsb=1023) == E  # 1024 bytes needed for 1024 units
+    need = lib.gla_workspace_size(gla.GLA_FWD, 1, 1, 256, 64, 64, 64, 1, gla.GLA_BF16)
+    assert need > 256 and _fwd(lib, wsb=need - 1) == E  # a small problem cut into sub-segments
     assert _fwd(lib, ws=FAKE) == E             # the workspace aliases q
 
 
@@ -131,14 +133,31 @@ def test_chunk_bwd_host_checks(lib):
     assert ws_call(ctypes.c_void_p(0x1480), 256) == E  # the workspace aliases chunk_states
 
 
+def _expected_workspace(B, H, T, dk, dv, C, P, fast=True):
+    """The workspace rule of include/gla.h, written out: with fewer than 256 units (b, h, segment)
+    each segment is cut into S sub-segments (S a power of two, at least 2 chunks each) until
+    B*H*P*S reaches 256; then one int flag per unit and sub-segment, and with S > 1 three float32
+    buffers (sub-segment states, their log decays, the scanned states), each rounded up to 256."""
+    units, nch, S = B * H * P, T // P // C, 1
+    while fast and units * S < 256 and nch % (2 * S) == 0 and nch // (2 * S) >= 2:
+        S *= 2
+    up = lambda n: (n + 255) // 256 * 256  # noqa
+    u = units * S
+    total = up(4 * u)
+    if S > 1:
+        total += up(4 * u * dk * dv) + up(4 * u * dk) + up(4 * u * dk * dv)
+    return total
+
+
 def test_workspace_size(lib):
-    # one int flag per unit (b, h, segment), rounded up to 256 bytes, for either call
-    for B, H, T, P in [(1, 1, 256, 1), (1, 4, 1 << 20, 64), (3, 5, 64 * 77, 77), (8, 16, 4096, 64)]:
+    for B, H, T, P, C in [(1, 1, 256, 1, 64), (1, 4, 1 << 20, 64, 64), (3, 5, 64 * 77, 77, 16), (8, 16, 4096, 64, 64),
+                          (2, 4, 16384, 1, 64), (1, 4, 32768, 8, 64), (1, 16, 16384, 4, 64), (1, 1, 1024, 4, 32)]:
         for which in (gla.GLA_FWD, gla.GLA_BWD):
-            n = lib.gla_workspace_size(which, B, H, T, 128, 256, 64 if T // P % 64 == 0 else 16, P, gla.GLA_BF16)
-            assert n == (4 * B * H * P + 255) // 256 * 256, (B, H, T, P)
-            assert n == gla.workspace_size(which, B, H, T, 128, 256, 64 if T // P % 64 == 0 else 16, P,
-                                           torch.bfloat16)
+            n = lib.gla_workspace_size(which, B, H, T, 128, 256, C, P, gla.GLA_BF16)
+            assert n == _expected_workspace(B, H, T, 128, 256, C, P, fast=C != 16), (B, H, T, P, C)
+            assert n == gla.workspace_size(which, B, H, T, 128, 256, C, P, torch.bfloat16)
+    # the headline workload fills the chip unsplit: flags only
+    assert lib.gla_workspace_size(gla.GLA_BWD, 1, 4, 1 << 20, 128, 256, 64, 64, gla.GLA_BF16) == 1024
     assert lib.gla_workspace_size(gla.GLA_FWD, 1, 1, 250, 64, 64, 64, 4, gla.GLA_BF16) == 0  # T % P
     assert lib.gla_workspace_size(7, 1, 1, 256, 64, 64, 64, 4, gla.GLA_BF16) == 0            # unknown call
     assert lib.gla_workspace_size(gla.GLA_BWD, 1, 1, 256, 48, 64, 64, 4, gla.GLA_BF16) == 0  # no kernel

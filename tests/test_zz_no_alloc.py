@@ -1,8 +1,9 @@
 """gla_chunk_fwd_noalloc (the forward's entry point that allocates nothing) against gla_chunk_fwd,
-through the C ABI: bit for bit, on two calls in a row, the second one smaller.  The first call
-uses a strongly decaying gate, so every unit's flag in the static scratch is left set; the second
-uses the default gate, so the fast kernel must overwrite those flags before the exact kernel
-reads them."""
+through the C ABI, on two calls in a row, the second one smaller.  The first call uses a strongly
+decaying gate, so every unit's flag in the static scratch is left set; the second uses the default
+gate, so the fast kernel must overwrite those flags before the exact kernel reads them.
+gla_chunk_fwd cuts these small problems' segments into sub-segments and the no-allocation call
+does not, so the two agree to rounding: max|x - r| / max|r| <= 2e-2 (bf16) and 1e-4 (f32)."""
 import ctypes
 
 import pytest
@@ -34,8 +35,12 @@ def test_noalloc_forward_matches_the_workspace_call(dtype):
         ref = gla.gla_chunk_fwd(d["q"], d["k"], d["v"], d["g"], chunk, P)
         got = gla.gla_chunk_fwd_noalloc(d["q"], d["k"], d["v"], d["g"], chunk, P, *_outputs(d, chunk, P))
         torch.cuda.synchronize()
+        tol = 2e-2 if dtype == "bf16" else 1e-4
         for name, a, b in zip(("o", "chunk_states", "seg_state", "seg_logdecay"), got, ref):
-            assert torch.equal(a, b), (B, H, T, dk, dv, chunk, P, gate, name)
+            a, b = a.double(), b.double()
+            assert not torch.isnan(a).any(), (B, H, T, dk, dv, chunk, P, gate, name)
+            err = float((a - b).abs().max() / b.abs().max())
+            assert err <= tol, (B, H, T, dk, dv, chunk, P, gate, name, err)
 
 
 def test_noalloc_rejects_more_units_than_its_scratch_holds():
