@@ -49,8 +49,8 @@ def log(*a):
 CSRC = os.path.join(ROOT, "sequence_state_scan_amd", "csrc")
 # the sources that build each call's kernels (their hash dates a traffic measurement)
 CALL_SOURCES = {
-    "gla_chunk_fwd": ["gla_fwd.hip", "gla_common.hpp", "gla_kernels.hpp"],
-    "gla_chunk_bwd": ["gla_bwd.hip", "gla_common.hpp", "gla_kernels.hpp"],
+    "gla_chunk_fwd": ["gla_fwd.hip", "gla_exact.hip", "gla_common.hpp", "gla_kernels.hpp"],
+    "gla_chunk_bwd": ["gla_bwd.hip", "gla_exact.hip", "gla_common.hpp", "gla_kernels.hpp"],
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 KERNELS_OF = {"gla_chunk_bwd": " (bwd_kernel)", "gla_chunk_fwd": " (fwd_local_kernel)"}
@@ -75,6 +75,20 @@ def measured_traffic(call, workload):
     if not (m_b and m_h) or m_h.group(1) != sources_hash(call):
         return None
     return int(m_b.group(1))
+
+
+def measured_mfma_busy(call, workload):
+    """MFMA busy fraction of the call's main kernel from the committed counter summary, if it still
+    matches the sources (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", "mfma_%s.md" % workload)
+    if call not in CALL_SOURCES or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^mfma_busy_%s:\s*([0-9.]+)" % call, text, re.M)
+    m_h = re.search(r"^sources_sha256_%s:\s*([0-9a-f]{64})" % call, text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != sources_hash(call):
+        return None
+    return float(m_b.group(1))
 
 
 def alg_bytes(w, part):
@@ -414,7 +428,8 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, w.name),
                 "kernel": dom + KERNELS_OF.get(dom, ""),
                 "alg_bytes_per_launch": dom_bytes,
-                "mfma_frac": round(dom_flops / (per_call[dom] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                "mfma_frac": round(dom_flops / (per_call[dom] / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "mfma_busy_counter": measured_mfma_busy(dom, w.name)}
     step_bytes = alg_bytes(w, "fwd") + alg_bytes(w, "bwd")
     step_flops = alg_flops(w, "fwd") + alg_flops(w, "bwd")
     step_roof = {"alg_bytes": step_bytes, "hbm_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
