@@ -28,17 +28,28 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
   const long st = (long)dk * dv;
   const long off = (long)r * dv + j;
   float acc = hb ? hb[bh * st + off] : 0.f;
-  if (!reverse) {
-    for (int p = 0; p < P; ++p) {
-      const long u = bh * P + p;
-      carry[u * st + off] = acc;
-      acc = fmaf(expf(logdecay[u * dk + r]), acc, state[u * st + off]);
+  // NB segments at a time: their loads are independent of the chain, so all of them are issued
+  // before the dependent multiply-adds (the chain's arithmetic and order are unchanged)
+  constexpr int NB = 8;
+  for (int p0 = 0; p0 < P; p0 += NB) {
+    float d[NB], x[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int p = reverse ? P - 1 - (p0 + i) : p0 + i;
+      if (p0 + i < P) {
+        const long u = bh * P + p;
+        d[i] = logdecay[u * dk + r];
+        x[i] = state[u * st + off];
+      }
     }
-  } else {
-    for (int p = P - 1; p >= 0; --p) {
-      const long u = bh * P + p;
-      carry[u * st + off] = acc;
-      acc = fmaf(expf(logdecay[u * dk + r]), acc, state[u * st + off]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int p = reverse ? P - 1 - (p0 + i) : p0 + i;
+      if (p0 + i < P) {
+        const long u = bh * P + p;
+        carry[u * st + off] = acc;
+        acc = fmaf(expf(d[i]), acc, x[i]);
+      }
     }
   }
   if (hout) hout[bh * st + off] = acc;
