@@ -88,6 +88,17 @@ int split_factor(int B, int H, int T, int P, int chunk, const Kernels& k) {
   return S;
 }
 
+// Sub-segments of the corrections, where the segments alone leave CUs idle: as many as fill the
+// chip, one chunk each at least.  (Cutting finer was slower: a sub-segment's gate walk over the
+// chunks before it grows with the number of cuts.)
+int correct_split(int B, int H, int T, int P, int chunk) {
+  const long long units = (long long)B * H * P;
+  const int nch = T / P / chunk;
+  int S = 1;
+  while (units * S < kFillUnits && nch % (2 * S) == 0) S *= 2;
+  return S;
+}
+
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Workspace of gla_chunk_fwd / gla_chunk_bwd, in this order: one int flag per unit (b, h, segment,
@@ -284,7 +295,8 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
   if (st != GLA_OK) return st;
-  gla::CorrArgs a{q, k, v, g, seg_in, seg_grad, o, chunk_states, dk_, dv_, dg, B * H, T, dk, dv, P};
+  gla::CorrArgs a{q, k, v, g, seg_in, seg_grad, o, chunk_states, dk_, dv_, dg, B * H, T, dk, dv, P,
+                  correct_split(B, H, T, P, chunk)};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == GLA_FWD) {
     if (!q || !g || !seg_in || !o || !chunk_states)

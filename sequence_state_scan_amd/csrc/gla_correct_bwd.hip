@@ -9,6 +9,13 @@
 // g from the chunk's first token to the segment's end).  Every term carries a decay to the
 // segment's end, so the loops walk each segment from its end; with g <= 0 the decays only shrink
 // going back, and once a whole chunk has exp(r_t) == 0.0f nothing before it changes.
+//
+// SPLIT: a segment is cut into a.S sub-segments of consecutive chunks, one workgroup each.  The
+// workgroup of an earlier sub-segment first walks the gate of the chunks after it, from the
+// segment's end, with the same prefix sums in the same order as the one-workgroup walk, so its
+// running sums, its early stop and so its results are bit for bit those of the whole walk.
+// Workgroups are numbered sub-segment first, from the last, so that the last sub-segments of
+// every segment, where the correction is live, are dispatched first.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 
@@ -21,7 +28,7 @@ namespace gla {
 // dk and dv are read and written as merged pairs of 16-column tiles, 16 bytes per lane.  Per live chunk,
 // every read of g, k, V and of the outputs to update is issued first; the global state before the
 // chunk (for R_n) is read after the chunk is known to be live.
-template <typename E, int C, int DK, int DV, int NW>
+template <typename E, int C, int DK, int DV, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_units) {
   constexpr int NT = NW * 64;
   constexpr int RI = C / 16, NCG = DK / 4, NI = 16 * NCG;  // strided items of g and k
@@ -48,11 +55,13 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   E* __restrict__ dk = static_cast<E*>(a.dk);
   E* __restrict__ dv = static_cast<E*>(a.dv);
   float* __restrict__ dg = a.dg;
+  const int NS = SPLIT ? a.S : 1, nseg = a.BH * a.P;  // sub-segments per segment, segments
+  const int sub = SPLIT ? NS - 1 - unit / nseg : 0, seg = SPLIT ? unit - (NS - 1 - sub) * nseg : unit;
   const int L = a.T / a.P;
-  const int nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
+  const int nchunks = L / C, nsub = nchunks / NS;
+  const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const long chunk0 = (long)seg * nchunks;
   constexpr long SS = (long)DK * DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
   const bool krole = w < NCB;            // holds rows 16w.. of G
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
 
   // G rows: Gr[jb][i] = G[16w + n16][16jb + 4g4 + i];  G columns: Gt[jj][kb][i] = G[16kb + 4g4 + i][16jb + n16]
   // with jb = JPW w + jj
-  const float* gp = a.seg_grad + (long)unit * SS;
+  const float* gp = a.seg_grad + (long)seg * SS;
   piece Gr[NJB], Gt[JPW][NKB];
   int nonzero = 0;
 #pragma unroll
@@ -90,7 +99,34 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
   if (!__syncthreads_or(nonzero)) return;  // G_p == 0: nothing to add
 
   float gcarry[4] = {0.f, 0.f, 0.f, 0.f};  // sum of g over the chunks after the current one
-  for (int n = nchunks - 1; n >= 0; --n) {
+  // the gate of the chunks after the sub-segment, from the segment's end, NB chunks' loads in
+  // flight at a time
+  constexpr int NB = 4;
+  const int n_last = (sub + 1) * nsub - 1;  // the sub-segment's last chunk
+  if constexpr (SPLIT) {
+    for (int n0 = nchunks - 1; n0 > n_last; n0 -= NB) {
+      RowsRx4<float, RI> pg[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (n0 - i > n_last && has_item) pg[i].load(g + (tok0 + (long)(n0 - i) * C + n16) * DK + cg * 4, 16 * DK);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (n0 - i > n_last) {
+          float b[RI][4], lam[4];
+          chunk_gate_prefix_strided<RI>(pg[i], has_item, b, lam);
+          int live = 0;
+#pragma unroll
+          for (int r = 0; r < RI; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) live |= (has_item ? __expf(gcarry[e] + (lam[e] - b[r][e])) : 0.f) != 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gcarry[e] += lam[e];
+          if (!__syncthreads_or(live)) return;  // the walk stops before the sub-segment
+        }
+      }
+    }
+  }
+  for (int n = n_last; n >= sub * nsub; --n) {
     const long t0 = tok0 + (long)n * C;
     // ---- every read of the chunk but the state: g, k, V and the outputs to update ----
     RowsRx4<float, RI> pg;
@@ -184,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void correct_bwd_kernel(CorrArgs a, int n_
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-          const f32x4 x = load4(a.seg_in + (long)unit * SS + roff + jb * 16);
+          const f32x4 x = load4(a.seg_in + (long)seg * SS + roff + jb * 16);
           piece sp;
 #pragma unroll
           for (int i = 0; i < 4; ++i) sp[i] = (E)x[i];
@@ -251,8 +287,11 @@ template <typename E, int C, int DK, int DV>
 struct CorrectBwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
-    const int n_units = a.BH * a.P;
-    hipLaunchKernelGGL((correct_bwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.BH * a.P * a.S;
+    if (a.S > 1)
+      hipLaunchKernelGGL((correct_bwd_kernel<E, C, DK, DV, 8, true>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    else
+      hipLaunchKernelGGL((correct_bwd_kernel<E, C, DK, DV, 8, false>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };

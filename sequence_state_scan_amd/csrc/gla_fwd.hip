@@ -397,6 +397,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
 // With g <= 0, a_t only decreases: once every a_t of a chunk is exactly 0.0f, so are all later
 // ones (and the chunk-end decays), and the loop stops.
 //
+// SPLIT: a segment is cut into a.S sub-segments of consecutive chunks, one workgroup each.  The
+// workgroup of a later sub-segment first walks the gate of the chunks before it, with the same
+// prefix sums in the same order as the one-workgroup walk, so its running sums, its early stop and
+// so its results are bit for bit those of the walk over the whole segment.  Workgroups are
+// numbered sub-segment first, so that the first sub-segments of every segment, where the
+// correction is live, are dispatched first.
+//
 // One workgroup of NW waves per unit.  S_in is constant over the segment: wave w owns the JPW
 // adjacent d_v column blocks JPW w.., held in fp32 registers in the store layout (4 consecutive
 // j of one row c) for S_n += a_end S_in, and S_in^T sits in LDS in the element type as the MFMA
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
 // chunk every read (g, q, o, the chunk state) is issued first; o moves as merged pairs of
 // 16-column tiles (16 bytes per lane) in bf16; q * a goes to LDS, double-buffered by chunk parity,
 // so that besides the gate tile's set exchange one barrier per chunk suffices.
-template <typename E, int C, int DK, int DV, int NW>
+template <typename E, int C, int DK, int DV, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_units) {
   typedef GateTile8<E, C, DK, NW * 64> GT;  // items of g and q: 16 tokens x 8 channels
   constexpr int LDQ = lds_ld<E>(DK), LDR = lds_ld<E>(DK);
@@ -425,11 +432,13 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   const float* __restrict__ g = a.g;
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
+  const int NS = SPLIT ? a.S : 1, nseg = a.BH * a.P;  // sub-segments per segment, segments
+  const int sub = SPLIT ? unit / nseg : 0, seg = SPLIT ? unit - sub * nseg : unit;
   const int L = a.T / a.P;
-  const int nchunks = L / C;
-  const int bh = unit / a.P, p = unit - bh * a.P;
+  const int nchunks = L / C, nsub = nchunks / NS;
+  const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L;
-  const long chunk0 = (long)unit * nchunks;
+  const long chunk0 = (long)seg * nchunks;
   constexpr long SS = (long)DK * DV;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), n16 = l & 15, g4 = l >> 4;
   const bool vrole = w * JPW < NJB;  // owns the column blocks JPW w ..
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
 
   // ST[jj][kb][i] = S_in[16kb + 4g4 + (n16&3)][16jb + (n16&~3) + i]  (store layout, fp32);
   // its quad transpose, S_in[16kb + 4g4 + i][16jb + n16], is 4 consecutive c of row j of S_in^T
-  const float* sin = a.seg_in + (long)unit * SS;
+  const float* sin = a.seg_in + (long)seg * SS;
   f32x4 ST[JPW][NKB];
   int nonzero = 0;
   if (vrole) {
@@ -456,7 +465,34 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   if (!__syncthreads_or(nonzero)) return;  // zero incoming state: nothing to add
 
   float carry[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // sum of g from the segment start to the previous chunk's end
-  for (int n = 0; n < nchunks; ++n) {
+  // the gate of the chunks before the sub-segment, NB chunks' loads in flight at a time
+  constexpr int NB = 4;
+  if constexpr (SPLIT) {
+    for (int n0 = 0; n0 < sub * nsub; n0 += NB) {
+      GT pg[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (n0 + i < sub * nsub) pg[i].load(g, nullptr, nullptr, (tok0 + (long)(n0 + i) * C) * DK, tid);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (n0 + i < sub * nsub) {
+          float b[GT::RI][8], lam[8];
+          pg[i].prefix(tid, sTot, b, lam);
+          int live = 0;
+          if (GT::active(tid)) {
+#pragma unroll
+            for (int r = 0; r < GT::RI; ++r)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) live |= __expf(carry[e] + b[r][e]) != 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) carry[e] += lam[e];
+          }
+          if (!__syncthreads_or(live)) return;  // the walk stops before the sub-segment
+        }
+      }
+    }
+  }
+  for (int n = sub * nsub; n < (sub + 1) * nsub; ++n) {
     const long t0 = tok0 + (long)n * C;
     const int par = n & 1;
     E* const cs = cst + (chunk0 + n) * SS;
@@ -582,8 +618,11 @@ template <typename E, int C, int DK, int DV>
 struct CorrectFwdLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const CorrArgs& a = *static_cast<const CorrArgs*>(pa);
-    const int n_units = a.BH * a.P;
-    hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.BH * a.P * a.S;
+    if (a.S > 1)
+      hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV, 8, true>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    else
+      hipLaunchKernelGGL((correct_fwd_kernel<E, C, DK, DV, 8, false>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };

@@ -58,6 +58,7 @@ struct CorrArgs {  // gla_segment_correct
   void *o, *chunk_states, *dk, *dv;
   float* dg;
   int BH, T, Dk, Dv, P;
+  int S;  // sub-segments per segment, one workgroup each (a power of 2 dividing the chunks)
 };
 
 typedef hipError_t (*launch_fn)(const void* args, hipStream_t stream);

@@ -231,6 +231,49 @@ def test_run_to_run_determinism():
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("gate", ["logsigmoid16", "strong", "zero"])
+def test_corrections_are_bitwise_independent_of_the_split(gate):
+    """Where B*H*P leaves CUs idle, both corrections cut each segment into sub-segments.  64 heads x
+    4 segments (256 units) run uncut; 16- and 4-head slices of the same tensors run cut into 4 and 16
+    sub-segments (16 and 1 chunks each).  The results must agree bit for bit, whether the decay dies inside the segment
+    (strong) or never (zero)."""
+    B, H, T, dk, dv, chunk, P = 1, 64, 4096, 128, 256, 64, 4
+    d = dev(inputs.generate(B, H, T, dk, dv, "bf16", 21, True, gate))
+    q, k, v, g = d["q"], d["k"], d["v"], d["g"]
+    rng = np.random.default_rng(5)
+    h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3).cuda()
+    dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3).cuda()
+    o, cs, S_loc, ld = gla.gla_chunk_fwd(q, k, v, g, chunk, P)
+    S_in, _ = gla.gla_segment_scan(S_loc, ld, 1, h_boundary=h0)
+    o_loc, cs_loc = o.clone(), cs.clone()
+    gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=q, g=g, seg_in=S_in, o=o, chunk_states=cs)
+    dq, dk_, dv_, dg, D = gla.gla_chunk_bwd(q, k, v, g, d["do"], cs, S_in, chunk, P)
+    G, _ = gla.gla_segment_scan(D, ld, 1, h_boundary=dhT, reverse=True)
+    local = (dk_.clone(), dv_.clone(), dg.clone())
+    gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=S_in, seg_grad=G, chunk_states=cs,
+                            dk=dk_, dv=dv_, dg=dg)
+    for nh in (16, 4):
+        for h in (0, H - nh):
+            sl = slice(h, h + nh)
+
+            def part(t):  # a copy: with B = 1 a head slice is already contiguous, and the calls write in place
+                return t[:, sl].clone(memory_format=torch.contiguous_format)
+
+            o2, cs2 = part(o_loc), part(cs_loc)
+            gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=part(q), g=part(g), seg_in=part(S_in), o=o2,
+                                    chunk_states=cs2)
+            dk2, dv2, dg2 = (part(t) for t in local)
+            gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=part(k), v=part(v), g=part(g), seg_in=part(S_in),
+                                    seg_grad=part(G), chunk_states=part(cs), dk=dk2, dv=dv2, dg=dg2)
+            torch.cuda.synchronize()
+            say("heads %d..%d of %d %s: o %s cs %s dk %s dv %s dg %s" % (
+                h, h + nh - 1, H, gate, *(bool(torch.equal(x, y[:, sl])) for x, y in
+                                          ((o2, o), (cs2, cs), (dk2, dk_), (dv2, dv_), (dg2, dg)))))
+            for x, y, n in ((o2, o, "o"), (cs2, cs, "chunk_states"), (dk2, dk_, "dk"), (dv2, dv_, "dv"),
+                            (dg2, dg, "dg")):
+                assert torch.equal(x, y[:, sl]), "%s differs with the split (heads %d..%d)" % (n, h, h + nh - 1)
+
+
 def test_scan_is_bitwise_independent_of_K():
     rng = np.random.default_rng(9)
     B, H, P, dk, dv = 2, 3, 7, 64, 48
