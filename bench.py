@@ -248,9 +248,10 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
     return res
 
 
-def path_buffers(torch, gla, w, dev, edt):
+def path_buffers(torch, gla, w, dev, edt, bwd=True):
     """Every output and intermediate of one fwd+bwd step, and the two calls' workspaces, allocated
-    before anything is timed."""
+    before anything is timed.  A forward-only workload keeps no per-chunk states (they exist for
+    the backward only)."""
     B, H, T, dk, dv, C, P = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P
     f32 = torch.float32
     st = (B, H, P, dk, dv)
@@ -258,7 +259,7 @@ def path_buffers(torch, gla, w, dev, edt):
              gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, C, P, edt))
     return {
         "o": torch.empty((B, H, T, dv), device=dev, dtype=edt),
-        "cs": torch.empty((B, H, T // C, dk, dv), device=dev, dtype=edt),
+        "cs": torch.empty((B, H, T // C, dk, dv), device=dev, dtype=edt) if bwd else None,
         "S_loc": torch.empty(st, device=dev, dtype=f32), "ld": torch.empty((B, H, P, dk), device=dev, dtype=f32),
         "S_in": torch.empty(st, device=dev, dtype=f32), "h_fin": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
         "dq": torch.empty((B, H, T, dk), device=dev, dtype=edt), "dk": torch.empty((B, H, T, dk), device=dev, dtype=edt),
@@ -276,7 +277,7 @@ def path_calls(gla, w, x, buf, bwd=True):
     calls = [
         ("gla_chunk_fwd", lambda: gla.gla_chunk_fwd(q, k, v, g, C, P, o=buf["o"], chunk_states=buf["cs"],
                                                      seg_state=buf["S_loc"], seg_logdecay=buf["ld"],
-                                                     workspace=buf["ws"])),
+                                                     workspace=buf["ws"], keep_chunk_states=buf["cs"] is not None)),
         ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
                                                            h_out=buf["h_fin"])),
         ("gla_segment_correct(FWD)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, P, q=q, g=g, seg_in=buf["S_in"],
@@ -331,13 +332,14 @@ def other_workloads(torch, gla, inputs, dev, stream, names, iters=50, warmup=5):
         d = inputs.generate_workload(w, bwd=w.bwd)
         x = {n: t.to(dev) for n, t in d.items()}
         del d
-        buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
+        buf = path_buffers(torch, gla, w, dev, x["q"].dtype, bwd=w.bwd)
         calls = path_calls(gla, w, x, buf, bwd=w.bwd)
         mean, med, per_call = time_scrubbed(torch, calls, iters, warmup, stream, scrub)
         ab = alg_bytes(w, "fwd") + (alg_bytes(w, "bwd") if w.bwd else 0)
         af = alg_flops(w, "fwd") + (alg_flops(w, "bwd") if w.bwd else 0)
         out[name] = {
-            "pass": "fwd+bwd" if w.bwd else "fwd", "tokens_per_s": round(w.B * w.T / (mean / 1e3), 1),
+            "pass": "fwd+bwd" if w.bwd else "fwd", "chunk_states_kept": bool(w.bwd),
+            "tokens_per_s": round(w.B * w.T / (mean / 1e3), 1),
             "ms_mean": round(mean, 4), "ms_median": round(med, 4), "iters": iters,
             "hbm_frac": round(ab / (mean / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(af / (mean / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4), "alg_bytes": ab,

@@ -112,6 +112,8 @@ size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int ch
  *   seg_logdecay[b,h,p,c]   = sum of g over the segment's tokens, float32
  * Inputs q, k, v (dtype), g (float32).  chunk is the tile length C of the chunkwise form.
  * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
+ * chunk_states may be NULL: a forward-only caller (no gla_chunk_bwd to follow) keeps no
+ * per-chunk states, and the other results are the same, bit for bit.
  * workspace: gla_workspace_size(GLA_FWD, ...) bytes of caller device memory (scratch).
  *
  * Tiled chunk-state layout (chunk_states only; every other state argument is row-major
@@ -195,7 +197,8 @@ gla_status gla_segment_scan_allgather(const float* seg_state, const float* seg_l
  *     o[t]            += (q[t] * a_t) . S_in[p]
  *     chunk_states[n] += diag(a at the last token of chunk n) S_in[p]     (n in segment p)
  *   Uses q, g, seg_in; o and chunk_states (dtype) are in/out.  k, v, seg_grad, dk_, dv_, dg
- *   may be NULL.  Afterwards chunk_states holds the GLOBAL state after every chunk.
+ *   may be NULL, and so may chunk_states (a forward-only caller that kept none: then only o is
+ *   corrected).  Afterwards chunk_states holds the GLOBAL state after every chunk.
  * mode == GLA_BWD: with G_p = seg_grad[p] (seg_carry of the reverse scan) and r_t = sum of g
  *   over the tokens after t up to the segment's end:
  *     dk_[t] += exp(r_t) * (G_p v[t])

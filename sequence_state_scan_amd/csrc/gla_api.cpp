@@ -210,9 +210,8 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
   if (st != GLA_OK) return st;
-  if (!q || !k || !v || !g || !o || !chunk_states || !seg_state || !seg_logdecay)
-    return fail(GLA_ERR_INVALID_ARG,
-                "%s: q, k, v, g, o, chunk_states, seg_state and seg_logdecay must be non-null", fn);
+  if (!q || !k || !v || !g || !o || !seg_state || !seg_logdecay)  // chunk_states may be NULL (forward only)
+    return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g, o, seg_state and seg_logdecay must be non-null", fn);
   const void* ins[] = {q, k, v, g};
   for (const void* p : ins)
     if (p == o || p == chunk_states || p == workspace)
@@ -299,8 +298,8 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
                   correct_split(B, H, T, P, chunk)};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == GLA_FWD) {
-    if (!q || !g || !seg_in || !o || !chunk_states)
-      return fail(GLA_ERR_INVALID_ARG, "%s(GLA_FWD): q, g, seg_in, o and chunk_states must be non-null", fn);
+    if (!q || !g || !seg_in || !o)  // chunk_states may be NULL (forward only)
+      return fail(GLA_ERR_INVALID_ARG, "%s(GLA_FWD): q, g, seg_in and o must be non-null", fn);
     return launched(fn, kern.corr_fwd(&a, s));
   }
   if (!k || !v || !g || !seg_in || !seg_grad || !chunk_states || !dk_ || !dv_ || !dg)

@@ -244,8 +244,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
       }
       __syncthreads();
     }
-    // ---- the local state after the chunk, in the tiled chunk-state layout ----
-    if (vrole) {
+    // ---- the local state after the chunk, in the tiled chunk-state layout (none kept for a
+    // forward-only caller) ----
+    if (vrole && cst) {
       E* cs = cst + (chunk0 + n) * (long)DK * DV;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {

@@ -22,7 +22,8 @@ namespace gla {
 // per lane.  After every chunk the state is also written out (chunk_states, element type E, in the
 // tiled chunk-state layout; with two blocks per wave the pair of tiles of each 16-row block leaves
 // as 1024 contiguous bytes): the local chunk states the correction turns into global ones and the
-// backward reads.
+// backward reads.  A forward-only caller passes no chunk_states, and the instance with KEEP false
+// writes none.
 //
 // A chunk in which some channel decays by more than kFastMinChunkLogDecay stops the unit: its flag
 // is set and the exact sub-block kernel (gla_exact.hip) recomputes the whole unit; otherwise the
@@ -34,7 +35,7 @@ namespace gla {
 // chunk's q, k, g, v are requested into registers;
 // (2) the intra-chunk scores; (3) outputs and the state update on MFMA.  The requests of (1) are
 // in flight during (2)-(3).
-template <typename E, int C, int DK, int DV, int NW>
+template <typename E, int C, int DK, int DV, int NW, bool KEEP>
 __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
   typedef GateTile8<E, C, DK, NW * 64> GT;  // items of q, k, g: 16 tokens x 8 channels
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     // serves the intra-chunk outputs and the state update; each A, Qbar and Ktil^T fragment
     // serves all of the wave's column blocks.
     if (w * JPW < NJB) {
-      E* cs = cst + (chunk0 + n) * (long)DK * DV;
+      E* const cs = KEEP ? cst + (chunk0 + n) * (long)DK * DV : nullptr;
       frag fv[JPW][NKS];
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj)
@@ -234,6 +235,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) S[jj][kb] = Mma<E>::mma(fk[ks], fv[jj][ks], S[jj][kb]);
         }
+        if constexpr (!KEEP) continue;  // a forward-only caller keeps no per-chunk states
         if constexpr (JPW == 2) {  // the wave's two blocks are a pair of the tiled layout
           store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), quad_transpose(S[0][kb]),
                                    quad_transpose(S[1][kb]));
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
 //   o_t              += (q_t * a_t) . S_in[p],   a_t = exp(sum of g from the segment start to t)
-//   chunk_states[n]  += diag(a at the end of chunk n) S_in[p]
+//   chunk_states[n]  += diag(a at the end of chunk n) S_in[p]    (unless no chunk states are kept)
 // With g <= 0, a_t only decreases: once every a_t of a chunk is exactly 0.0f, so are all later
 // ones (and the chunk-end decays), and the loop stops.
 //
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
   for (int n = sub * nsub; n < (sub + 1) * nsub; ++n) {
     const long t0 = tok0 + (long)n * C;
     const int par = n & 1;
-    E* const cs = cst + (chunk0 + n) * SS;
+    E* const cs = cst ? cst + (chunk0 + n) * SS : nullptr;  // null: a forward-only caller keeps no chunk states
     // ---- every read of the chunk first ----
     GT pgt;
     pgt.load(g, q, nullptr, t0 * DK, tid);
@@ -514,6 +516,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        if (!cs) break;
         if constexpr (JPW == 2) {
           load_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), cprev[0][kb], cprev[1][kb]);
         } else {
@@ -580,6 +583,7 @@ __global__ __launch_bounds__(NW * 64) void correct_fwd_kernel(CorrArgs a, int n_
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        if (!cs) break;
         const float ae = sAend[par][kb * 16 + 4 * g4 + (n16 & 3)];
         if constexpr (JPW == 2) {
           store_state_pair<E, NJB>(cs, kb, w, state_lane_qt(n16, g4), widen(cprev[0][kb]) + ae * ST[0][kb],
@@ -599,7 +603,10 @@ struct FwdLocalLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
     const int n_units = a.BH * a.P * a.S;
-    hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    if (a.chunk_states)
+      hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DV, 8, true>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    else
+      hipLaunchKernelGGL((fwd_local_kernel<E, C, DK, DV, 8, false>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
     return hipGetLastError();
   }
 };

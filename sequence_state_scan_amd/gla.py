@@ -200,23 +200,28 @@ def _seg_shapes(B, H, T, dk, dv, chunk, P):
 
 
 def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg_state=None, seg_logdecay=None,
-                  workspace=None):
+                  workspace=None, keep_chunk_states: bool = True):
     """Local pass.  Returns (o_local, chunk_states [B,H,T/chunk,dk,dv] (local, q's dtype, each
     state in the tiled layout: chunk_states_dense gives the row-major view),
     seg_state [B,H,P,dk,dv], seg_logdecay [B,H,P,dk]).  ``workspace`` (a device tensor of at
-    least workspace_size(GLA_FWD, ...) bytes) is allocated when not given."""
+    least workspace_size(GLA_FWD, ...) bytes) is allocated when not given.
+    keep_chunk_states=False (a forward-only caller: no backward follows) keeps no per-chunk states
+    and returns None in their place; the other results are the same bit for bit."""
     B, H, T, dk, dv = _head_args(q, k, v, g)
     cs_shape, st_shape, ld_shape = _seg_shapes(B, H, T, dk, dv, chunk, P)
     dev, f32 = q.device, torch.float32
     o = torch.empty_like(v) if o is None else o
-    if chunk_states is None:
+    if not keep_chunk_states:
+        if chunk_states is not None:
+            raise ValueError("chunk_states given with keep_chunk_states=False")
+    elif chunk_states is None:
         chunk_states = torch.empty(cs_shape, device=dev, dtype=q.dtype)
     if seg_state is None:
         seg_state = torch.empty(st_shape, device=dev, dtype=f32)
     if seg_logdecay is None:
         seg_logdecay = torch.empty(ld_shape, device=dev, dtype=f32)
     _expect(o, "o", (B, H, T, dv), q.dtype, dev)
-    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev, optional=not keep_chunk_states)
     _expect(seg_state, "seg_state", st_shape, f32, dev)
     _expect(seg_logdecay, "seg_logdecay", ld_shape, f32, dev)
     ws, nbytes = _workspace(workspace, GLA_FWD, B, H, T, dk, dv, chunk, P, q.dtype, dev)
@@ -228,12 +233,12 @@ def gla_chunk_fwd(q, k, v, g, chunk: int, P: int, o=None, chunk_states=None, seg
 
 def gla_chunk_fwd_noalloc(q, k, v, g, chunk: int, P: int, o, chunk_states, seg_state, seg_logdecay):
     """gla_chunk_fwd without a workspace (the library's static one): every output is the caller's
-    and must be given; nothing is allocated."""
+    and must be given (chunk_states may be None: no per-chunk states kept); nothing is allocated."""
     B, H, T, dk, dv = _head_args(q, k, v, g)
     cs_shape, st_shape, ld_shape = _seg_shapes(B, H, T, dk, dv, chunk, P)
     dev, f32 = q.device, torch.float32
     _expect(o, "o", (B, H, T, dv), q.dtype, dev)
-    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev, optional=True)
     _expect(seg_state, "seg_state", st_shape, f32, dev)
     _expect(seg_logdecay, "seg_logdecay", ld_shape, f32, dev)
     _check(load_library().gla_chunk_fwd_noalloc(_p(q), _p(k), _p(v), _p(g), _p(o), _p(chunk_states), _p(seg_state),
@@ -304,7 +309,8 @@ def gla_segment_correct(mode: int, chunk: int, P: int, q=None, k=None, v=None, g
     cs_shape, st_shape, _ = _seg_shapes(B, H, T, d_k, d_v, chunk, P)
     _expect(g, "g", (B, H, T, d_k), f32, dev)
     _expect(seg_in, "seg_in", st_shape, f32, dev)
-    _expect(chunk_states, "chunk_states", cs_shape, dt, dev)
+    # GLA_FWD may go without chunk states (a forward-only caller kept none)
+    _expect(chunk_states, "chunk_states", cs_shape, dt, dev, optional=mode == GLA_FWD)
     if mode == GLA_FWD:
         _expect(q, "q", (B, H, T, d_k), dt, dev)
         _expect(o, "o", (B, H, T, d_v), dt, dev)
@@ -349,12 +355,15 @@ def gla_chunk_bwd(q, k, v, g, do, chunk_states, seg_in, chunk: int, P: int, dq=N
 
 # ------------------------------------------------------------------------------ method chains
 
-def zeco_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain"):
+def zeco_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain",
+                 keep_chunk_states: bool = True):
     """Local pass -> forward segment scan -> correction.  Returns a dict of tensors:
-    o (global output), chunk_states (global state after every chunk), seg_in (state entering
-    each segment), h_final (state after the last token), seg_state / seg_logdecay (local pass).
+    o (global output), chunk_states (global state after every chunk; None with
+    keep_chunk_states=False, for a forward-only caller), seg_in (state entering each segment),
+    h_final (state after the last token), seg_state / seg_logdecay (local pass).
     scan: "chain" (gla_segment_scan) or "allgather" (gla_segment_scan_allgather)."""
-    o, chunk_states, seg_state, seg_logdecay = gla_chunk_fwd(q, k, v, g, chunk, P)
+    o, chunk_states, seg_state, seg_logdecay = gla_chunk_fwd(q, k, v, g, chunk, P,
+                                                             keep_chunk_states=keep_chunk_states)
     seg_in, h_final = _scan(scan, seg_state, seg_logdecay, K, h0, False)
     gla_segment_correct(GLA_FWD, chunk, P, q=q, g=g, seg_in=seg_in, o=o, chunk_states=chunk_states)
     return {"o": o, "chunk_states": chunk_states, "seg_in": seg_in, "h_final": h_final, "seg_state": seg_state,

@@ -274,6 +274,36 @@ def test_corrections_are_bitwise_independent_of_the_split(gate):
                 assert torch.equal(x, y[:, sl]), "%s differs with the split (heads %d..%d)" % (n, h, h + nh - 1)
 
 
+@pytest.mark.parametrize("B,H,T,dk,dv,chunk,P,dtype,gate", [
+    (1, 4, 1 << 16, 128, 256, 64, 64, "bf16", "logsigmoid16"),  # 256 units: uncut
+    (2, 4, 16384, 128, 256, 64, 1, "bf16", "logsigmoid16"),     # cut into sub-segments
+    (1, 3, 1024, 64, 128, 32, 4, "bf16", "strong5"),            # the exact kernels
+    (1, 3, 1024, 64, 128, 16, 4, "bf16", "weak"),               # bf16 chunk 16: exact kernels
+    (1, 3, 1024, 32, 16, 32, 4, "f32", "logsigmoid16")])
+def test_forward_without_chunk_states(B, H, T, dk, dv, chunk, P, dtype, gate):
+    """A forward-only caller keeps no per-chunk states (chunk_states NULL through the C ABI): the
+    local outputs, segment states and log-decays, and the corrected outputs, equal the run that
+    keeps them bit for bit; and the backward refuses to run without them."""
+    d = dev(inputs.generate(B, H, T, dk, dv, dtype, 3, False, gate))
+    q, k, v, g = d["q"], d["k"], d["v"], d["g"]
+    rng = np.random.default_rng(8)
+    h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3).cuda()
+    with_cs = gla.zeco_forward(q, k, v, g, chunk, P, 1, h0=h0)
+    no_cs = gla.zeco_forward(q, k, v, g, chunk, P, 1, h0=h0, keep_chunk_states=False)
+    loc = gla.gla_chunk_fwd(q, k, v, g, chunk, P, keep_chunk_states=False)
+    loc_cs = gla.gla_chunk_fwd(q, k, v, g, chunk, P)
+    torch.cuda.synchronize()
+    assert no_cs["chunk_states"] is None and loc[1] is None
+    for n in ("o", "seg_state", "seg_logdecay", "seg_in", "h_final"):
+        assert torch.equal(no_cs[n], with_cs[n]), n
+    for i, n in ((0, "o_local"), (2, "seg_state"), (3, "seg_logdecay")):
+        assert torch.equal(loc[i], loc_cs[i]), n
+    with pytest.raises(ValueError):
+        gla.gla_chunk_bwd(q, k, v, g, torch.zeros_like(v), None, no_cs["seg_in"], chunk, P)
+    with pytest.raises(ValueError):
+        gla.gla_chunk_fwd(q, k, v, g, chunk, P, chunk_states=loc_cs[1], keep_chunk_states=False)
+
+
 def test_scan_is_bitwise_independent_of_K():
     rng = np.random.default_rng(9)
     B, H, P, dk, dv = 2, 3, 7, 64, 48
