@@ -49,10 +49,9 @@
  *   - Shapes, dtype, pointers, the workspace size and the supported-shape table are all checked
  *     on the host BEFORE any HIP call; a rejected call enqueues nothing.  A failed launch
  *     returns GLA_ERR_HIP.  gla_last_error() describes the last failure of the calling thread.
- *   - gla_chunk_fwd and gla_chunk_bwd take a caller-owned device workspace of
- *     gla_workspace_size() bytes (one int per unit: which units the exact kernels recompute).
- *     The call writes it before reading it, so its contents on entry do not matter; it must
- *     not be shared by calls that may run at the same time.
+ *   - gla_chunk_fwd and gla_chunk_bwd take a caller-owned device workspace (see
+ *     gla_workspace_size).  The call writes it before reading it, so its contents on entry do
+ *     not matter; it must not be shared by calls that may run at the same time.
  *
  * Supported shapes (gla_supported() answers for a given combination):
  *   GLA_BF16: chunk in {16, 32, 64}; dk in {32, 64, 128}; dv in {32, 64, 128, 256}
@@ -91,9 +90,17 @@ const char* gla_last_error(void);
 
 /*
  * gla_workspace_size -- bytes of device workspace gla_chunk_fwd (which == GLA_FWD) or
- * gla_chunk_bwd (which == GLA_BWD) needs for these arguments: one int per unit (b, h, segment),
- * rounded up to 256 bytes.  Returns 0, with gla_last_error() set, if the arguments are rejected
- * (the same checks as the call itself).  Any alignment of 4 bytes or more will do.
+ * gla_chunk_bwd (which == GLA_BWD) needs for the fastest schedule of these arguments.  The
+ * workspace holds one int per unit (b, h, segment): which units the exact kernels recompute.
+ * When B*H*P units would leave CUs idle (fewer than 256), the call cuts every segment into S
+ * sub-segments (a power of 2) and the workspace also holds, per sub-segment, a float32 state
+ * and log-decay for the in-call scan and its float32 result; the flags are then per
+ * sub-segment.  Each of these regions is rounded up to 256 bytes.
+ * A smaller workspace is accepted down to B*H*P ints rounded up to 256 bytes: the call then
+ * runs as many sub-segments as fit (S halved until they do), or none, with the same results up
+ * to rounding.  (A caller running several calls side by side on one GPU may want exactly that.)
+ * Returns 0, with gla_last_error() set, if the arguments are rejected (the same checks as the
+ * call itself).  Any alignment of 4 bytes or more will do.
  */
 size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype);
 
@@ -114,7 +121,8 @@ size_t gla_workspace_size(int which, int B, int H, int T, int dk, int dv, int ch
  * Outputs are fully overwritten.  Results do not depend on chunk beyond rounding.
  * chunk_states may be NULL: a forward-only caller (no gla_chunk_bwd to follow) keeps no
  * per-chunk states, and the other results are the same, bit for bit.
- * workspace: gla_workspace_size(GLA_FWD, ...) bytes of caller device memory (scratch).
+ * workspace: caller device memory (scratch), gla_workspace_size(GLA_FWD, ...) bytes for the
+ * fastest schedule, at least one int per unit (see gla_workspace_size).
  *
  * Tiled chunk-state layout (chunk_states only; every other state argument is row-major
  * [dk][dv]): a state is (dk/16) x (dv/16) tiles of 16 x 16.  Element (16 cb + c, 16 jb + j)
@@ -229,7 +237,8 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
  *                    own outputs, float32 [dk][dv]
  * q, k, v, do, chunk_states and the outputs dq, dk_, dv_ share dtype.  Outputs are fully
  * overwritten and must not alias inputs.
- * workspace: gla_workspace_size(GLA_BWD, ...) bytes of caller device memory (scratch).
+ * workspace: caller device memory (scratch), gla_workspace_size(GLA_BWD, ...) bytes for the
+ * fastest schedule, at least one int per unit (see gla_workspace_size).
  */
 gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                          const void* do_, const void* chunk_states, const float* seg_in,

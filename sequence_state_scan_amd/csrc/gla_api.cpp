@@ -127,6 +127,13 @@ size_t workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int P, co
   return workspace_layout(B, H, P, dk, dv, split_factor(B, H, T, P, chunk, k)).total;
 }
 
+// The sub-segments a workspace of `bytes` allows: S halved until its layout fits (a smaller
+// workspace runs fewer sub-segments, or none); 0 if not even one flag per unit fits.
+int fitting_split(int S, int B, int H, int P, int dk, int dv, size_t bytes) {
+  while (S > 1 && workspace_layout(B, H, P, dk, dv, S).total > bytes) S /= 2;
+  return workspace_layout(B, H, P, dk, dv, S).total <= bytes ? S : 0;
+}
+
 // Shape checks shared by the chunked entry points.
 gla_status check_shape(const char* fn, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
                        Kernels* kern) {
@@ -218,10 +225,12 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
   int S = split_factor(B, H, T, P, chunk, kern);
   if (max_split > 0 && S > max_split) S = max_split;
+  if (workspace) S = fitting_split(S, B, H, P, dk, dv, workspace_size);
+  if (!workspace || S == 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs at least %zu bytes (one int per unit; "
+                "gla_workspace_size gives the size for the fastest schedule), got %zu", fn,
+                workspace_layout(B, H, P, dk, dv, 1).total, workspace ? workspace_size : (size_t)0);
   const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
-  if (!workspace || workspace_size < lay.total)
-    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
-                lay.total, workspace ? workspace_size : (size_t)0);
   char* ws = static_cast<char*>(workspace);
   gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, reinterpret_cast<int*>(ws + lay.flags),
                  B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
@@ -322,11 +331,12 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
   for (const void* p : ins)
     if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace)
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
-  const int S = split_factor(B, H, T, P, chunk, kern);
+  const int S = workspace ? fitting_split(split_factor(B, H, T, P, chunk, kern), B, H, P, dk, dv, workspace_size) : 0;
+  if (S == 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs at least %zu bytes (one int per unit; "
+                "gla_workspace_size gives the size for the fastest schedule), got %zu", fn,
+                workspace_layout(B, H, P, dk, dv, 1).total, workspace ? workspace_size : (size_t)0);
   const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
-  if (!workspace || workspace_size < lay.total)
-    return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs %zu bytes (gla_workspace_size), got %zu", fn,
-                lay.total, workspace ? workspace_size : (size_t)0);
   char* ws = static_cast<char*>(workspace);
   gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate,
                  reinterpret_cast<int*>(ws + lay.flags), B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};

@@ -166,16 +166,21 @@ def workspace_size(which: int, B: int, H: int, T: int, dk: int, dv: int, chunk: 
     return int(n)
 
 
+def flags_workspace_size(B: int, H: int, P: int) -> int:
+    """The smallest workspace gla_chunk_fwd / gla_chunk_bwd accept (include/gla.h,
+    gla_workspace_size): one int per unit (b, h, segment), rounded up to 256 bytes.  With it a call
+    cuts no segment into sub-segments."""
+    return (B * H * P * 4 + 255) // 256 * 256
+
+
 def _workspace(ws, which, B, H, T, dk, dv, chunk, P, dtype, device):
-    need = workspace_size(which, B, H, T, dk, dv, chunk, P, dtype)
+    """The caller's workspace, or one of the size for the fastest schedule.  A smaller one is the
+    library's to accept (fewer sub-segments) or reject, before any HIP call."""
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = torch.empty(workspace_size(which, B, H, T, dk, dv, chunk, P, dtype), dtype=torch.uint8, device=device)
     if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % device)
-    nbytes = ws.numel() * ws.element_size()
-    if nbytes < need:
-        raise ValueError("workspace has %d bytes, the call needs %d" % (nbytes, need))
-    return ws, nbytes
+    return ws, ws.numel() * ws.element_size()
 
 
 # ------------------------------------------------------------------------------------ C calls
@@ -407,8 +412,9 @@ def zeco_step_streams(q, k, v, g, do, chunk: int, P: int, K: int, n_streams: int
     calls (local pass, scan, correction; local backward, reverse scan, correction) in order on a
     stream of its own.  The streams fork from torch's current stream and join back into it, so
     the result is ordered like any other call on the current stream.  While one group runs its
-    scans and corrections, another group's local passes can use the CUs they leave free (every unit
-    is computed exactly as in the one-stream chain, so the results are identical bit for bit).
+    scans and corrections, another group's local passes can use the CUs they leave free.  The
+    groups' calls get flag-only workspaces, so none cuts its segments into sub-segments: every unit
+    is computed exactly as in the one-stream chain run with such workspaces, bit for bit.
 
     ``out``: optional dict of preallocated buffers (as returned by a previous call) to reuse.
     ``stagger``: each group's chain waits for the previous group's local pass, so that a group's
@@ -435,11 +441,10 @@ def zeco_step_streams(q, k, v, g, do, chunk: int, P: int, K: int, n_streams: int
     n = max(1, min(n_streams, BH))
     bounds = [BH * i // n for i in range(n + 1)]
     if "workspaces" not in out or len(out["workspaces"]) != n:
-        out["workspaces"] = []
-        for i in range(n):
-            sz = max(workspace_size(GLA_FWD, bounds[i + 1] - bounds[i], 1, T, dk_, dv_, chunk, P, edt),
-                     workspace_size(GLA_BWD, bounds[i + 1] - bounds[i], 1, T, dk_, dv_, chunk, P, edt))
-            out["workspaces"].append(torch.empty(sz, device=dev, dtype=torch.uint8))
+        # flags only: a group's calls cut no segment into sub-segments, because the groups share the
+        # chip; each call on its own would cut its fewer units to fill it
+        out["workspaces"] = [torch.empty(flags_workspace_size(bounds[i + 1] - bounds[i], 1, P), device=dev,
+                                         dtype=torch.uint8) for i in range(n)]
     main = torch.cuda.current_stream(dev)
     streams = _side_streams(dev, n)
     local_done = None

@@ -54,16 +54,17 @@ def dev(d):
     return {k: v.to("cuda") for k, v in d.items()}
 
 
-def gpu_pipeline(d, chunk, P, K, bwd, h0=None, dhT=None):
-    """Every step through the C ABI, keeping the intermediates.  Returns float64 numpy arrays."""
+def gpu_pipeline(d, chunk, P, K, bwd, h0=None, dhT=None, ws=None):
+    """Every step through the C ABI, keeping the intermediates.  Returns float64 numpy arrays.
+    ws: the workspace of both chunked calls (default: the size for the fastest schedule)."""
     q, k, v, g = d["q"], d["k"], d["v"], d["g"]
-    o, cs, S_loc, ld = gla.gla_chunk_fwd(q, k, v, g, chunk, P)
+    o, cs, S_loc, ld = gla.gla_chunk_fwd(q, k, v, g, chunk, P, workspace=ws)
     res = {"o_local": o.clone(), "cs_local": gla.chunk_states_dense(cs), "S_local": S_loc, "logdecay": ld}
     S_in, h_final = gla.gla_segment_scan(S_loc, ld, K, h_boundary=h0)
     gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=q, g=g, seg_in=S_in, o=o, chunk_states=cs)
     res.update(S_in=S_in, h_final=h_final, o=o, cs=gla.chunk_states_dense(cs))
     if bwd:
-        dq, dk, dv, dg, D = gla.gla_chunk_bwd(q, k, v, g, d["do"], cs, S_in, chunk, P)
+        dq, dk, dv, dg, D = gla.gla_chunk_bwd(q, k, v, g, d["do"], cs, S_in, chunk, P, workspace=ws)
         res.update(dq=dq, dk_local=dk.clone(), dv_local=dv.clone(), dg_local=dg.clone(), D_local=D)
         G, dh0 = gla.gla_segment_scan(D, ld, K, h_boundary=dhT, reverse=True)
         gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=S_in, seg_grad=G,
@@ -355,8 +356,9 @@ def test_allgather_pipeline_matches_chain_pipeline():
 @pytest.mark.parametrize("n_streams", [2, 3])
 def test_multi_stream_schedule(n_streams):
     # the sequences split over several streams, each group's six calls on its own stream: bit for
-    # bit the one-stream chain, and the oracle's results (boundary states given, one group of
-    # sequences taking the exact kernels through a strongly decaying stretch)
+    # bit the one-stream chain with flag-only workspaces (no sub-segments, as the groups run), and
+    # the oracle's results (boundary states given, one group of sequences taking the exact kernels
+    # through a strongly decaying stretch)
     B, H, T, dk, dv, chunk, P, K = 2, 3, 2048, 64, 128, 64, 4, 2
     d = inputs.generate(B, H, T, dk, dv, "bf16", 19, True, "logsigmoid16")
     d["g"][1, 2, 700:760] = -3.0
@@ -366,7 +368,8 @@ def test_multi_stream_schedule(n_streams):
     x = dev(d)
     got = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], chunk, P, K, n_streams,
                                 h0=h0.cuda(), dhT=dhT.cuda())
-    one = gpu_pipeline(x, chunk, P, K, True, h0.cuda(), dhT.cuda())
+    ws = torch.empty(gla.flags_workspace_size(B, H, P), dtype=torch.uint8, device="cuda")
+    one = gpu_pipeline(x, chunk, P, K, True, h0.cuda(), dhT.cuda(), ws=ws)
     torch.cuda.synchronize()
     names = {"o": "o", "h_final": "h_final", "dq": "dq", "dk": "dk", "dv": "dv", "dg": "dg", "dh0": "dh0",
              "seg_in": "S_in", "seg_grad": "G"}
@@ -375,6 +378,45 @@ def test_multi_stream_schedule(n_streams):
     ref = oracle_pipeline(d, chunk, P, True, h0.numpy(), dhT.numpy())
     check({k_: one[k_] for k_ in ("o", "h_final", "dq", "dk", "dv", "dg", "dh0")}, ref,
           ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL["bf16"], "%d streams" % n_streams)
+
+
+def _layout_bytes(units, dk, dv, S):
+    """The workspace rule of include/gla.h (gla_workspace_size) for S sub-segments per segment."""
+    a = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    u = units * S
+    return a(4 * u) + (a(4 * u * dk * dv) + a(4 * u * dk) + a(4 * u * dk * dv) if S > 1 else 0)
+
+
+def test_small_workspace_runs_fewer_sub_segments():
+    """A workspace below gla_workspace_size (down to the flags) runs fewer sub-segments, or none.
+    8 units of 32 chunks are cut into 16 with the full workspace; here also into 4 and 1.  Every
+    run matches the oracle, the runs agree to rounding, and the flags-only forward equals
+    gla_chunk_fwd_noalloc (which never cuts) bit for bit."""
+    B, H, T, dk, dv, chunk, P, K = 2, 2, 4096, 64, 128, 64, 2, 1
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 23, True, "logsigmoid16")
+    x = dev(d)
+    full = gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, chunk, P, torch.bfloat16)
+    assert full == _layout_bytes(B * H * P, dk, dv, 16)
+    ref = oracle_pipeline(d, chunk, P, True)
+    runs = {}
+    for S in (16, 4, 1):
+        ws = torch.empty(_layout_bytes(B * H * P, dk, dv, S) + (255 if S < 16 else 0), dtype=torch.uint8,
+                         device="cuda")
+        runs[S] = gpu_pipeline(x, chunk, P, K, True, ws=ws)
+        check(runs[S], ref, FWD_KEYS + BWD_KEYS, TOL["bf16"], "workspace for %d sub-segments" % S)
+    for S in (4, 1):
+        for n in ("o", "dq", "dk", "dv", "dg"):
+            assert maxrel(runs[S][n], runs[16][n]) < 1e-2, (S, n)  # bf16 outputs: a few ulps
+    o = torch.empty_like(x["v"])
+    cs = torch.empty((B, H, T // chunk, dk, dv), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((B, H, P, dk, dv), device="cuda")
+    ld = torch.empty((B, H, P, dk), device="cuda")
+    gla.gla_chunk_fwd_noalloc(x["q"], x["k"], x["v"], x["g"], chunk, P, o, cs, st, ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(as_f64(o), runs[1]["o_local"]) and np.array_equal(as_f64(st), runs[1]["S_local"])
+    with pytest.raises(gla.GLAError):  # below the flags
+        gla.gla_chunk_fwd(x["q"], x["k"], x["v"], x["g"], chunk, P,
+                          workspace=torch.empty(255, dtype=torch.uint8, device="cuda"))
 
 
 def test_state_carry_across_calls():
