@@ -25,7 +25,8 @@
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers owned by the caller (for example torch tensors).
- *     The library never allocates, frees or keeps device memory, and never writes inputs.
+ *     The library never allocates or frees device memory and never writes inputs; the one
+ *     memory it keeps is gla_chunk_fwd_noalloc's static array (256 KiB per GPU).
  *   - All tensors are contiguous, row-major:
  *       q, k, dq, dk, g, dg:   [B][H][T][dk]
  *       v, o, do, dv:          [B][H][T][dv]
