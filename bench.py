@@ -173,26 +173,31 @@ def cpu_baseline(w, gate, budget_s=15.0, budget_1t_s=5.0):
 
 
 def time_steps(torch, calls, steps, warmup, stream):
-    """Warm up, then time `steps` passes over `calls` with events on the launch stream.
-    Returns (ms per step, mean ms per call, wall seconds of the timed region)."""
+    """Warm up, then time `steps` passes over `calls` with events on the launch stream, twice: once
+    with events around the whole timed region only (the step time: an event recorded between two
+    calls leaves the GPU idle for about 10 us), then with events around every call (the per-call
+    breakdown).  Returns (ms per step, mean ms per call, wall seconds of the first timed region)."""
     for _ in range(warmup):
         for _, fn in calls:
             fn()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-          for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
+    for _ in range(steps):
+        for _, fn in calls:
+            fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(steps)]
     for s in range(steps):
         for i, (_, fn) in enumerate(calls):
             ev[s][i][0].record(stream)
             fn()
             ev[s][i][1].record(stream)
-    stop.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     per_call = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
                 for i, (name, _) in enumerate(calls)}
     return start.elapsed_time(stop) / steps, per_call, wall
