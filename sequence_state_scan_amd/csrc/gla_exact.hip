@@ -58,11 +58,8 @@ struct SubGate {
 };
 
 // part[s] = sum over the thread's 4 channels of q_t k_s exp(b_t - b_s) for s <= t, 0 for s > t.
-// Then summed over the 4 lane rows of the wave (reduce-scatter): lane row g4 ends with the sums
-// of s = 4 g4 .. 4 g4 + 3 in r[0..3].
 template <typename E>
-__device__ __forceinline__ f32x4 diag_scores(const SubGate<E>& x, int t) {
-  float part[16];
+__device__ __forceinline__ void diag_parts(const SubGate<E>& x, int t, float (&part)[16]) {
   static_for<0, 16>([&](auto S) {
     constexpr int s = decltype(S)::value;
     float acc = 0.f;
@@ -74,6 +71,11 @@ __device__ __forceinline__ f32x4 diag_scores(const SubGate<E>& x, int t) {
     part[s] = s <= t ? acc : 0.f;  // a select: the discarded exponent may be positive
     __builtin_amdgcn_sched_barrier(0);  // one s at a time: bounded register use
   });
+}
+
+// The parts summed over the 4 lane rows of the wave (reduce-scatter): lane row g4 ends with the
+// sums of s = 4 g4 .. 4 g4 + 3 in r[0..3].
+__device__ __forceinline__ f32x4 reduce_scores(const float (&part)[16]) {
   const int g4 = lane_id() >> 4, hi = g4 >> 1, lo = g4 & 1;
   float r1[8];
 #pragma unroll
@@ -198,7 +200,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
         if (NVP % NT == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
       }
       if (w < NGW) {
-        const f32x4 r = diag_scores(x, t);
+float part[16];
+        diag_parts(x, t, part);
+        const f32x4 r = reduce_scores(part);
         *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
       }
       __syncthreads();
@@ -405,20 +409,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       // ---- element-wise sums inside the sub-block: scores, and the intra parts of dq and dk ----
       f32x4 dqd = zero4(), dkd = zero4();
       if (urole) {
+        // one exponential of b_t - b_s serves the scores and dq (the scores' sums as in diag_parts)
+        float part[16];
         static_for<0, 16>([&](auto S) {
           constexpr int s = decltype(S)::value;
           const float dats = sdA[t][s], dast = sdA[s][t];
+          float acc = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float ks = row_bcast<s>(x.k[e]), qs = row_bcast<s>(x.q[e]), bs = row_bcast<s>(x.b[e]);
-            const float et = s <= t ? __expf(x.b[e] - bs) : 0.f;  // token s up to token t
+            const float ets = __expf(x.b[e] - bs);
+            const float et = s <= t ? ets : 0.f;  // token s up to token t
             const float es = s >= t ? __expf(bs - x.b[e]) : 0.f;  // token t up to token s
             dqd[e] += dats * ks * et;
             dkd[e] += dast * qs * es;
+            acc += x.q[e] * ks * ets;
           }
+          part[s] = s <= t ? acc : 0.f;  // a select: the discarded exponent may be positive
           __builtin_amdgcn_sched_barrier(0);  // one s at a time: bounded register use
         });
-        const f32x4 r = diag_scores(x, t);
+        const f32x4 r = reduce_scores(part);
         *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
       }
       __syncthreads();
