@@ -559,14 +559,14 @@ template <> struct Vec8<bf16> {
   __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
 };
 template <> struct Vec8<float> {
-  float4 a, b;
+  f32x4 a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
+    a = load4(p);
+    b = load4(p + 4);
   }
   __device__ __forceinline__ void store(float* p) const {
-    *reinterpret_cast<float4*>(p) = a;
-    *reinterpret_cast<float4*>(p + 4) = b;
+    store4(p, a);
+    store4(p + 4, b);
   }
 };
 

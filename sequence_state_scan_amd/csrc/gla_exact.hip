@@ -39,21 +39,28 @@ constexpr int kSB = 16;  // tokens per sub-block
 template <typename E>
 struct SubGate {
   f32x4 q, k, b, lam;  // b: inclusive running sum of g inside the sub-block; lam: its total
-  __device__ __forceinline__ void load(const E* qp, const E* kp, const float* gp, long tok, int DK, int R,
-                                       bool act) {
-    f32x4 g = zero4();
-    q = k = zero4();
+  // the loads alone (b holds the raw gate until scan())
+  __device__ __forceinline__ void fetch(const E* qp, const E* kp, const float* gp, long tok, int DK, int R,
+                                        bool act) {
+    b = q = k = zero4();
     if (act) {
       const long off = tok * DK + 4 * R;
       q = load4(qp + off);
       k = load4(kp + off);
-      g = load4(gp + off);
+      b = load4(gp + off);
     }
+  }
+  __device__ __forceinline__ void scan() {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      b[e] = seg_scan_incl<16>(g[e]);
+      b[e] = seg_scan_incl<16>(b[e]);
       lam[e] = seg_last<16>(b[e]);
     }
+  }
+  __device__ __forceinline__ void load(const E* qp, const E* kp, const float* gp, long tok, int DK, int R,
+                                       bool act) {
+    fetch(qp, kp, gp, tok, DK, R, act);
+    scan();
   }
 };
 
@@ -90,6 +97,16 @@ __device__ __forceinline__ f32x4 reduce_scores(const float (&part)[16]) {
     r[i] = mine + __shfl_xor(other, 16);
   }
   return r;
+}
+
+// A sub-block's gate items and one 8-element piece of its dO per thread (threads beyond the NVS
+// pieces re-read the last one, which they never store), issued ahead of their use.
+template <typename E, int DK, int DV, int NVS>
+__device__ __forceinline__ void fetch_sub_block(SubGate<E>& x, Vec8<E>& pd, const E* q, const E* k, const float* g,
+                                                const E* dO, long ts, int tid, bool act) {
+  x.fetch(q, k, g, ts + (tid & 15), DK, tid >> 4, act);
+  const int pc = tid < NVS ? tid : NVS - 1;
+  pd.load(dO + (ts + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
 }
 
 // The lane's 4 accumulator columns of a state tile pair / piece from the tiled chunk-state layout
@@ -356,6 +373,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
     for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
   }
 
+  // the next sub-block's gate items and dO piece, fetched one sub-block ahead of their use; the walk
+  // goes backwards through contiguous chunks, so the next sub-block is always the previous 16 tokens
+  static_assert(NVS <= NT, "one piece of a sub-block's dO per thread");
+  SubGate<E> xn;
+  Vec8<E> pdn;
+  fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, tok0 + (long)(nchunks - 1) * C + (NSB - 1) * kSB, threadIdx.x,
+                                   urole);
+
   for (int n = nchunks - 1; n >= 0; --n) {
     const long tc0 = tok0 + (long)n * C;
     const int tid = fresh_tid(), R = tid >> 4, t = tid & 15;
@@ -391,13 +416,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       const long ts0 = tc0 + j * kSB;
       // lane indices re-derived here, so the per-lane addresses are not held across the loop
       const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4, R = tid >> 4, t = n16;
-      SubGate<E> x;
-      x.load(q, k, a.g, ts0 + t, DK, R, urole);
-      for (int pc = tid; pc < NVS; pc += NT) {
-        Vec8<E> pd;
-        pd.load(dO + (ts0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
-        pd.store(sdO + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
-      }
+      SubGate<E> x = xn;  // fetched one sub-block ahead
+      x.scan();
+      if (NVS == NT || tid < NVS) pdn.store(sdO + (tid / (DV / 8)) * LDV + (tid % (DV / 8)) * 8);
+      if (n > 0 || j > 0) fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, ts0 - kSB, tid, urole);
       __syncthreads();
       // ---- dA[t][s] = dO_t . V_s (s <= t) ----
       if (w == 0) {
