@@ -99,14 +99,15 @@ __device__ __forceinline__ f32x4 reduce_scores(const float (&part)[16]) {
   return r;
 }
 
-// A sub-block's gate items and one 8-element piece of its dO per thread (threads beyond the NVS
-// pieces re-read the last one, which they never store), issued ahead of their use.
-template <typename E, int DK, int DV, int NVS>
-__device__ __forceinline__ void fetch_sub_block(SubGate<E>& x, Vec8<E>& pd, const E* q, const E* k, const float* g,
-                                                const E* dO, long ts, int tid, bool act) {
+// A sub-block's gate items, and one 8-element piece per thread of a [token][DV] tensor of the
+// sub-block (V in the forward, dO in the backward; threads beyond the NP pieces re-read the last
+// one, which they never store), issued ahead of their use.
+template <typename E, int DK, int DV, int NP>
+__device__ __forceinline__ void fetch_sub_block(SubGate<E>& x, Vec8<E>& piece, const E* q, const E* k, const float* g,
+                                                const E* rows, long ts, int tid, bool act) {
   x.fetch(q, k, g, ts + (tid & 15), DK, tid >> 4, act);
-  const int pc = tid < NVS ? tid : NVS - 1;
-  pd.load(dO + (ts + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+  const int pc = tid < NP ? tid : NP - 1;
+  piece.load(rows + (ts + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
 }
 
 // The lane's 4 accumulator columns of a state tile pair / piece from the tiled chunk-state layout
@@ -182,18 +183,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
     }
   f32x4 ldsum = zero4();  // log cumulative decay of the segment, channels 4R ..
 
+  // the next sub-block's gate items and V piece, fetched one sub-block ahead of their use (the walk
+  // goes forwards through contiguous chunks: the next sub-block is always the next 16 tokens)
+  static_assert(VPT == 1, "one piece of a sub-block's V per thread");
+  SubGate<E> xn;
+  Vec8<E> pvn;
+  fetch_sub_block<E, DK, DV, NVP>(xn, pvn, q, k, a.g, v, tok0, tid, gact);
+
   for (int n = 0; n < nchunks; ++n) {
     for (int j = 0; j < NSB; ++j) {
       const long ts0 = tok0 + (long)n * C + j * kSB;
       // ---- gate prefix, Qbar, Ktil, V -> LDS; element-wise scores of the sub-block ----
-      SubGate<E> x;
-      x.load(q, k, a.g, ts0 + t, DK, R, gact);
-      Vec8<E> pv[VPT];
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int pc = tid + NT * i;
-        if (NVP % NT == 0 || pc < NVP) pv[i].load(v + (ts0 + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
-      }
+      SubGate<E> x = xn;
+      x.scan();
+      if (NVP == NT || tid < NVP) pvn.store(sV + (tid / (DV / 8)) * LDV + (tid % (DV / 8)) * 8);
+      if (n < nchunks - 1 || j < NSB - 1) fetch_sub_block<E, DK, DV, NVP>(xn, pvn, q, k, a.g, v, ts0 + kSB, tid, gact);
       if (gact) {
         f32x4 xq, xk;
 #pragma unroll
@@ -211,13 +215,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
         }
         ldsum += x.lam;
       }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int pc = tid + NT * i;
-        if (NVP % NT == 0 || pc < NVP) pv[i].store(sV + (pc / (DV / 8)) * LDV + (pc % (DV / 8)) * 8);
-      }
       if (w < NGW) {
-float part[16];
+        float part[16];
         diag_parts(x, t, part);
         const f32x4 r = reduce_scores(part);
         *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
