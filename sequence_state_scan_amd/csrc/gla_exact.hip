@@ -430,7 +430,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       // ---- element-wise sums inside the sub-block: scores, and the intra parts of dq and dk ----
       f32x4 dqd = zero4(), dkd = zero4();
       if (urole) {
-        // one exponential of b_t - b_s serves the scores and dq (the scores' sums as in diag_parts)
+        // one exponential per (t, s, channel) serves the scores, dq and dk: exp(b_t - b_s) for s <= t
+        // (scores and dq), exp(b_s - b_t) for s >= t (dk); -(b_t - b_s) is b_s - b_t exactly.  (The
+        // scores' sums run as in diag_parts; their s > t terms are dropped by the select below.)
         float part[16];
         static_for<0, 16>([&](auto S) {
           constexpr int s = decltype(S)::value;
@@ -439,12 +441,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float ks = row_bcast<s>(x.k[e]), qs = row_bcast<s>(x.q[e]), bs = row_bcast<s>(x.b[e]);
-            const float ets = __expf(x.b[e] - bs);
-            const float et = s <= t ? ets : 0.f;  // token s up to token t
-            const float es = s >= t ? __expf(bs - x.b[e]) : 0.f;  // token t up to token s
+            const float d = x.b[e] - bs;
+            const float ex = __expf(s <= t ? d : -d);  // never a positive exponent
+            const float et = s <= t ? ex : 0.f;  // token s up to token t
+            const float es = s >= t ? ex : 0.f;  // token t up to token s
             dqd[e] += dats * ks * et;
             dkd[e] += dast * qs * es;
-            acc += x.q[e] * ks * ets;
+            acc += x.q[e] * ks * ex;
           }
           part[s] = s <= t ? acc : 0.f;  // a select: the discarded exponent may be positive
           __builtin_amdgcn_sched_barrier(0);  // one s at a time: bounded register use
