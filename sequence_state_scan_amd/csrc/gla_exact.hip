@@ -420,6 +420,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       if (NVS == NT || tid < NVS) pdn.store(sdO + (tid / (DV / 8)) * LDV + (tid % (DV / 8)) * 8);
       if (n > 0 || j > 0) fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, ts0 - kSB, tid, urole);
       __syncthreads();
+      // the stored global state before the chunk, requested here and used after the element-wise
+      // sums (the segment's first chunk starts from seg_in, read where it is used)
+      const bool from_store = n > 0 || sub > 0;
+      typename Piece4<E>::type Sc[NJB];
+      if (urole && from_store) {
+        const E* st = cst + (chunk0 + n - 1) * SS;
+        const int L = state_lane_row(n16, g4);
+        if constexpr (NJB % 2 == 0) {
+#pragma unroll
+          for (int m = 0; m < NJB / 2; ++m) load_state_pair<E, NJB>(st, w, m, L, Sc[2 * m], Sc[2 * m + 1]);
+        } else {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) Sc[jb] = load_state_piece<E, NJB>(st, w, jb, L);
+        }
+      }
       // ---- dA[t][s] = dO_t . V_s (s <= t) ----
       if (w == 0) {
         const f32x4 acc = mma<E, false, false>(zero4(), sdO, LDV, sV + j * kSB * LDV, LDV, 0, DV);
@@ -470,8 +485,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       if (urole) {
         // the stored state before the chunk, advanced through the chunk's earlier sub-blocks
         f32x4 Sf[NJB];
-        if (n > 0 || sub > 0) {
-          load_state_rows<E, NJB>(cst + (chunk0 + n - 1) * SS, w, Sf);
+        if (from_store) {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) Sf[jb] = widen(Sc[jb]);
         } else {
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb)
