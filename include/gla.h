@@ -96,10 +96,17 @@ const char* gla_last_error(void);
  * When B*H*P units would leave CUs idle (fewer than 256), the call cuts every segment into S
  * sub-segments (a power of 2) and the workspace also holds, per sub-segment, a float32 state
  * and log-decay for the in-call scan and its float32 result; the flags are then per
- * sub-segment.  Each of these regions is rounded up to 256 bytes.
- * A smaller workspace is accepted down to B*H*P ints rounded up to 256 bytes: the call then
- * runs as many sub-segments as fit (S halved until they do), or none, with the same results up
- * to rounding.  (A caller running several calls side by side on one GPU may want exactly that.)
+ * sub-segment (unit).  Then, when units have at least 4 chunks, the region for the re-split of
+ * flagged units: R = min(256, units * xmax) slots, xmax the largest power of 2 that divides a
+ * unit's chunks into pieces of at least 2; 2 + R ints, and per slot the same three float32
+ * arrays.  (A unit is flagged when one of its chunks decays too fast for the fast kernels; the
+ * flagged units are cut into pieces that fill the R slots and redone piece by piece, so a few
+ * such units cost about as much as one piece each, not a whole unit each.)  Each of these
+ * regions is rounded up to 256 bytes.
+ * A smaller workspace is accepted down to B*H*P ints rounded up to 256 bytes: the call first
+ * gives up the re-split, then halves S and tries the re-split again, down to no sub-segments
+ * and no re-split, with the same results up to rounding.  (A caller running several calls side
+ * by side on one GPU may want fewer sub-segments.)
  * Returns 0, with gla_last_error() set, if the arguments are rejected (the same checks as the
  * call itself).  Any alignment of 4 bytes or more will do.
  */

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgla.so")
-SOURCES = ["gla_fwd.hip", "gla_bwd.hip", "gla_correct_bwd.hip", "gla_exact.hip", "gla_scan.hip", "gla_noalloc.hip", "gla_api.cpp"]
+SOURCES = ["gla_fwd.hip", "gla_bwd.hip", "gla_correct_bwd.hip", "gla_exact.hip", "gla_scan.hip", "gla_resplit.hip", "gla_noalloc.hip", "gla_api.cpp"]
 ARCH = "gfx950"
 
 CFLAGS = [

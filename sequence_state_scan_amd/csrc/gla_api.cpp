@@ -99,39 +99,88 @@ int correct_split(int B, int H, int T, int P, int chunk) {
   return S;
 }
 
+// The re-split of flagged units.  A unit the fast kernel flags is redone by the exact sub-block
+// kernels, several times slower per token: alone it would keep one workgroup busy long after the
+// rest of the chip is done.  So the flagged units are listed on the device and each is cut into X
+// pieces of at least 2 chunks, with X chosen there from how many were flagged, so that the pieces
+// fill R slots (workgroups): a state pass over the pieces, the scan over each unit's pieces, then
+// the exact kernels run every piece from its true incoming state.  Flagged units beyond R run
+// whole, as before.  xmax: the most pieces a unit of S-split segments allows.
+int resplit_xmax(int T, int P, int S, int chunk) {
+  const int nch = T / P / S / chunk;
+  int X = 1;
+  while (nch % (2 * X) == 0 && nch / (2 * X) >= 2) X *= 2;
+  return X;
+}
+int resplit_slots(int B, int H, int T, int P, int S, int chunk, const Kernels& k) {
+  if (!k.fwd) return 0;  // every unit runs the exact kernels, split as the units are
+  const int x = resplit_xmax(T, P, S, chunk);
+  if (x < 2) return 0;
+  const long long slots = (long long)B * H * P * S * x;
+  return (int)(slots < kFillUnits ? slots : kFillUnits);
+}
+
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Workspace of gla_chunk_fwd / gla_chunk_bwd, in this order: one int flag per unit (b, h, segment,
 // sub-segment); with S > 1 the sub-segments' states from the state pass, their summed log-gates,
-// and the scan's incoming states (forward) or gradients (backward), all float32.
+// and the scan's incoming states (forward) or gradients (backward), all float32; with R > 0 the
+// re-split's list (2 + R ints) and per slot the same three float32 arrays.
 struct Workspace {
-  size_t flags, sub_state, sub_ld, carry, total;
+  size_t flags, sub_state, sub_ld, carry, list, r_state, r_ld, r_carry, total;
 };
-Workspace workspace_layout(int B, int H, int P, int dk, int dv, int S) {
-  const size_t u = (size_t)B * H * P * S;
+Workspace workspace_layout(int B, int H, int P, int dk, int dv, int S, int R) {
+  const size_t u = (size_t)B * H * P * S, ss = (size_t)dk * dv * sizeof(float);
   Workspace w{};
   w.flags = 0;
   size_t off = align256(u * sizeof(int));
   if (S > 1) {
     w.sub_state = off;
-    off += align256(u * dk * dv * sizeof(float));
+    off += align256(u * ss);
     w.sub_ld = off;
     off += align256(u * dk * sizeof(float));
     w.carry = off;
-    off += align256(u * dk * dv * sizeof(float));
+    off += align256(u * ss);
+  }
+  if (R > 0) {
+    w.list = off;
+    off += align256((size_t)(2 + R) * sizeof(int));
+    w.r_state = off;
+    off += align256((size_t)R * ss);
+    w.r_ld = off;
+    off += align256((size_t)R * dk * sizeof(float));
+    w.r_carry = off;
+    off += align256((size_t)R * ss);
   }
   w.total = off;
   return w;
 }
+
+// The schedule a workspace allows: S sub-segments per segment and R re-split slots.
+struct Schedule {
+  int S, R;
+};
+Schedule fastest_schedule(int B, int H, int T, int chunk, int P, const Kernels& k, int max_split) {
+  int S = split_factor(B, H, T, P, chunk, k);
+  if (max_split > 0 && S > max_split) S = max_split;
+  return {S, resplit_slots(B, H, T, P, S, chunk, k)};
+}
 size_t workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int P, const Kernels& k) {
-  return workspace_layout(B, H, P, dk, dv, split_factor(B, H, T, P, chunk, k)).total;
+  const Schedule f = fastest_schedule(B, H, T, chunk, P, k, 0);
+  return workspace_layout(B, H, P, dk, dv, f.S, f.R).total;
 }
 
-// The sub-segments a workspace of `bytes` allows: S halved until its layout fits (a smaller
-// workspace runs fewer sub-segments, or none); 0 if not even one flag per unit fits.
-int fitting_split(int S, int B, int H, int P, int dk, int dv, size_t bytes) {
-  while (S > 1 && workspace_layout(B, H, P, dk, dv, S).total > bytes) S /= 2;
-  return workspace_layout(B, H, P, dk, dv, S).total <= bytes ? S : 0;
+// The fastest schedule a workspace of `bytes` allows: a smaller workspace first gives up the
+// re-split, then halves S and tries the re-split again, down to S = 1 with no re-split (one flag
+// per unit); S = 0 if not even that fits.
+Schedule fitting_schedule(int B, int H, int T, int dk, int dv, int chunk, int P, const Kernels& k, int max_split,
+                          size_t bytes) {
+  for (int S = fastest_schedule(B, H, T, chunk, P, k, max_split).S; S >= 1; S /= 2) {
+    const int R = resplit_slots(B, H, T, P, S, chunk, k);
+    if (workspace_layout(B, H, P, dk, dv, S, R).total <= bytes) return {S, R};
+    if (workspace_layout(B, H, P, dk, dv, S, 0).total <= bytes) return {S, 0};
+  }
+  return {0, 0};
 }
 
 // Shape checks shared by the chunked entry points.
@@ -223,14 +272,14 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
   for (const void* p : ins)
     if (p == o || p == chunk_states || p == workspace)
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
-  int S = split_factor(B, H, T, P, chunk, kern);
-  if (max_split > 0 && S > max_split) S = max_split;
-  if (workspace) S = fitting_split(S, B, H, P, dk, dv, workspace_size);
-  if (!workspace || S == 0)
+  const Schedule sch = workspace ? fitting_schedule(B, H, T, dk, dv, chunk, P, kern, max_split, workspace_size)
+                                 : Schedule{0, 0};
+  const int S = sch.S;
+  if (S == 0)
     return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs at least %zu bytes (one int per unit; "
                 "gla_workspace_size gives the size for the fastest schedule), got %zu", fn,
-                workspace_layout(B, H, P, dk, dv, 1).total, workspace ? workspace_size : (size_t)0);
-  const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
+                workspace_layout(B, H, P, dk, dv, 1, 0).total, workspace ? workspace_size : (size_t)0);
+  const Workspace lay = workspace_layout(B, H, P, dk, dv, S, sch.R);
   char* ws = static_cast<char*>(workspace);
   gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, reinterpret_cast<int*>(ws + lay.flags),
                  B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
@@ -252,6 +301,24 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
   if (kern.fwd) {  // the fast kernel, then the exact one for the units it flagged
     st = launched(fn, kern.fwd(&a, s));
     if (st != GLA_OK) return st;
+    if (sch.R > 0) {
+      // the flagged units' list, the state pass over their pieces and the scan over each unit's
+      // pieces (from the unit's incoming state; with S = 1 its end value is the segment's)
+      int* list = reinterpret_cast<int*>(ws + lay.list);
+      float* r_carry = reinterpret_cast<float*>(ws + lay.r_carry);
+      a.list = list;
+      a.R = sch.R;
+      a.r_init = r_carry;
+      a.r_state = reinterpret_cast<float*>(ws + lay.r_state);
+      a.r_ld = reinterpret_cast<float*>(ws + lay.r_ld);
+      st = launched(fn, gla::launch_resplit_list(a.flags, list, B * H * P * S, sch.R, resplit_xmax(T, P, S, chunk), s));
+      if (st != GLA_OK) return st;
+      st = launched(fn, kern.fwd_state(&a, s));
+      if (st != GLA_OK) return st;
+      st = launched(fn, gla::launch_resplit_scan(list, a.r_state, a.r_ld, a.init, r_carry, S > 1 ? nullptr : seg_state,
+                                                 sch.R, dk, dv, 0, s));
+      if (st != GLA_OK) return st;
+    }
   } else {
     a.flags = nullptr;  // every unit
   }
@@ -331,12 +398,14 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
   for (const void* p : ins)
     if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace)
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
-  const int S = workspace ? fitting_split(split_factor(B, H, T, P, chunk, kern), B, H, P, dk, dv, workspace_size) : 0;
+  const Schedule sch = workspace ? fitting_schedule(B, H, T, dk, dv, chunk, P, kern, 0, workspace_size)
+                                 : Schedule{0, 0};
+  const int S = sch.S;
   if (S == 0)
     return fail(GLA_ERR_INVALID_ARG, "%s: the workspace needs at least %zu bytes (one int per unit; "
                 "gla_workspace_size gives the size for the fastest schedule), got %zu", fn,
-                workspace_layout(B, H, P, dk, dv, 1).total, workspace ? workspace_size : (size_t)0);
-  const Workspace lay = workspace_layout(B, H, P, dk, dv, S);
+                workspace_layout(B, H, P, dk, dv, 1, 0).total, workspace ? workspace_size : (size_t)0);
+  const Workspace lay = workspace_layout(B, H, P, dk, dv, S, sch.R);
   char* ws = static_cast<char*>(workspace);
   gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate,
                  reinterpret_cast<int*>(ws + lay.flags), B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
@@ -358,6 +427,24 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
   if (kern.bwd) {  // the fast kernel, then the exact one for the units it flagged
     st = launched(fn, kern.bwd(&a, s));
     if (st != GLA_OK) return st;
+    if (sch.R > 0) {
+      // the flagged units' list, the state-gradient pass over their pieces and the reverse scan
+      // over each unit's pieces (with S = 1 its end value is the segment's)
+      int* list = reinterpret_cast<int*>(ws + lay.list);
+      float* r_carry = reinterpret_cast<float*>(ws + lay.r_carry);
+      a.list = list;
+      a.R = sch.R;
+      a.r_init = r_carry;
+      a.r_state = reinterpret_cast<float*>(ws + lay.r_state);
+      a.r_ld = reinterpret_cast<float*>(ws + lay.r_ld);
+      st = launched(fn, gla::launch_resplit_list(a.flags, list, B * H * P * S, sch.R, resplit_xmax(T, P, S, chunk), s));
+      if (st != GLA_OK) return st;
+      st = launched(fn, kern.bwd_state(&a, s));
+      if (st != GLA_OK) return st;
+      st = launched(fn, gla::launch_resplit_scan(list, a.r_state, a.r_ld, a.init, r_carry,
+                                                 S > 1 ? nullptr : seg_dstate, sch.R, dk, dv, 1, s));
+      if (st != GLA_OK) return st;
+    }
   } else {
     a.flags = nullptr;  // every unit
   }

@@ -441,11 +441,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sLamE[DK];
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
 
-  const int unit = blockIdx.x;
-  if (unit >= n_units) return;
+  const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
+  if (!up.live || up.X == 1) return;  // a whole re-split unit has no pieces to combine
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ dO = static_cast<const E*>(a.dO);
-  const int NS = a.S, sub = unit % NS, seg = unit / NS;
+  const int NS = up.NS, sub = up.sub, seg = up.seg;
   const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
   const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
@@ -514,14 +514,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
     __syncthreads();
   }
   if (urole) {
-    float* dst = a.sub_state + (long)unit * DK * DV;
+    float* dst = up.st;
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[jb]);
   }
   const int tid = threadIdx.x;
   if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
-    store8(a.sub_ld + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
+    store8(up.ld + 8 * GT::group_of(tid), ldsum);
 }
 
 template <typename E, int C, int DK, int DV>
@@ -538,8 +538,9 @@ template <typename E, int C, int DK, int DV>
 struct BwdStateLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
-    const int n_units = a.BH * a.P * a.S;
-    hipLaunchKernelGGL((bwd_state_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.list ? 0 : a.BH * a.P * a.S;  // the units, or the re-split pieces' slots
+    hipLaunchKernelGGL((bwd_state_kernel<E, C, DK, DV, 8>), dim3(a.list ? a.R : n_units), dim3(8 * 64), 0, s, a,
+                       n_units);
     return hipGetLastError();
   }
 };

@@ -50,6 +50,56 @@ __device__ __forceinline__ int fresh_tid() {
   return x;
 }
 
+// Where a workgroup's tokens lie.  Workgroup i < n_plain is unit i: sub-segment i % S of segment
+// i / S, its arrays (init, sub_state, sub_ld) at index i.  With a.list = {n, X, u_0 .. u_{n-1}},
+// workgroup n_plain + j serves piece j % X of unit u_{j / X} (j / X < n): that unit's tokens cut
+// into X equal pieces, i.e. sub-segment (u % S) X + j % X of its segment cut into S X, its arrays
+// (r_init, r_state, r_ld) at slot j.  With X = 1 the piece is the whole unit, entered from init[u].
+struct UnitPlace {
+  bool live;
+  int unit, seg, sub, NS, X;  // X = 0 for a plain unit
+  const float* init;          // the state (gradient) entering the sub-segment from its segment, or null
+  float *st, *ld;             // the state pass's outputs
+  const float* ldb;           // the summed log-gates of the segment's parts, nld of them, DK apart
+  int nld;
+};
+template <class A>
+__device__ __forceinline__ UnitPlace unit_place(const A& a, int n_plain, int DK, long SS) {
+  const int i = blockIdx.x;
+  UnitPlace u{};
+  if (i < n_plain) {
+    u.live = true;
+    u.unit = i;
+    u.seg = i / a.S;
+    u.sub = i - u.seg * a.S;
+    u.NS = a.S;
+    u.init = a.init ? a.init + (long)i * SS : nullptr;
+    u.st = a.sub_state ? a.sub_state + (long)i * SS : nullptr;
+    u.ld = a.sub_ld ? a.sub_ld + (long)i * DK : nullptr;
+    u.ldb = a.sub_ld ? a.sub_ld + (long)u.seg * a.S * DK : nullptr;
+    u.nld = a.S;
+    return u;
+  }
+  if (!a.list) return u;
+  const int j = i - n_plain, n = a.list[0], X = a.list[1], e = j / X;
+  if (e >= n) return u;
+  const int x = j - e * X;
+  u.live = true;
+  u.unit = a.list[2 + e];
+  u.seg = u.unit / a.S;
+  u.sub = (u.unit - u.seg * a.S) * X + x;
+  u.NS = a.S * X;
+  u.X = X;
+  u.init = X > 1 ? a.r_init + (long)j * SS : a.init ? a.init + (long)u.unit * SS : nullptr;
+  u.st = a.r_state + (long)j * SS;
+  u.ld = a.r_ld + (long)j * DK;
+  // the segment's log decay: from the unit split's parts where there is one (a unit's is exact at
+  // any decay), else from this unit's pieces
+  u.ldb = a.S > 1 ? a.sub_ld + (long)u.seg * a.S * DK : a.r_ld + (long)(j - x) * DK;
+  u.nld = a.S > 1 ? a.S : X;
+  return u;
+}
+
 // --------------------------------------------------------------------------------------------
 // Element loads and stores (4 or 8 consecutive elements <-> float registers)
 // --------------------------------------------------------------------------------------------

@@ -22,8 +22,10 @@
 // (the last line is the exact carry of the fast backward, at sub-block granularity).
 //
 // One workgroup of 8 waves per unit (b, h, segment); with flags non-null only the units whose
-// flag is 1 (set by the fast kernel) run.  These kernels favour simplicity over speed: they serve
-// chunks of 16 tokens in bf16, and units with strongly decaying channels.
+// flag is 1 (set by the fast kernel) run.  With a re-split list, further workgroups serve the
+// pieces of the listed flagged units, each from its true incoming state (unit_place).  These
+// kernels favour simplicity over speed: they serve chunks of 16 tokens in bf16, and units with
+// strongly decaying channels.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 
@@ -152,16 +154,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sRed[NGW][kSB][kSB];  // per-wave partial scores
   __shared__ __attribute__((aligned(16))) float sLamE[DK];            // exp(lam)
 
-  const int unit = blockIdx.x;
-  if (unit >= n_units) return;
-  if (a.flags && a.flags[unit] == 0) return;  // the fast kernel has done this unit
+  const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
+  if (!up.live) return;
+  if (!up.X && a.flags && a.flags[up.unit] == 0) return;  // the fast kernel has done this unit
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
   E* __restrict__ o = static_cast<E*>(a.o);
   E* __restrict__ cst = static_cast<E*>(a.chunk_states);
   const int C = a.chunk, NSB = C / kSB;
-  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments, as in fwd_local_kernel
+  const int unit = up.unit, NS = up.NS, sub = up.sub, seg = up.seg;  // sub-segments, as in fwd_local_kernel
   const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
   const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if (a.init && sub > 0 && vrole)  // the state entering the sub-segment
-        S[jj][kb] = quad_transpose(load4(a.init + (long)unit * DK * DV + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV +
+      if (up.init && sub > 0 && vrole)  // the state entering the sub-segment
+        S[jj][kb] = quad_transpose(load4(up.init + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV +
                                          (w * JPW + jj) * 16 + (n16 & ~3)));
       else
         S[jj][kb] = zero4();
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
     // the end state comes from the scan over the sub-segments; the log decay is their sum
     for (int c = tid; c < DK; c += NW * 64) {
       float sum = 0.f;
-      for (int s2 = 0; s2 < NS; ++s2) sum += a.sub_ld[((long)seg * NS + s2) * DK + c];
+      for (int s2 = 0; s2 < up.nld; ++s2) sum += up.ldb[(long)s2 * DK + c];
       a.seg_logdecay[(long)seg * DK + c] = sum;
     }
   }
@@ -330,9 +332,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   E* const sU = reinterpret_cast<E*>(sUR);                            // U [c][j], after the scores
   float (*const sRed)[kSB][kSB] = reinterpret_cast<float (*)[kSB][kSB]>(sUR);  // per-wave partial scores
 
-  const int unit = blockIdx.x;
-  if (unit >= n_units) return;
-  if (a.flags && a.flags[unit] == 0) return;  // the fast kernel has done this unit
+  const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
+  if (!up.live) return;
+  if (!up.X && a.flags && a.flags[up.unit] == 0) return;  // the fast kernel has done this unit
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   E* __restrict__ dk = static_cast<E*>(a.dk);
   E* __restrict__ dv = static_cast<E*>(a.dv);
   const int C = a.chunk, NSB = C / kSB;
-  const int NS = a.S, sub = unit % NS, seg = unit / NS;  // sub-segments, as in bwd_kernel
+  const int unit = up.unit, NS = up.NS, sub = up.sub, seg = up.seg;  // sub-segments, as in bwd_kernel
   const int L = a.T / a.P, Ls = L / NS, nchunks = Ls / C;
   const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
@@ -353,12 +355,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
 
   f32x4 U[NJB];  // U[jb][i] = U[16w + n16][16jb + 4g4 + i]
   f32x4 cin = zero4();  // rowsum(S_after * U_after) for c = 16w + 4g4 + i
-  if (a.init && sub < NS - 1 && urole) {
+  if (up.init && sub < NS - 1 && urole) {
     // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment), and the
     // carry rowsum(S * U) with S the global state after the sub-segment's last chunk
     const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) U[jb] = load4(a.init + (long)unit * SS + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
+    for (int jb = 0; jb < NJB; ++jb) U[jb] = load4(up.init + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
     f32x4 Se[NJB];
     load_state_rows<E, NJB>(cst + (chunk0 + nchunks - 1) * SS, w, Se);
     float part = 0.f;
@@ -576,8 +578,9 @@ template <typename E, int DK, int DV>
 struct FwdExactLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
-    const int n_units = a.BH * a.P * a.S;
-    hipLaunchKernelGGL((fwd_exact_kernel<E, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.BH * a.P * a.S;  // then the re-split pieces' slots
+    hipLaunchKernelGGL((fwd_exact_kernel<E, DK, DV, 8>), dim3(n_units + (a.list ? a.R : 0)), dim3(8 * 64), 0, s, a,
+                       n_units);
     return hipGetLastError();
   }
 };
@@ -586,8 +589,9 @@ template <typename E, int DK, int DV>
 struct BwdExactLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const BwdArgs& a = *static_cast<const BwdArgs*>(pa);
-    const int n_units = a.BH * a.P * a.S;
-    hipLaunchKernelGGL((bwd_exact_kernel<E, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.BH * a.P * a.S;  // then the re-split pieces' slots
+    hipLaunchKernelGGL((bwd_exact_kernel<E, DK, DV, 8>), dim3(n_units + (a.list ? a.R : 0)), dim3(8 * 64), 0, s, a,
+                       n_units);
     return hipGetLastError();
   }
 };

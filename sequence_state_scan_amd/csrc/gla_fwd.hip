@@ -296,11 +296,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sLamE[DK];
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
 
-  const int unit = blockIdx.x;
-  if (unit >= n_units) return;
+  const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
+  if (!up.live || up.X == 1) return;  // a whole re-split unit has no pieces to combine
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
-  const int S = a.S, sub = unit % S, seg = unit / S;
+  const int S = up.NS, sub = up.sub, seg = up.seg;
   const int L = a.T / a.P, Ls = L / S, nchunks = Ls / C;
   const int bh = seg / a.P, p = seg - bh * a.P;
   const long tok0 = (long)bh * a.T + (long)p * L + (long)sub * Ls;
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
     }
     __syncthreads();
   }
-  float* st = a.sub_state + (long)unit * DK * DV;
+  float* st = up.st;
   const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
   if (w * JPW < NJB) {
 #pragma unroll
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
   }
   const int tid = threadIdx.x;
   if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
-    store8(a.sub_ld + (long)unit * DK + 8 * GT::group_of(tid), ldsum);
+    store8(up.ld + 8 * GT::group_of(tid), ldsum);
 }
 
 // Correction of segment p's local results with its incoming global state S_in[p]:
@@ -615,8 +615,9 @@ template <typename E, int C, int DK, int DV>
 struct FwdStateLauncher {
   static hipError_t run(const void* pa, hipStream_t s) {
     const FwdArgs& a = *static_cast<const FwdArgs*>(pa);
-    const int n_units = a.BH * a.P * a.S;
-    hipLaunchKernelGGL((fwd_state_kernel<E, C, DK, DV, 8>), dim3(n_units), dim3(8 * 64), 0, s, a, n_units);
+    const int n_units = a.list ? 0 : a.BH * a.P * a.S;  // the units, or the re-split pieces' slots
+    hipLaunchKernelGGL((fwd_state_kernel<E, C, DK, DV, 8>), dim3(a.list ? a.R : n_units), dim3(8 * 64), 0, s, a,
+                       n_units);
     return hipGetLastError();
   }
 };

@@ -169,13 +169,13 @@ def workspace_size(which: int, B: int, H: int, T: int, dk: int, dv: int, chunk: 
 def flags_workspace_size(B: int, H: int, P: int) -> int:
     """The smallest workspace gla_chunk_fwd / gla_chunk_bwd accept (include/gla.h,
     gla_workspace_size): one int per unit (b, h, segment), rounded up to 256 bytes.  With it a call
-    cuts no segment into sub-segments."""
+    cuts no segment into sub-segments and runs the units it flags whole (no re-split)."""
     return (B * H * P * 4 + 255) // 256 * 256
 
 
 def _workspace(ws, which, B, H, T, dk, dv, chunk, P, dtype, device):
     """The caller's workspace, or one of the size for the fastest schedule.  A smaller one is the
-    library's to accept (fewer sub-segments) or reject, before any HIP call."""
+    library's to accept (no re-split, fewer sub-segments) or reject, before any HIP call."""
     if ws is None:
         ws = torch.empty(workspace_size(which, B, H, T, dk, dv, chunk, P, dtype), dtype=torch.uint8, device=device)
     if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():

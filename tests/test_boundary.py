@@ -140,7 +140,10 @@ def _expected_workspace(B, H, T, dk, dv, C, P, fast=True):
     """The workspace rule of include/gla.h, written out: with fewer than 256 units (b, h, segment)
     each segment is cut into S sub-segments (S a power of two, at least 2 chunks each) until
     B*H*P*S reaches 256; then one int flag per unit and sub-segment, and with S > 1 three float32
-    buffers (sub-segment states, their log decays, the scanned states), each rounded up to 256."""
+    buffers (sub-segment states, their log decays, the scanned states); then, where a unit (b, h,
+    segment, sub-segment) splits into pieces of at least 2 chunks, the re-split of flagged units:
+    2 + R ints and the same three buffers for R = min(256, units * xmax) slots.  Each region is
+    rounded up to 256 bytes."""
     units, nch, S = B * H * P, T // P // C, 1
     while fast and units * S < 256 and nch % (2 * S) == 0 and nch // (2 * S) >= 2:
         S *= 2
@@ -149,6 +152,12 @@ def _expected_workspace(B, H, T, dk, dv, C, P, fast=True):
     total = up(4 * u)
     if S > 1:
         total += up(4 * u * dk * dv) + up(4 * u * dk) + up(4 * u * dk * dv)
+    nch_u, xmax = nch // S, 1
+    while nch_u % (2 * xmax) == 0 and nch_u // (2 * xmax) >= 2:
+        xmax *= 2
+    R = min(256, u * xmax) if fast and xmax >= 2 else 0
+    if R:
+        total += up(4 * (2 + R)) + up(4 * R * dk * dv) + up(4 * R * dk) + up(4 * R * dk * dv)
     return total
 
 
@@ -159,8 +168,12 @@ def test_workspace_size(lib):
             n = lib.gla_workspace_size(which, B, H, T, 128, 256, C, P, gla.GLA_BF16)
             assert n == _expected_workspace(B, H, T, 128, 256, C, P, fast=C != 16), (B, H, T, P, C)
             assert n == gla.workspace_size(which, B, H, T, 128, 256, C, P, torch.bfloat16)
-    # the headline workload fills the chip unsplit: flags only
-    assert lib.gla_workspace_size(gla.GLA_BWD, 1, 4, 1 << 20, 128, 256, 64, 64, gla.GLA_BF16) == 1024
+    # the headline workload fills the chip unsplit: flags, then the re-split's 256 slots
+    state = 128 * 256 * 4
+    assert lib.gla_workspace_size(gla.GLA_BWD, 1, 4, 1 << 20, 128, 256, 64, 64, gla.GLA_BF16) == \
+        1024 + 1280 + 256 * (2 * state + 128 * 4)
+    # units of 2 chunks do not split further: no re-split region
+    assert lib.gla_workspace_size(gla.GLA_FWD, 1, 4, 64 * 128, 128, 256, 64, 64, gla.GLA_BF16) == 1024
     assert lib.gla_workspace_size(gla.GLA_FWD, 1, 1, 250, 64, 64, 64, 4, gla.GLA_BF16) == 0  # T % P
     assert lib.gla_workspace_size(7, 1, 1, 256, 64, 64, 64, 4, gla.GLA_BF16) == 0            # unknown call
     assert lib.gla_workspace_size(gla.GLA_BWD, 1, 1, 256, 48, 64, 64, 4, gla.GLA_BF16) == 0  # no kernel

@@ -380,11 +380,18 @@ def test_multi_stream_schedule(n_streams):
           ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL["bf16"], "%d streams" % n_streams)
 
 
-def _layout_bytes(units, dk, dv, S):
-    """The workspace rule of include/gla.h (gla_workspace_size) for S sub-segments per segment."""
+def _layout(units, dk, dv, S, R=0):
+    """The workspace rule of include/gla.h (gla_workspace_size) for S sub-segments per segment and R
+    re-split slots: the byte offset of the re-split's list, and the total."""
     a = lambda n: (n + 255) // 256 * 256  # noqa: E731
     u = units * S
-    return a(4 * u) + (a(4 * u * dk * dv) + a(4 * u * dk) + a(4 * u * dk * dv) if S > 1 else 0)
+    off = a(4 * u) + (a(4 * u * dk * dv) + a(4 * u * dk) + a(4 * u * dk * dv) if S > 1 else 0)
+    total = off + (a(4 * (2 + R)) + a(4 * R * dk * dv) + a(4 * R * dk) + a(4 * R * dk * dv) if R else 0)
+    return off, total
+
+
+def _layout_bytes(units, dk, dv, S):
+    return _layout(units, dk, dv, S)[1]
 
 
 def test_small_workspace_runs_fewer_sub_segments():
@@ -417,6 +424,60 @@ def test_small_workspace_runs_fewer_sub_segments():
     with pytest.raises(gla.GLAError):  # below the flags
         gla.gla_chunk_fwd(x["q"], x["k"], x["v"], x["g"], chunk, P,
                           workspace=torch.empty(255, dtype=torch.uint8, device="cuda"))
+
+
+# (dtype, B, H, T, dk, dv, chunk, P, gate, strong units, S, R, n, X): strong units are the units
+# (b, h, segment, sub-segment) that get a strongly decaying stretch (None: the gate decays strongly
+# everywhere); S the sub-segments per segment, R the re-split slots; n units listed, X pieces each.
+RESPLIT_CASES = [
+    # 256 units of 16 chunks: two flagged, 8 pieces each
+    ("bf16", 1, 4, 65536, 64, 64, 64, 64, "logsigmoid16", [3, 200], 1, 256, 2, 8),
+    # forty flagged: 4 pieces each
+    ("bf16", 1, 4, 65536, 32, 32, 64, 64, "logsigmoid16", list(range(0, 240, 6)), 1, 256, 40, 4),
+    # 512 units, all flagged: the first 256 listed whole, the rest in the plain exact pass
+    ("bf16", 2, 4, 32768, 32, 32, 64, 64, "strong5", None, 1, 256, 256, 1),
+    # 8 segments cut into 32 sub-segments of 8 chunks; one sub-segment flagged, 4 pieces
+    ("bf16", 1, 2, 65536, 64, 64, 64, 4, "logsigmoid16", [77], 32, 256, 1, 4),
+    # every sub-segment flagged: listed whole, each from the sub-segment split's incoming state
+    ("bf16", 1, 2, 65536, 64, 64, 64, 4, "strong5", None, 32, 256, 256, 1),
+    ("f32", 1, 4, 32768, 32, 32, 32, 64, "logsigmoid16", [5, 130, 131], 1, 256, 3, 8),
+]
+
+
+@pytest.mark.parametrize("case", RESPLIT_CASES, ids=lambda c: "%s-T%d-P%d-%s-n%d" % (c[0], c[3], c[7], c[8], c[12]))
+def test_flagged_units_are_re_split(case):
+    """Units the fast kernels flag are cut into pieces and redone from each piece's true incoming
+    state: the whole path matches the oracle, the workspace's list names the flagged units and the
+    piece count the rule gives, and a flags-only workspace (no re-split) agrees to rounding."""
+    dtype, B, H, T, dk, dv, chunk, P, gate, strong, S, R, n, X = case
+    d = inputs.generate(B, H, T, dk, dv, dtype, 29, True, gate)
+    units = B * H * P * S
+    Ls = T // P // S
+    if strong is not None:
+        g = d["g"].clone()
+        for u in strong:  # a stretch of 48 tokens decaying by e^-3 per token in every other channel
+            b, rest = divmod(u, H * P * S)
+            h, rest = divmod(rest, P * S)
+            t0 = rest * Ls + Ls // 2 - 24
+            g[b, h, t0:t0 + 48, ::2] = -3.0
+        d["g"] = g
+    x = dev(d)
+    full = gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, chunk, P, x["q"].dtype)
+    list_at, total = _layout(B * H * P, dk, dv, S, R)
+    assert full == total
+    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    say("re-split case", case[:9], "units", units)
+    gpu = gpu_pipeline(x, chunk, P, 2, True, ws=ws)
+    lst = ws[list_at:list_at + 4 * (2 + n)].view(torch.int32).cpu().numpy()  # the backward's list
+    expect = list(range(n)) if strong is None else sorted(strong)
+    assert lst[0] == n and lst[1] == X and list(lst[2:]) == expect, (lst[:2], lst[2:12])
+    ref = oracle_pipeline(d, chunk, P, True)
+    check(gpu, ref, FWD_KEYS + BWD_KEYS, TOL[dtype], "re-split %s" % (case[:9],))
+    flags_only = torch.empty(gla.flags_workspace_size(B, H, P) if S == 1 else _layout_bytes(B * H * P, dk, dv, S),
+                             dtype=torch.uint8, device="cuda")
+    plain = gpu_pipeline(x, chunk, P, 2, True, ws=flags_only)
+    for k_ in ("o", "dq", "dk", "dv", "dg", "S_local", "D_local"):
+        assert maxrel(gpu[k_], plain[k_]) < TOL[dtype] / 2, k_
 
 
 def test_state_carry_across_calls():
