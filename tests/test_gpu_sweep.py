@@ -8,13 +8,19 @@ Each case draws together:
 
 It runs 40 cases by default.  Set GLA_SWEEP to run more (GLA_SWEEP=2000 takes about four minutes
 on one MI355X), and GLA_SWEEP_SEED to draw another sample.
+
+A second sweep (test_random_strong_windows, GLA_SWEEP_WINDOWS cases, 10 by default) puts strongly
+decaying stretches at random places into shapes with at least 256 units of 4 or more chunks, where
+the flagged units are cut into pieces (the re-split) or, beyond the slots, run whole.
 """
 import os
 
 import numpy as np
 import pytest
+import torch
 
-from test_gpu_parity import SUPPORTED, run_case
+from sequence_state_scan_amd import gla, inputs
+from test_gpu_parity import SUPPORTED, TOL, FWD_KEYS, BWD_KEYS, check, dev, gpu_pipeline, oracle_pipeline, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -41,3 +47,52 @@ def _cases(n, seed):
 def test_random_configuration(case):
     B, H, T, dk, dv, chunk, P, K, dtype, gate, seed, carry = case
     run_case(B, H, T, dk, dv, chunk, P, K, dtype, bwd=True, gate=gate, seed=seed, carry=carry)
+
+
+def _window_cases(n, seed):
+    """Shapes with at least 256 units of 4 to 16 chunks (so flagged units are re-split), and 1 to 12
+    strongly decaying stretches at random places: (b, h, first token, length, channel step, g)."""
+    rng = np.random.default_rng(seed)
+    fast = [c for c in SUPPORTED if c[3] != 16 or c[0] == "f32"]
+    out = []
+    while len(out) < n:
+        dtype, dk, dv, chunk = fast[int(rng.integers(len(fast)))]
+        if dk * dv > 64 * 128:
+            continue
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+        P = int(-(-256 // (B * H)))
+        P += int(rng.integers(0, 2)) * P  # up to twice as many units as slots
+        per_seg = (4, 8, 16)[int(rng.integers(3))]
+        T = P * per_seg * chunk
+        if B * H * T > 400_000:
+            continue
+        wins = []
+        for _ in range(int(rng.integers(1, 13))):
+            ln = int(rng.integers(8, 81))
+            wins.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(T - ln)), ln,
+                         int(rng.integers(1, 4)), -float(rng.uniform(2.0, 6.0))))
+        out.append((dtype, B, H, T, dk, dv, chunk, P, wins, int(rng.integers(1000)), bool(rng.integers(2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _window_cases(int(os.environ.get("GLA_SWEEP_WINDOWS", "10")), SEED + 1))
+def test_random_strong_windows(case):
+    """Strongly decaying stretches at random places: the units they touch are flagged and re-split
+    (or, past the slots, run whole), the rest take the fast kernels; fwd+bwd against the oracle."""
+    dtype, B, H, T, dk, dv, chunk, P, wins, seed, carry = case
+    print("windows case", dtype, B, H, T, dk, dv, chunk, P, len(wins), flush=True)
+    d = inputs.generate(B, H, T, dk, dv, dtype, seed, True, "logsigmoid16")
+    g = d["g"].clone()
+    for b, h, t0, ln, step, val in wins:
+        g[b, h, t0:t0 + ln, ::step] = val
+    d["g"] = g
+    h0 = dhT = None
+    if carry:
+        rng = np.random.default_rng(seed + 100)
+        h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+        dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    gpu = gpu_pipeline(dev(d), chunk, P, 1, True, None if h0 is None else h0.cuda(),
+                       None if dhT is None else dhT.cuda())
+    ref = oracle_pipeline(d, chunk, P, True, None if h0 is None else h0.numpy(), None if dhT is None else dhT.numpy())
+    check(gpu, ref, FWD_KEYS + BWD_KEYS, TOL[dtype], "windows %s B%d H%d T%d dk%d dv%d C%d P%d" %
+          (dtype, B, H, T, dk, dv, chunk, P))
