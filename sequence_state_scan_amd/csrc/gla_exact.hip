@@ -35,6 +35,26 @@ namespace {
 
 constexpr int kMaxChunk = 64;
 constexpr int kSB = 16;  // tokens per sub-block
+constexpr float kLog2e = 1.44269504088896341f;
+
+// exp(b_t - b_s) or exp(b_s - b_t), whichever exponent is not positive, from b in base 2 (b2 = b log2 e):
+// b does not rise along a sub-block (the gates are <= 0), so this is exp(b_t - b_s) for s <= t and
+// exp(b_s - b_t) for s >= t, up to the rounding of the prefix sums.  One v_exp_f32 with a -|x|
+// operand modifier.
+__device__ __forceinline__ float exp_nonpos(float b2t, float b2s) { return __builtin_amdgcn_exp2f(-fabsf(b2t - b2s)); }
+
+// b in base 2.  The values are hidden from the optimiser, so that b2_t - b2_s stays one subtraction
+// (with the broadcast of b2_s folded into it) rather than a multiply-add that recomputes b2_t.
+__device__ __forceinline__ f32x4 base2(f32x4 b) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = b[e] * kLog2e;
+    asm volatile("" : "+v"(v));
+    r[e] = v;
+  }
+  return r;
+}
 
 // Gate item of a 16-token sub-block: thread (row R = tid / 16, lane t = tid % 16) holds token t's
 // q, k and g for the channels 4R .. 4R + 3; rows R < DK / 4 take part (others hold zeros).
@@ -69,15 +89,13 @@ struct SubGate {
 // part[s] = sum over the thread's 4 channels of q_t k_s exp(b_t - b_s) for s <= t, 0 for s > t.
 template <typename E>
 __device__ __forceinline__ void diag_parts(const SubGate<E>& x, int t, float (&part)[16]) {
+  const f32x4 b2 = base2(x.b);
   static_for<0, 16>([&](auto S) {
     constexpr int s = decltype(S)::value;
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ks = row_bcast<s>(x.k[e]), bs = row_bcast<s>(x.b[e]);
-      acc += x.q[e] * ks * __expf(x.b[e] - bs);
-    }
-    part[s] = s <= t ? acc : 0.f;  // a select: the discarded exponent may be positive
+    for (int e = 0; e < 4; ++e) acc += x.q[e] * (row_bcast<s>(x.k[e]) * exp_nonpos(b2[e], row_bcast<s>(b2[e])));
+    part[s] = s <= t ? acc : 0.f;  // the s > t terms are dropped
     __builtin_amdgcn_sched_barrier(0);  // one s at a time: bounded register use
   });
 }
@@ -448,8 +466,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       f32x4 dqd = zero4(), dkd = zero4();
       if (urole) {
         // one exponential per (t, s, channel) serves the scores, dq and dk: exp(b_t - b_s) for s <= t
-        // (scores and dq), exp(b_s - b_t) for s >= t (dk); -(b_t - b_s) is b_s - b_t exactly.  (The
-        // scores' sums run as in diag_parts; their s > t terms are dropped by the select below.)
+        // (scores and dq), exp(b_s - b_t) for s >= t (dk).  dA is masked (zero for s > t), so
+        // dA[t][s] keeps dq to s <= t and dA[s][t] keeps dk to s >= t; the scores' s > t terms are
+        // dropped by the select below.
+        const f32x4 b2 = base2(x.b);
         float part[16];
         static_for<0, 16>([&](auto S) {
           constexpr int s = decltype(S)::value;
@@ -457,16 +477,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
           float acc = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float ks = row_bcast<s>(x.k[e]), qs = row_bcast<s>(x.q[e]), bs = row_bcast<s>(x.b[e]);
-            const float d = x.b[e] - bs;
-            const float ex = __expf(s <= t ? d : -d);  // never a positive exponent
-            const float et = s <= t ? ex : 0.f;  // token s up to token t
-            const float es = s >= t ? ex : 0.f;  // token t up to token s
-            dqd[e] += dats * ks * et;
-            dkd[e] += dast * qs * es;
-            acc += x.q[e] * ks * ex;
+            const float ex = exp_nonpos(b2[e], row_bcast<s>(b2[e]));
+            const float kx = row_bcast<s>(x.k[e]) * ex;
+            dqd[e] += dats * kx;
+            acc += x.q[e] * kx;
+            dkd[e] += dast * row_bcast<s>(x.q[e]) * ex;
           }
-          part[s] = s <= t ? acc : 0.f;  // a select: the discarded exponent may be positive
+          part[s] = s <= t ? acc : 0.f;
           __builtin_amdgcn_sched_barrier(0);  // one s at a time: bounded register use
         });
         const f32x4 r = reduce_scores(part);
