@@ -7,12 +7,15 @@ Inputs are drawn once (seeded, synthetic) and stay resident in HBM; every output
 buffer is allocated before the timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--gate VARIANT]
-                  [--no-cpu-baseline] [--no-extras] [--copy-calibration] [--compare-orderings]
+                  [--strong-windows N] [--no-cpu-baseline] [--no-extras] [--copy-calibration]
+                  [--compare-orderings]
 
 Besides the headline line, the default run adds (under "extras"): the same step with g = 0 (no
-decay, so the corrections never stop early: the full second pass), and the other fwd+bwd and
-forward workloads, each timed over 50 iterations with a 512 MiB scrub written between them
-(untimed) so that no input stays in the 256 MB last-level cache.
+decay, so the corrections never stop early: the full second pass); the same step with 1, 8 and 32
+strongly decaying 64-token stretches in as many segments (those segments take the exact kernels,
+cut into pieces); the two-stream schedule; and the other fwd+bwd and forward workloads, each timed
+over 50 iterations with a 512 MiB scrub written between them (untimed) so that no input stays in
+the 256 MB last-level cache.  --strong-windows N puts N such stretches into the timed step itself.
 
 --compare-orderings also times, on the same inputs, the two baseline orderings of the pages
 rendered on one GPU, and adds them under "orderings": the all-gather scan (LASP2's pattern,
@@ -363,6 +366,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--gate", default="logsigmoid16")
+    ap.add_argument("--strong-windows", type=int, default=0,
+                    help="add this many strongly decaying 64-token stretches to the gates, in as many segments")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step (no g = 0 step, no other workloads)")
@@ -394,6 +399,8 @@ def main():
 
     t = time.time()
     d = inputs.generate_workload(w, gate=args.gate, bwd=True)
+    if args.strong_windows:
+        d["g"] = inputs.add_strong_windows(d["g"], w.P, args.strong_windows)
     x = {n: v.to(dev) for n, v in d.items()}
     del d
     log("inputs %s drawn and uploaded in %.1fs" % (w.name, time.time() - t))
@@ -459,6 +466,18 @@ def main():
             "gate": "zero", "ms_per_step": round(ms0, 4), "tokens_per_s": round(tokens / (ms0 / 1e3), 1),
             "hbm_frac": round(step_bytes / (ms0 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0.items()}}}
+        if args.strong_windows == 0 and args.gate == "logsigmoid16":
+            # the same step with a few strongly decaying 64-token stretches: the segments they touch
+            # are flagged by the fast kernels and redone, cut into pieces, by the exact kernels
+            extras["strong_windows_steps"] = {}
+            for n_w in (1, 8, 32):
+                xw = dict(x, g=inputs.add_strong_windows(x["g"], P, n_w))
+                msw, pcw, _ = time_steps(torch, path_calls(gla, w, xw, buf), 10, 3, stream)
+                del xw
+                log("%d strong windows: %.4f ms per step" % (n_w, msw))
+                extras["strong_windows_steps"][str(n_w)] = {
+                    "ms_per_step": round(msw, 4), "tokens_per_s": round(tokens / (msw / 1e3), 1),
+                    "per_call_ms": {k_: round(v_, 4) for k_, v_ in pcw.items()}}
         if args.streams == 1:
             # the same step with the heads split over two streams (the scans and corrections of one
             # half can run beside the local passes of the other)

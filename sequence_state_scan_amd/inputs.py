@@ -206,6 +206,25 @@ def generate_workload(w: Workload, seed: int = 0, gate: str = "logsigmoid16", bw
     return generate(w.B, w.H, w.T, w.dk, w.dv, w.dtype, seed, w.bwd if bwd is None else bwd, gate)
 
 
+def add_strong_windows(g: torch.Tensor, P: int, n: int, length: int = 64, value: float = -3.0) -> torch.Tensor:
+    """A copy of the log-gates g [B, H, T, dk] with n strongly decaying stretches: `length` tokens of
+    g = `value` in every channel, in the middle of n of the B*H*P segments spread evenly over them
+    (segment i * (B*H*P // n) for i < n, counted over b, h, then segment).  A stretch like this
+    sends its segment's chunks past the fast kernels' decay bound."""
+    B, H, T, _ = g.shape
+    units, L = B * H * P, T // P
+    if not 0 <= n <= units or length > L:
+        raise ValueError("n must be in [0, B*H*P] and length at most the segment length")
+    out = g.clone()
+    for i in range(n):
+        u = i * (units // n)
+        b, r = divmod(u, H * P)
+        h, p = divmod(r, P)
+        t0 = p * L + (L - length) // 2
+        out[b, h, t0:t0 + length] = value
+    return out
+
+
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a (bf16 or fp32) tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float32).numpy().astype(np.float64)

@@ -1,5 +1,6 @@
 """The seeded input generator: reproducible, correctly distributed, bf16 rounding is RNE."""
 import numpy as np
+import pytest
 import torch
 
 from sequence_state_scan_amd import inputs
@@ -81,3 +82,19 @@ def test_head_slice_regenerates_alone():
     one = inputs.generate_head(2, 3, 9000, 16, 16, 1, 2, "bf16", seed=7, bwd=True)
     for n in full:
         assert torch.equal(full[n][1:2, 2:3], one[n]), n
+
+
+def test_strong_windows_land_in_the_middle_of_evenly_spread_segments():
+    g = inputs.generate(2, 3, 4 * 256, 8, 8, "bf16", 1, False, "logsigmoid16")["g"]
+    P, L = 4, 256
+    out = inputs.add_strong_windows(g, P, 5, length=64, value=-3.0)
+    changed = (out != g).any(dim=-1)  # [B, H, T]
+    units = sorted({(b * 3 + h) * P + t // L for b, h, t in changed.nonzero().tolist()})
+    assert units == [0, 4, 8, 12, 16]  # i * (24 // 5)
+    b, h, p = 0, 1, 0  # unit 4
+    seg = out[b, h, p * L:(p + 1) * L]
+    assert bool((seg[96:160] == -3.0).all()) and bool((seg[:96] == g[b, h, :96]).all())
+    assert bool((out[1, 2] == g[1, 2]).all())  # untouched sequences stay
+    assert torch.equal(inputs.add_strong_windows(g, P, 0), g)
+    with pytest.raises(ValueError):
+        inputs.add_strong_windows(g, P, 25)
