@@ -302,21 +302,20 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
     st = launched(fn, kern.fwd(&a, s));
     if (st != GLA_OK) return st;
     if (sch.R > 0) {
-      // the flagged units' list, the state pass over their pieces and the scan over each unit's
-      // pieces (from the unit's incoming state; with S = 1 its end value is the segment's)
+      // the state pass over the flagged units' pieces (it lists them) and the scan over each
+      // unit's pieces (from the unit's incoming state; with S = 1 its end value is the segment's)
       int* list = reinterpret_cast<int*>(ws + lay.list);
       float* r_carry = reinterpret_cast<float*>(ws + lay.r_carry);
       a.list = list;
       a.R = sch.R;
+      a.xmax = resplit_xmax(T, P, S, chunk);
       a.r_init = r_carry;
       a.r_state = reinterpret_cast<float*>(ws + lay.r_state);
       a.r_ld = reinterpret_cast<float*>(ws + lay.r_ld);
-      st = launched(fn, gla::launch_resplit_list(a.flags, list, B * H * P * S, sch.R, resplit_xmax(T, P, S, chunk), s));
-      if (st != GLA_OK) return st;
       st = launched(fn, kern.fwd_state(&a, s));
       if (st != GLA_OK) return st;
-      st = launched(fn, gla::launch_resplit_scan(list, a.r_state, a.r_ld, a.init, r_carry, S > 1 ? nullptr : seg_state,
-                                                 sch.R, dk, dv, 0, s));
+      st = launched(fn, gla::launch_resplit_scan(list, a.flags, a.r_state, a.r_ld, a.init, r_carry,
+                                                 S > 1 ? nullptr : seg_state, sch.R, dk, dv, 0, s));
       if (st != GLA_OK) return st;
     }
   } else {
@@ -428,20 +427,19 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
     st = launched(fn, kern.bwd(&a, s));
     if (st != GLA_OK) return st;
     if (sch.R > 0) {
-      // the flagged units' list, the state-gradient pass over their pieces and the reverse scan
-      // over each unit's pieces (with S = 1 its end value is the segment's)
+      // the state-gradient pass over the flagged units' pieces (it lists them) and the reverse
+      // scan over each unit's pieces (with S = 1 its end value is the segment's)
       int* list = reinterpret_cast<int*>(ws + lay.list);
       float* r_carry = reinterpret_cast<float*>(ws + lay.r_carry);
       a.list = list;
       a.R = sch.R;
+      a.xmax = resplit_xmax(T, P, S, chunk);
       a.r_init = r_carry;
       a.r_state = reinterpret_cast<float*>(ws + lay.r_state);
       a.r_ld = reinterpret_cast<float*>(ws + lay.r_ld);
-      st = launched(fn, gla::launch_resplit_list(a.flags, list, B * H * P * S, sch.R, resplit_xmax(T, P, S, chunk), s));
-      if (st != GLA_OK) return st;
       st = launched(fn, kern.bwd_state(&a, s));
       if (st != GLA_OK) return st;
-      st = launched(fn, gla::launch_resplit_scan(list, a.r_state, a.r_ld, a.init, r_carry,
+      st = launched(fn, gla::launch_resplit_scan(list, a.flags, a.r_state, a.r_ld, a.init, r_carry,
                                                  S > 1 ? nullptr : seg_dstate, sch.R, dk, dv, 1, s));
       if (st != GLA_OK) return st;
     }

@@ -51,7 +51,8 @@ __device__ __forceinline__ int fresh_tid() {
 }
 
 // Where a workgroup's tokens lie.  Workgroup i < n_plain is unit i: sub-segment i % S of segment
-// i / S, its arrays (init, sub_state, sub_ld) at index i.  With a.list = {n, X, u_0 .. u_{n-1}},
+// i / S, its arrays (init, sub_state, sub_ld) at index i.  With a.list = {n, X, u_0 .. u_{n-1}}
+// (written by the state pass over the pieces, resplit_derive),
 // workgroup n_plain + j serves piece j % X of unit u_{j / X} (j / X < n): that unit's tokens cut
 // into X equal pieces, i.e. sub-segment (u % S) X + j % X of its segment cut into S X, its arrays
 // (r_init, r_state, r_ld) at slot j.  With X = 1 the piece is the whole unit, entered from init[u].
@@ -63,6 +64,26 @@ struct UnitPlace {
   const float* ldb;           // the summed log-gates of the segment's parts, nld of them, DK apart
   int nld;
 };
+// Piece j % X of unit `unit`, the listed unit of entry j / X (see unit_place).
+template <class A>
+__device__ __forceinline__ UnitPlace list_place(const A& a, int j, int X, int unit, int DK, long SS) {
+  UnitPlace u{};
+  const int x = j % X;
+  u.live = true;
+  u.unit = unit;
+  u.seg = unit / a.S;
+  u.sub = (unit - u.seg * a.S) * X + x;
+  u.NS = a.S * X;
+  u.X = X;
+  u.init = X > 1 ? a.r_init + (long)j * SS : a.init ? a.init + (long)unit * SS : nullptr;
+  u.st = a.r_state + (long)j * SS;
+  u.ld = a.r_ld + (long)j * DK;
+  // the segment's log decay: from the unit split's parts where there is one (a unit's is exact at
+  // any decay), else from this unit's pieces
+  u.ldb = a.S > 1 ? a.sub_ld + (long)u.seg * a.S * DK : a.r_ld + (long)(j - x) * DK;
+  u.nld = a.S > 1 ? a.S : X;
+  return u;
+}
 template <class A>
 __device__ __forceinline__ UnitPlace unit_place(const A& a, int n_plain, int DK, long SS) {
   const int i = blockIdx.x;
@@ -83,21 +104,67 @@ __device__ __forceinline__ UnitPlace unit_place(const A& a, int n_plain, int DK,
   if (!a.list) return u;
   const int j = i - n_plain, n = a.list[0], X = a.list[1], e = j / X;
   if (e >= n) return u;
-  const int x = j - e * X;
-  u.live = true;
-  u.unit = a.list[2 + e];
-  u.seg = u.unit / a.S;
-  u.sub = (u.unit - u.seg * a.S) * X + x;
-  u.NS = a.S * X;
-  u.X = X;
-  u.init = X > 1 ? a.r_init + (long)j * SS : a.init ? a.init + (long)u.unit * SS : nullptr;
-  u.st = a.r_state + (long)j * SS;
-  u.ld = a.r_ld + (long)j * DK;
-  // the segment's log decay: from the unit split's parts where there is one (a unit's is exact at
-  // any decay), else from this unit's pieces
-  u.ldb = a.S > 1 ? a.sub_ld + (long)u.seg * a.S * DK : a.r_ld + (long)(j - x) * DK;
-  u.nld = a.S > 1 ? a.S : X;
-  return u;
+  return list_place(a, j, X, a.list[2 + e], DK, SS);
+}
+
+// The re-split's list, derived from the flags of n_units units by every workgroup of the state pass
+// over the pieces (each gets the same): n = min(flagged, R) listed units, the first flagged ones in
+// unit order; X = the largest power of 2 <= xmax with n X <= R.  Returns the unit of entry
+// slot / X (-1 if slot / X >= n) and sets n and X.  With list non-null it also writes
+// list = {n, X, u_0 .. u_{n-1}}.  Every thread of the workgroup calls it (it synchronises the
+// workgroup); red: NT / 64 ints of LDS.
+template <int NT>
+__device__ int resplit_derive(const int* __restrict__ flags, int n_units, int R, int xmax, int slot, int* list, int* red,
+                              int& n_out, int& X_out) {
+  constexpr int NWV = NT / 64;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  int c = 0;
+  for (int u = threadIdx.x; u < n_units; u += NT) c += flags[u] != 0;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) red[wv] = c;
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < NWV; ++w) total += red[w];
+  __syncthreads();
+  const int n = min(total, R);
+  int X = xmax;
+  while (X > 1 && n * X > R) X >>= 1;
+  const int want = slot / X;
+  // each flagged unit's rank: the flagged units of the blocks of NT before its own, of the waves
+  // before its own, and of the lanes before it
+  int found = -1, base = 0;
+  for (int u0 = 0; u0 < n_units && base < n; u0 += NT) {
+    const int u = u0 + threadIdx.x;
+    const bool f = u < n_units && flags[u] != 0;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0) red[wv] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < NWV; ++w) {
+      before += w < wv ? red[w] : 0;
+      tot += red[w];
+    }
+    __syncthreads();
+    const int rank = base + before + __popcll(m & ((1ull << lane) - 1ull));
+    if (f && rank < n) {
+      if (list) list[2 + rank] = u;
+      if (rank == want) found = u;
+    }
+    base += tot;
+  }
+  if (threadIdx.x == 0) red[0] = -1;
+  __syncthreads();
+  if (found >= 0) red[0] = found;
+  __syncthreads();
+  const int unit = red[0];
+  __syncthreads();
+  if (list && threadIdx.x == 0) {
+    list[0] = n;
+    list[1] = X;
+  }
+  n_out = n;
+  X_out = X;
+  return want < n ? unit : -1;
 }
 
 // --------------------------------------------------------------------------------------------

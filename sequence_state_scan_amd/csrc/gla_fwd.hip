@@ -296,7 +296,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sLamE[DK];
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
 
-  const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
+  __shared__ int sList[NT / 64];
+  UnitPlace up;
+  if (a.list) {  // the re-split: list the flagged units (workgroup 0 writes the list), then this piece
+    int n, X;
+    const int u = resplit_derive<NT>(a.flags, a.BH * a.P * a.S, a.R, a.xmax, blockIdx.x, blockIdx.x == 0 ? a.list : nullptr,
+                                     sList, n, X);
+    up = u >= 0 ? list_place(a, blockIdx.x, X, u, DK, (long)DK * DV) : UnitPlace{};
+  } else {
+    up = unit_place(a, n_units, DK, (long)DK * DV);
+  }
   if (!up.live || up.X == 1) return;  // a whole re-split unit has no pieces to combine
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);

@@ -26,10 +26,11 @@ struct FwdArgs {  // gla_chunk_fwd
   const float* init;
   float *sub_state, *sub_ld;
   // Re-split of the units the fast kernel flagged (list non-null; see unit_place): R slots, one
-  // workgroup each, over the listed units' pieces.  r_init: [R][Dk][Dv] state entering each piece,
-  // counted from its segment's start; r_state / r_ld: the state pass's outputs per piece.
-  const int* list;
-  int R;
+  // workgroup each, over the listed units' pieces (at most xmax per unit).  r_init: [R][Dk][Dv]
+  // state entering each piece, counted from its segment's start; r_state / r_ld: the state pass's
+  // outputs per piece.  The state pass over the pieces writes the list (resplit_derive).
+  int* list;
+  int R, xmax;
   const float* r_init;
   float *r_state, *r_ld;
 };
@@ -53,8 +54,8 @@ struct BwdArgs {  // gla_chunk_bwd
   float *sub_state, *sub_ld;
   // Re-split of flagged units as in FwdArgs; r_init: gradient w.r.t. the state leaving each piece
   // from the rest of its segment.
-  const int* list;
-  int R;
+  int* list;
+  int R, xmax;
   const float* r_init;
   float *r_state, *r_ld;
 };
@@ -116,14 +117,11 @@ launch_fn lookup_bwd_state(int dtype, int chunk, int dk, int dv);
 hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int K,
                                int reverse, hipStream_t stream);
-// The re-split of flagged units.  resplit_list: one workgroup turns the flags of n_units units into
-// list = {n, X, u_0 .. u_{n-1}}: the first n = min(flagged, R) flagged units in unit order, each to
-// be cut into X pieces (the largest power of 2 <= xmax with n X <= R), and clears their flags, so
-// the plain exact pass skips them and takes only the flagged units beyond R.  resplit_scan: the
-// segment scan over each listed unit's X pieces (nothing when X = 1), starting from hb[u] (null:
-// zero) and writing the end value to hout[u] (null: not written).
-hipError_t launch_resplit_list(int* flags, int* list, int n_units, int R, int xmax, hipStream_t stream);
-hipError_t launch_resplit_scan(const int* list, const float* r_state, const float* r_ld, const float* hb,
+// The scan of the re-split (list = {n, X, u_0 .. u_{n-1}}, written by the state pass over the
+// pieces): clears the listed units' flags, so that the plain exact pass skips them and takes only
+// the flagged units beyond R; then, when X > 1, the segment scan over each listed unit's X pieces,
+// starting from hb[u] (null: zero) and writing the end value to hout[u] (null: not written).
+hipError_t launch_resplit_scan(const int* list, int* flags, const float* r_state, const float* r_ld, const float* hb,
                                float* r_carry, float* hout, int R, int dk, int dv, int reverse, hipStream_t stream);
 
 hipError_t launch_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
