@@ -578,3 +578,63 @@ def test_headline_workload_at_full_size():
         " ".join("%s=%.1e" % kv for kv in el.items()))
     bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("strong", [False, True], ids=["default-gates", "strong-stretches"])
+def test_the_whole_path_replays_in_a_hip_graph(strong):
+    """The six calls recorded into one HIP graph (torch's capture: no call allocates, clears or
+    synchronises), replayed three times with eager work and synchronisations in between: every
+    replay equals the eager run bit for bit.  16 heads of 8 segments, cut into sub-segments; with
+    strong stretches the fast kernels flag units and the re-split redoes them, inside the graph."""
+    B, H, T, dk, dv, chunk, P, K = 1, 16, 65536, 64, 64, 64, 8, 2
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 31, True, "logsigmoid16")
+    if strong:
+        d["g"] = inputs.add_strong_windows(d["g"], P, 12)
+    x = dev(d)
+    ws = torch.empty(gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, chunk, P, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    f32 = dict(device="cuda", dtype=torch.float32)
+    buf = {"o": torch.empty_like(x["v"]), "cs": torch.empty((B, H, T // chunk, dk, dv), device="cuda",
+                                                             dtype=torch.bfloat16),
+           "S": torch.empty((B, H, P, dk, dv), **f32), "ld": torch.empty((B, H, P, dk), **f32),
+           "S_in": torch.empty((B, H, P, dk, dv), **f32), "h": torch.empty((B, H, dk, dv), **f32),
+           "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+           "dg": torch.empty_like(x["g"]), "D": torch.empty((B, H, P, dk, dv), **f32),
+           "G": torch.empty((B, H, P, dk, dv), **f32), "dh0": torch.empty((B, H, dk, dv), **f32)}
+    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
+
+    def path():
+        gla.gla_chunk_fwd(q, k, v, g, chunk, P, o=buf["o"], chunk_states=buf["cs"], seg_state=buf["S"],
+                          seg_logdecay=buf["ld"], workspace=ws)
+        gla.gla_segment_scan(buf["S"], buf["ld"], K, seg_carry=buf["S_in"], h_out=buf["h"])
+        gla.gla_segment_correct(gla.GLA_FWD, chunk, P, q=q, g=g, seg_in=buf["S_in"], o=buf["o"],
+                                chunk_states=buf["cs"])
+        gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], buf["S_in"], chunk, P, dq=buf["dq"], dk=buf["dk"],
+                          dv=buf["dv"], dg=buf["dg"], seg_dstate=buf["D"], workspace=ws)
+        gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True, seg_carry=buf["G"], h_out=buf["dh0"])
+        gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=buf["S_in"], seg_grad=buf["G"],
+                                chunk_states=buf["cs"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"])
+
+    path()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in buf.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()  # warm-up on the capture's stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in buf.values():
+            t.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in ref.items():
+            assert torch.equal(buf[n], t), (r, n)
+    check({n: as_f64(buf[n]) for n in ("o", "dq", "dk", "dv", "dg")},
+          oracle_pipeline(d, chunk, P, True), ("o", "dq", "dk", "dv", "dg"), TOL["bf16"], "graph replay")
