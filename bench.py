@@ -220,13 +220,16 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
     ]
     ms_ag, pc_ag, _ = time_steps(torch, ag, 10, 2, stream)
     # serial chain: one segment per (b, h); the scan is a copy and the corrections find a zero
-    # incoming state, so the step is the two local passes over the whole sequence
+    # incoming state, so the step is the two local passes over the whole sequence.  A flags-only
+    # workspace keeps each call from cutting the sequence into sub-segments (which would be the
+    # decomposition again, inside the call)
     f32 = torch.float32
     one = {n: torch.empty((B, H, 1, dk, dv), device=q.device, dtype=f32) for n in ("S", "S_in", "D", "G")}
     ld1 = torch.empty((B, H, 1, dk), device=q.device, dtype=f32)
+    ws1 = torch.empty(gla.flags_workspace_size(B, H, 1), device=q.device, dtype=torch.uint8)
     serial = [
         ("gla_chunk_fwd(P=1)", lambda: gla.gla_chunk_fwd(q, k, v, g, C, 1, o=buf["o"], chunk_states=buf["cs"],
-                                                          seg_state=one["S"], seg_logdecay=ld1, workspace=buf["ws"])),
+                                                          seg_state=one["S"], seg_logdecay=ld1, workspace=ws1)),
         ("gla_segment_scan(P=1)", lambda: gla.gla_segment_scan(one["S"], ld1, K, seg_carry=one["S_in"],
                                                                 h_out=buf["h_fin"])),
         ("gla_segment_correct(FWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_FWD, C, 1, q=q, g=g,
@@ -234,7 +237,7 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
                                                                            chunk_states=buf["cs"])),
         ("gla_chunk_bwd(P=1)", lambda: gla.gla_chunk_bwd(q, k, v, g, do, buf["cs"], one["S_in"], C, 1,
                                                           dq=buf["dq"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"],
-                                                          seg_dstate=one["D"], workspace=buf["ws"])),
+                                                          seg_dstate=one["D"], workspace=ws1)),
         ("gla_segment_scan(reverse, P=1)", lambda: gla.gla_segment_scan(one["D"], ld1, K, reverse=True,
                                                                          seg_carry=one["G"], h_out=buf["dh0"])),
         ("gla_segment_correct(BWD, P=1)", lambda: gla.gla_segment_correct(gla.GLA_BWD, C, 1, k=k, v=v, g=g,
