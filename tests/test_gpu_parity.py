@@ -87,6 +87,20 @@ def oracle_pipeline(d, chunk, P, bwd, h0=None, dhT=None):
     return res
 
 
+def homogeneity(x, dx, ref):
+    """Per (b, h): the homogeneity identity sum<x, dx> = sum<do, o> (o is degree 1 in each of q, k, v),
+    as two ratios.  gated: |sum<x, dx> - sum<do, o>| / ||x * dx||_2, the difference against the
+    natural size of a sum of that many terms of either sign (a gradient of the right size but
+    wrong signs or places still gives a ratio near 1).  cond: the same difference over
+    |sum<do, o>|, reported only: that sum cancels, so where it happens to be small the ratio grows
+    with no error in dx."""
+    prod = x.double() * dx.double()
+    diff = (prod.sum(dim=(2, 3)) - ref).abs()
+    scale = prod.pow(2).sum(dim=(2, 3)).sqrt()
+    del prod
+    return (diff / scale)[0].tolist(), (diff / ref.abs())[0].tolist()
+
+
 def check(gpu, ref, keys, tol, label):
     errs = {n: maxrel(gpu[n], ref[n]) for n in keys}
     say(label, " ".join("%s=%.2e(el %.1e)" % (n, e, elemrel(gpu[n], ref[n])) for n, e in errs.items()))
@@ -530,13 +544,11 @@ def test_headline_workload_at_full_size():
     torch.cuda.synchronize()
     say("gpu fwd+bwd done")
     # homogeneity on every (b, h)
-    def dot(a, c):
-        return (a.double() * c.double()).sum(dim=(2, 3))
-    ref = dot(x["do"], f["o"])
+    ref = (x["do"].double() * f["o"].double()).sum(dim=(2, 3))
     for xn, dn in (("q", "dq"), ("k", "dk"), ("v", "dv")):
-        rel = float(((dot(x[xn], b[dn]) - ref).abs() / ref.abs()).max())
-        say("homogeneity %s: %.2e" % (xn, rel))
-        assert rel <= TOL["bf16"], xn
+        gated, cond = homogeneity(x[xn], b[dn], ref)
+        say("homogeneity %s: %.2e (over |sum<do,o>|: %.2e)" % (xn, max(gated), max(cond)))
+        assert max(gated) <= TOL["bf16"], xn
     # oracle on head 0, every token
     h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, 0, w.dtype, 0, True)
     a = {n: as_f64(t) for n, t in h.items()}
@@ -638,3 +650,43 @@ def test_the_whole_path_replays_in_a_hip_graph(strong):
             assert torch.equal(buf[n], t), (r, n)
     check({n: as_f64(buf[n]) for n in ("o", "dq", "dk", "dv", "dg")},
           oracle_pipeline(d, chunk, P, True), ("o", "dq", "dk", "dv", "dg"), TOL["bf16"], "graph replay")
+
+
+def test_element_offsets_beyond_two_to_the_31():
+    """9 heads of 1M tokens at d_k = 128, d_v = 256 (576 units, three waves of workgroups): v, o, do
+    and dv hold 2.4e9 elements and the chunk states 4.8e9, so every kernel indexes past 2^31.  The
+    last head, whose elements sit highest, is compared with the oracle over all its tokens; the
+    homogeneity identity is checked on every head."""
+    import dataclasses
+    w = dataclasses.replace(inputs.WORKLOADS[inputs.HEADLINE], name="h9_t1m_p64", H=9)
+    assert w.B * w.H * w.T * w.dv > 2 ** 31 and w.B * w.H * (w.T // w.chunk) * w.dk * w.dv > 2 ** 32
+    t = time.time()
+    x = dev(inputs.generate_workload(w))
+    say("generated %s in %.1fs" % (w.name, time.time() - t))
+    f = gla.zeco_forward(x["q"], x["k"], x["v"], x["g"], w.chunk, w.P, w.K)
+    b = gla.zeco_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, w.chunk, w.P, w.K)
+    torch.cuda.synchronize()
+    say("gpu fwd+bwd done")
+
+    ref = (x["do"].double() * f["o"].double()).sum(dim=(2, 3))
+    hom = {}
+    for xn, dn in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        gated, cond = homogeneity(x[xn], b[dn], ref)
+        say("homogeneity %s per head: %s (over |sum<do,o>|: %s)" % (xn, " ".join("%.1e" % r for r in gated),
+                                                                   " ".join("%.1e" % r for r in cond)))
+        hom[xn] = max(gated)
+    hl = w.H - 1
+    h = inputs.generate_head(w.B, w.H, w.T, w.dk, w.dv, 0, hl, w.dtype, 0, True)
+    a = {n: as_f64(t_) for n, t_ in h.items()}
+    del h
+    t = time.time()
+    o_ref, hT = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"])
+    gb = oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"])
+    say("oracle fwd+bwd of head %d over %d tokens: %.1fs" % (hl, w.T, time.time() - t))
+    errs = {"o": maxrel(as_f64(f["o"][:1, hl:hl + 1]), o_ref), "h_final": maxrel(as_f64(f["h_final"][:1, hl:hl + 1]), hT)}
+    for n in ("dq", "dk", "dv", "dg", "dh0"):
+        errs[n] = maxrel(as_f64(b[n][:1, hl:hl + 1]), gb[n])
+    say("head %d: " % hl + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad
+    assert all(r <= TOL["bf16"] for r in hom.values()), hom
