@@ -59,7 +59,9 @@
  *             (chunk 16 always runs the sub-block kernels: the bf16 MFMA contracts 32 tokens)
  *   GLA_F32:  chunk in {16, 32, 64}; dk in {16, 32}; dv in {16, 32}
  *   always:   B, H, T, P >= 1 (an empty sequence is rejected with GLA_ERR_INVALID_ARG);
- *             T % P == 0; (T / P) % chunk == 0
+ *             T % P == 0; (T / P) % chunk == 0.  A sequence of another length may be padded at
+ *             its end with q = k = v = do = 0 and g = 0: such tokens leave every output and
+ *             gradient of the real tokens, the final state and dh0 unchanged.
  */
 #ifndef GLA_H
 #define GLA_H

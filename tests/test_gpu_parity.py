@@ -690,3 +690,38 @@ def test_element_offsets_beyond_two_to_the_31():
     bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
     assert not bad, bad
     assert all(r <= TOL["bf16"] for r in hom.values()), hom
+
+
+@pytest.mark.parametrize("T_real,chunk,P", [(1000, 64, 4), (333, 16, 3), (4097, 32, 8)])
+def test_a_ragged_sequence_padded_with_zeros_is_exact(T_real, chunk, P):
+    """The calls take T as a multiple of P * chunk.  A sequence of any other length is padded at
+    its end with q = k = v = do = 0 and g = 0: the padded tokens add nothing to the state and
+    decay nothing, so the real tokens' outputs and gradients, h_final and dh0 are those of the
+    unpadded sequence.  Checked against the oracle's recurrence over the T_real tokens alone,
+    with boundary states."""
+    B, H, dk, dv, K = 1, 2, 64, 128, 2
+    step = P * chunk
+    T = -(-T_real // step) * step
+    d = inputs.generate(B, H, T_real, dk, dv, "bf16", 37, True, "logsigmoid16")
+    pad = {}
+    for n, t in d.items():
+        z = torch.zeros((B, H, T - T_real, t.shape[-1]), dtype=t.dtype)
+        pad[n] = torch.cat([t, z], dim=2).contiguous()
+    rng = np.random.default_rng(5)
+    h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    x = dev(pad)
+    f = gla.zeco_forward(x["q"], x["k"], x["v"], x["g"], chunk, P, K, h0=h0.cuda())
+    b = gla.zeco_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, chunk, P, K, dhT=dhT.cuda())
+    torch.cuda.synchronize()
+    a = {n: as_f64(t) for n, t in d.items()}
+    o, hT = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"], h0.numpy())
+    ref = {"o": o, "h_final": hT}
+    ref.update(oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"], h0.numpy(), dhT.numpy()))
+    got = {n: as_f64(f[n][:, :, :T_real]) for n in ("o",)}
+    got["h_final"] = as_f64(f["h_final"])
+    for n in ("dq", "dk", "dv", "dg"):
+        got[n] = as_f64(b[n][:, :, :T_real])
+    got["dh0"] = as_f64(b["dh0"])
+    check(got, ref, ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL["bf16"],
+          "T %d padded to %d, chunk %d, P %d" % (T_real, T, chunk, P))
