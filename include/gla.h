@@ -152,9 +152,11 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
 /*
  * gla_chunk_fwd_noalloc -- gla_chunk_fwd for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
- * arguments, results and checks without the workspace, which here is a library-owned device
- * array of 256 KiB on each GPU (one int per unit), looked up once per device and kept until the
- * process ends.  The call allocates nothing.  B*H*P above 65536 is rejected with
+ * arguments and checks without the workspace, which here is a library-owned device array of
+ * 256 KiB on each GPU (one int per unit), looked up once per device and kept until the process
+ * ends.  The array holds the per-unit flags only, so the call neither cuts segments into
+ * sub-segments nor re-splits flagged units; its results equal gla_chunk_fwd's up to rounding
+ * (bit for bit where gla_chunk_fwd does neither).  The call allocates nothing.  B*H*P above 65536 is rejected with
  * GLA_ERR_INVALID_ARG before any HIP call.  The array's contents are written before they are
  * read, so nothing needs clearing between calls; calls that may run at the same time on one GPU
  * (two streams, two threads) share the array and race.
