@@ -166,11 +166,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   static_assert(NGR <= NT / 16, "one gate row per 4 channels");
 
   __shared__ __attribute__((aligned(16))) E sQb[kSB * LDQ];  // Qbar [t][c]
+  __shared__ __attribute__((aligned(16))) E sQh[kSB * LDQ];  // q exp(b - lam) [t][c] (scores on MFMA)
   __shared__ __attribute__((aligned(16))) E sKt[kSB * LDQ];  // Ktil [s][c]
   __shared__ __attribute__((aligned(16))) E sV[kSB * LDV];   // V [s][j]
   __shared__ __attribute__((aligned(16))) E sA[kSB * LDA];   // A [t][s], masked
   __shared__ __attribute__((aligned(16))) float sRed[NGW][kSB][kSB];  // per-wave partial scores
   __shared__ __attribute__((aligned(16))) float sLamE[DK];            // exp(lam)
+  __shared__ __attribute__((aligned(8))) unsigned char sMod[8];       // per wave: see post_moderate
+  static_assert(NW <= 8, "one verdict byte per wave");
 
   const UnitPlace up = unit_place(a, n_units, DK, (long)DK * DV);
   if (!up.live) return;
@@ -209,15 +212,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   SubGate<E> xn;
   Vec8<E> pvn;
   fetch_sub_block<E, DK, DV, NVP>(xn, pvn, q, k, a.g, v, tok0, tid, gact);
+  // Whether every channel of the sub-block whose raw gates xr holds decays by at most
+  // exp(kFastMinChunkLogDecay): sufficient is that none of its 16 log-gates is below a 16th of that.
+  // Each wave posts its verdict in sMod for the next sub-block before the barrier that ends the
+  // current one, so the choice between the two forms of the scores needs no barrier of its own.
+  constexpr float kModerateGate = kFastMinChunkLogDecay / kSB;
+  constexpr unsigned long long kAllModerate = (NW == 8 ? ~0ull : (1ull << (8 * NW)) - 1) & 0x0101010101010101ull;
+  auto post_moderate = [&](const SubGate<E>& xr) {
+    const bool ok = xr.b[0] >= kModerateGate && xr.b[1] >= kModerateGate && xr.b[2] >= kModerateGate &&
+                    xr.b[3] >= kModerateGate;
+    const bool wave_ok = __ballot(!ok) == 0;
+    if (lane_id() == 0) sMod[w] = wave_ok ? 1 : 0;
+  };
+  post_moderate(xn);
+  __syncthreads();
 
   for (int n = 0; n < nchunks; ++n) {
     for (int j = 0; j < NSB; ++j) {
       const long ts0 = tok0 + (long)n * C + j * kSB;
-      // ---- gate prefix, Qbar, Ktil, V -> LDS; element-wise scores of the sub-block ----
+      const bool moderate = (*reinterpret_cast<const unsigned long long*>(sMod) & kAllModerate) == kAllModerate;
+      // ---- gate prefix, Qbar, Ktil, V -> LDS; the scores of the sub-block ----
       SubGate<E> x = xn;
       x.scan();
       if (NVP == NT || tid < NVP) pvn.store(sV + (tid / (DV / 8)) * LDV + (tid % (DV / 8)) * 8);
-      if (n < nchunks - 1 || j < NSB - 1) fetch_sub_block<E, DK, DV, NVP>(xn, pvn, q, k, a.g, v, ts0 + kSB, tid, gact);
+      const bool more = n < nchunks - 1 || j < NSB - 1;
+      if (more) fetch_sub_block<E, DK, DV, NVP>(xn, pvn, q, k, a.g, v, ts0 + kSB, tid, gact);
       if (gact) {
         f32x4 xq, xk;
 #pragma unroll
@@ -227,6 +246,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
         }
         store4(sQb + t * LDQ + 4 * R, xq);
         store4(sKt + t * LDQ + 4 * R, xk);
+        if (moderate) {
+          f32x4 xh;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xh[e] = x.q[e] * __expf(x.b[e] - x.lam[e]);
+          store4(sQh + t * LDQ + 4 * R, xh);
+        }
         if (t == 0) {
           f32x4 le;
 #pragma unroll
@@ -235,19 +260,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
         }
         ldsum += x.lam;
       }
-      if (w < NGW) {
-        float part[16];
-        diag_parts(x, t, part);
-        const f32x4 r = reduce_scores(part);
-        *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
-      }
-      __syncthreads();
-      if (tid < kSB * kSB) {
-        const int tt = tid >> 4, ss = tid & 15;
-        float acc = 0.f;
+      if (moderate) {
+        // A = (q exp(b - lam)) (k exp(lam - b))^T on one MFMA tile, as the fast kernels factor it
+        // (both factors within exp(40) here), masked to s <= t
+        __syncthreads();
+        if (w == 0) {
+          const f32x4 acc = mma<E, false, false>(zero4(), sQh, LDQ, sKt, LDQ, 0, DK);
 #pragma unroll
-        for (int ww = 0; ww < NGW; ++ww) acc += sRed[ww][tt][ss];
-        sA[tt * LDA + ss] = (E)acc;
+          for (int i = 0; i < 4; ++i) sA[(4 * g4 + i) * LDA + n16] = (E)(n16 <= 4 * g4 + i ? acc[i] : 0.f);
+        }
+      } else {
+        // element by element, every exponent non-positive
+        if (w < NGW) {
+          float part[16];
+          diag_parts(x, t, part);
+          const f32x4 r = reduce_scores(part);
+          *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
+        }
+        __syncthreads();
+        if (tid < kSB * kSB) {
+          const int tt = tid >> 4, ss = tid & 15;
+          float acc = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NGW; ++ww) acc += sRed[ww][tt][ss];
+          sA[tt * LDA + ss] = (E)acc;
+        }
       }
       __syncthreads();
       // ---- O^T[j][t] = V^T A^T + S^T Qbar^T; S = diag(exp(lam)) S + Ktil^T V ----
@@ -282,6 +319,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
             S[jj][kb] = mma_k16<E, true, true>(S[jj][kb] * le, sKt + kb * 16, LDQ, sV + (w * JPW + jj) * 16, LDV);
         }
       }
+      if (more) post_moderate(xn);  // every wave has read sMod for this sub-block before its first barrier
       __syncthreads();
     }
     // ---- the local state after the chunk, in the tiled chunk-state layout (none kept for a
