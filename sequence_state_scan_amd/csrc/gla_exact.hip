@@ -383,6 +383,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) E sdO[kSB * LDV];        // dO [t][j], sub-block
   __shared__ __attribute__((aligned(16))) E sA[kSB * LDA];         // A [t][s], masked
   __shared__ float sdA[kSB][kSB + 1];                               // dA [t][s], masked
+  __shared__ __attribute__((aligned(16))) E sQh[kSB * LDQ];        // q exp(b - lam) [t][c], sub-block
+  __shared__ __attribute__((aligned(16))) E sdAb[kSB * LDA];       // dA [t][s], masked, element type
+  __shared__ __attribute__((aligned(8))) unsigned char sMod[8];     // per wave: see post_moderate
+  static_assert(NW <= 8, "one verdict byte per wave");
   __shared__ __attribute__((aligned(16))) float sLamE[kMaxChunk / kSB][DK];  // exp(lam) per sub-block
   __shared__ __attribute__((aligned(16))) unsigned char sUR[SZ_U > SZ_RED ? SZ_U : SZ_RED];
   E* const sU = reinterpret_cast<E*>(sUR);                            // U [c][j], after the scores
@@ -437,6 +441,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   Vec8<E> pdn;
   fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, tok0 + (long)(nchunks - 1) * C + (NSB - 1) * kSB, threadIdx.x,
                                    urole);
+  // Whether every channel of the sub-block whose raw gates xr holds decays by at most
+  // exp(kFastMinChunkLogDecay), as in the forward: posted per wave for the next sub-block before the
+  // barrier that ends the current one
+  constexpr float kModerateGate = kFastMinChunkLogDecay / kSB;
+  constexpr unsigned long long kAllModerate = (NW == 8 ? ~0ull : (1ull << (8 * NW)) - 1) & 0x0101010101010101ull;
+  auto post_moderate = [&](const SubGate<E>& xr) {
+    const bool ok = xr.b[0] >= kModerateGate && xr.b[1] >= kModerateGate && xr.b[2] >= kModerateGate &&
+                    xr.b[3] >= kModerateGate;
+    const bool wave_ok = __ballot(!ok) == 0;
+    if (lane_id() == 0) sMod[w] = wave_ok ? 1 : 0;
+  };
+  post_moderate(xn);
+  __syncthreads();
 
   for (int n = nchunks - 1; n >= 0; --n) {
     const long tc0 = tok0 + (long)n * C;
@@ -473,10 +490,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       const long ts0 = tc0 + j * kSB;
       // lane indices re-derived here, so the per-lane addresses are not held across the loop
       const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4, R = tid >> 4, t = n16;
+      const bool moderate = (*reinterpret_cast<const unsigned long long*>(sMod) & kAllModerate) == kAllModerate;
       SubGate<E> x = xn;  // fetched one sub-block ahead
       x.scan();
       if (NVS == NT || tid < NVS) pdn.store(sdO + (tid / (DV / 8)) * LDV + (tid % (DV / 8)) * 8);
-      if (n > 0 || j > 0) fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, ts0 - kSB, tid, urole);
+      const bool more = n > 0 || j > 0;
+      if (more) fetch_sub_block<E, DK, DV, NVS>(xn, pdn, q, k, a.g, dO, ts0 - kSB, tid, urole);
+      if (moderate && urole) {
+        f32x4 xh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xh[e] = x.q[e] * __expf(x.b[e] - x.lam[e]);
+        store4(sQh + t * LDQ + 4 * R, xh);
+      }
       __syncthreads();
       // the stored global state before the chunk, requested here and used after the element-wise
       // sums (the segment's first chunk starts from seg_in, read where it is used)
@@ -497,12 +522,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
       if (w == 0) {
         const f32x4 acc = mma<E, false, false>(zero4(), sdO, LDV, sV + j * kSB * LDV, LDV, 0, DV);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdA[4 * g4 + i][n16] = n16 <= 4 * g4 + i ? acc[i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const float d = n16 <= 4 * g4 + i ? acc[i] : 0.f;
+          sdA[4 * g4 + i][n16] = d;
+          if (moderate) sdAb[(4 * g4 + i) * LDA + n16] = (E)d;
+        }
       }
       __syncthreads();
-      // ---- element-wise sums inside the sub-block: scores, and the intra parts of dq and dk ----
       f32x4 dqd = zero4(), dkd = zero4();
-      if (urole) {
+      if (moderate) {
+        // ---- a sub-block that decays by at most exp(-40): the fast kernels' factoring on MFMA tiles.
+        // Scores A = (q exp(b - lam)) Ktil^T; dq's intra part exp(b_t - lam) (dA Ktil)[t]; dk's
+        // exp(-b_s) (dA^T Qbar)[s] (every factor within exp(40)) ----
+        if (w == 0) {
+          const f32x4 acc = mma<E, false, false>(zero4(), sQh, LDQ, sKt + j * kSB * LDQ, LDQ, 0, DK);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sA[(4 * g4 + i) * LDA + n16] = (E)(n16 <= 4 * g4 + i ? acc[i] : 0.f);
+        }
+        if (urole) {
+          const f32x4 aq = mma_k16<E, true, false>(zero4(), sKt + j * kSB * LDQ + 16 * w, LDQ, sdAb, LDA);
+          const f32x4 ak = mma_k16<E, true, true>(zero4(), sQb + j * kSB * LDQ + 16 * w, LDQ, sdAb, LDA);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dqd[i] = __expf(x.b[i] - x.lam[i]) * aq[i];
+            dkd[i] = __expf(-x.b[i]) * ak[i];
+          }
+        }
+      } else if (urole) {
+        // ---- element-wise sums inside the sub-block: scores, and the intra parts of dq and dk ----
         // one exponential per (t, s, channel) serves the scores, dq and dk: exp(b_t - b_s) for s <= t
         // (scores and dq), exp(b_s - b_t) for s >= t (dk).  dA is masked (zero for s > t), so
         // dA[t][s] keeps dq to s <= t and dA[s][t] keeps dk to s >= t; the scores' s > t terms are
@@ -528,7 +575,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
         *reinterpret_cast<f32x4*>(&sRed[w][t][4 * g4]) = r;
       }
       __syncthreads();
-      if (tid < kSB * kSB) {
+      if (!moderate && tid < kSB * kSB) {
         const int tt = tid >> 4, ss = tid & 15;
         float acc = 0.f;
 #pragma unroll
@@ -616,6 +663,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
 #pragma unroll
         for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
       }
+      if (more) post_moderate(xn);  // every wave has read sMod for this sub-block before its first barrier
       __syncthreads();
     }
   }
