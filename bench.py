@@ -310,6 +310,27 @@ def path_calls(gla, w, x, buf, bwd=True):
     return calls
 
 
+def path_calls_states_first(gla, w, x, buf):
+    """The same step with the segments' incoming states first: state pass, scan, local pass from the
+    true incoming state (no correction), and the same for the backward."""
+    C, P, K = w.chunk, w.P, w.K
+    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
+    return [
+        ("gla_chunk_state", lambda: gla.gla_chunk_state(k, v, g, C, P, seg_state=buf["S_loc"], seg_logdecay=buf["ld"],
+                                                         workspace=buf["ws"])),
+        ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
+                                                           h_out=buf["h_fin"])),
+        ("gla_chunk_fwd_from", lambda: gla.gla_chunk_fwd_from(q, k, v, g, buf["S_in"], C, P, o=buf["o"],
+                                                               chunk_states=buf["cs"], workspace=buf["ws"])),
+        ("gla_chunk_dstate", lambda: gla.gla_chunk_dstate(q, g, do, C, P, seg_dstate=buf["D"], workspace=buf["ws"])),
+        ("gla_segment_scan(reverse)", lambda: gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True,
+                                                                    seg_carry=buf["G"], h_out=buf["dh0"])),
+        ("gla_chunk_bwd_from", lambda: gla.gla_chunk_bwd_from(q, k, v, g, do, buf["cs"], buf["S_in"], buf["G"], C, P,
+                                                               dq=buf["dq"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"],
+                                                               workspace=buf["ws"])),
+    ]
+
+
 def time_scrubbed(torch, calls, iters, warmup, stream, scrub):
     """Time each of `iters` steps on its own, with `scrub` (a large buffer) overwritten between them
     outside the timed events, so that no input is left in the last-level cache.  Returns
@@ -374,6 +395,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step (no g = 0 step, no other workloads)")
+    ap.add_argument("--order", choices=("correction", "states-first"), default="correction",
+                    help="the order of the step's calls: local pass, scan, correction (ZeCO's), or state pass, "
+                         "scan, local pass from the true incoming state")
     ap.add_argument("--streams", type=int, default=1,
                     help="time the step with the sequences split over this many streams (zeco_step_streams)")
     ap.add_argument("--stagger", action="store_true",
@@ -410,7 +434,7 @@ def main():
 
     B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
     buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
-    calls = path_calls(gla, w, x, buf)
+    calls = path_calls(gla, w, x, buf) if args.order == "correction" else path_calls_states_first(gla, w, x, buf)
     if args.streams > 1:
         sbuf = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, args.streams)
         calls = [("zeco_step_streams(%d)" % args.streams,
@@ -432,7 +456,7 @@ def main():
 
     # the dominant call and its roofline (algorithmic bytes of that call / its mean duration)
     dom = max(per_call, key=per_call.get) if args.streams == 1 else None
-    if dom == "gla_chunk_bwd":
+    if dom in ("gla_chunk_bwd", "gla_chunk_bwd_from"):  # the same inputs and outputs
         dom_bytes, dom_flops = alg_bytes(w, "chunk_bwd"), alg_flops(w, "chunk_bwd")
     elif dom == "gla_chunk_fwd":
         dom_bytes, dom_flops = alg_bytes(w, "fwd"), alg_flops(w, "chunk_fwd")
@@ -463,12 +487,24 @@ def main():
         x0 = dict(x)
         x0["g"] = torch.zeros_like(x["g"])
         ms0, pc0, _ = time_steps(torch, path_calls(gla, w, x0, buf), 10, 3, stream)
-        del x0
         log("g = 0: %.4f ms per step" % ms0)
+        # and in the order with the incoming states first, which has no correction pass to grow
+        ms0s, pc0s, _ = time_steps(torch, path_calls_states_first(gla, w, x0, buf), 10, 3, stream)
+        del x0
+        log("g = 0, states first: %.4f ms per step" % ms0s)
         extras = {"no_decay_step": {
             "gate": "zero", "ms_per_step": round(ms0, 4), "tokens_per_s": round(tokens / (ms0 / 1e3), 1),
             "hbm_frac": round(step_bytes / (ms0 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0.items()}}}
+            "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0.items()},
+            "states_first": {"ms_per_step": round(ms0s, 4), "tokens_per_s": round(tokens / (ms0s / 1e3), 1),
+                             "hbm_frac": round(step_bytes / (ms0s / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0s.items()}}}}
+        # the headline step itself in that order (default gates)
+        mss, pcs, _ = time_steps(torch, path_calls_states_first(gla, w, x, buf), 10, 3, stream)
+        log("states first: %.4f ms per step" % mss)
+        extras["states_first_step"] = {"gate": args.gate, "ms_per_step": round(mss, 4),
+                                       "tokens_per_s": round(tokens / (mss / 1e3), 1),
+                                       "per_call_ms": {k_: round(v_, 4) for k_, v_ in pcs.items()}}
         if args.strong_windows == 0 and args.gate == "logsigmoid16":
             # the same step with a few strongly decaying 64-token stretches: the segments they touch
             # are flagged by the fast kernels and redone, cut into pieces, by the exact kernels
@@ -507,7 +543,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C, "P": P, "K": K,
-                   "segment_tokens": w.L, "gate": args.gate, "streams": args.streams,
+                   "segment_tokens": w.L, "gate": args.gate, "order": args.order, "streams": args.streams,
                    "stagger": bool(args.stagger)},
         "roofline": roof, "cpu_baseline": cpu,
         "step_roofline": step_roof,

@@ -244,7 +244,9 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
  *   dk_[t], dv_[t] = gradients from segment p's own outputs (state gradient U starting at
  *                    zero at the segment's end): dk_[t] = U_t v[t], dv_[t] = U_t^T k[t]
  *   dg[t]          = sum_{t' >= t in segment} (q[t'] dq[t'] - k[t'] dk_[t'])  (float32; formed
- *                    chunk by chunk with the exact carry rowsum(S * U) at chunk boundaries)
+ *                    chunk by chunk with the exact carry rowsum(S * U) at chunk boundaries,
+ *                    itself formed from the chunk's own dk terms so that it cancels them to
+ *                    float32 rounding under strong decay)
  *   seg_dstate[b,h,p] = D_p = gradient w.r.t. the state entering segment p from segment p's
  *                    own outputs, float32 [dk][dv]
  * q, k, v, do, chunk_states and the outputs dq, dk_, dv_ share dtype.  Outputs are fully
@@ -257,6 +259,77 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          void* dq, void* dk_, void* dv_, float* dg, float* seg_dstate,
                          int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
                          void* workspace, size_t workspace_size, void* stream);
+
+/*
+ * ---- The same path with the incoming states first: no correction pass ----
+ *
+ * In the order above, every segment runs from a zero state and the correction afterwards makes its
+ * results global: a second pass over the chunks that the incoming state still reaches (the second
+ * pass over Q, K, V of the pith.science referee report, major comment 1).  Under weak or no decay
+ * it reaches every chunk.  The four calls below order the same decomposition the other way, as
+ * LASP's devices do (elamur.ai LASP summary: the K^T V state, the right product, carries the
+ * dependency between devices, and a device computes its outputs from the state it receives):
+ *
+ *   gla_chunk_state -> gla_segment_scan -> gla_chunk_fwd_from                        (forward)
+ *   gla_chunk_dstate -> gla_segment_scan(reverse) -> gla_chunk_bwd_from             (backward)
+ *
+ * A state pass reads k, v, g (forward) or q, g, do (backward) once more, a fixed cost; the
+ * corrections cost the chunks the incoming states reach, which depends on the decay.  The results
+ * equal those of the correction order up to rounding; seg_state, seg_logdecay and seg_dstate
+ * are the same quantities (local, from a zero state).
+ */
+
+/*
+ * gla_chunk_state -- each segment's local end state and summed log-gates, computed from a zero
+ * start (seg_state, seg_logdecay exactly as gla_chunk_fwd returns them, up to rounding), reading only
+ * k, v and g: S <- diag(exp(lam)) S + Ktil^T V per chunk, the state update of the chunkwise form.
+ * Inputs k, v (dtype), g (float32), [B][H][T][d]; outputs seg_state [B][H][P][dk][dv] and
+ * seg_logdecay [B][H][P][dk], float32, fully overwritten.
+ * workspace: optional (NULL, or gla_workspace_size(GLA_FWD, ...) bytes): with room, segments are cut
+ * into sub-segments when B*H*P < 256, as in gla_chunk_fwd.  bf16 with chunk 16 has no state-pass
+ * kernel of its own; the pass then runs in chunks of 64 or 32 tokens (whichever divides the
+ * segments), else GLA_ERR_UNSUPPORTED.
+ */
+gla_status gla_chunk_state(const void* k, const void* v, const float* g, float* seg_state, float* seg_logdecay,
+                           int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                           void* workspace, size_t workspace_size, void* stream);
+
+/*
+ * gla_chunk_fwd_from -- gla_chunk_fwd with each segment starting from its true incoming state
+ * seg_in[p] (the forward gla_segment_scan's seg_carry over gla_chunk_state's results) instead of
+ * zero: o and chunk_states come out GLOBAL, as after gla_segment_correct(GLA_FWD), and no
+ * correction follows.  seg_in: float32 [B][H][P][dk][dv].  Other arguments, layouts, the workspace
+ * and errors as gla_chunk_fwd (chunk_states may be NULL); there is no seg_state / seg_logdecay
+ * output.
+ */
+gla_status gla_chunk_fwd_from(const void* q, const void* k, const void* v, const float* g, const float* seg_in,
+                              void* o, void* chunk_states, int B, int H, int T, int dk, int dv, int chunk, int P,
+                              int dtype, void* workspace, size_t workspace_size, void* stream);
+
+/*
+ * gla_chunk_dstate -- each segment's local state gradient D_p (seg_dstate exactly as gla_chunk_bwd
+ * returns it, up to rounding): U <- diag(exp(lam)) U + Qbar^T dO walking the chunks back from a zero
+ * gradient at the segment's end, reading only q, g and do.  Output seg_dstate float32
+ * [B][H][P][dk][dv], fully overwritten.  The reverse scan takes it with gla_chunk_state's
+ * seg_logdecay.  workspace and the bf16 chunk-16 rule as gla_chunk_state (GLA_BWD size).
+ */
+gla_status gla_chunk_dstate(const void* q, const float* g, const void* do_, float* seg_dstate, int B, int H, int T,
+                            int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
+                            void* stream);
+
+/*
+ * gla_chunk_bwd_from -- gla_chunk_bwd with each segment's backward starting from seg_grad[p], the
+ * gradient w.r.t. the state leaving segment p from the later segments (the reverse gla_segment_scan's
+ * seg_carry over gla_chunk_dstate's results): dq, dk, dv and dg come out GLOBAL, as after
+ * gla_segment_correct(GLA_BWD), and no correction follows.  chunk_states must hold the global
+ * states (gla_chunk_fwd_from) and seg_in the forward scan's seg_carry.  dg includes the
+ * rowsum(S_end * seg_grad[p]) term at each segment's end.  Other arguments, layouts, the workspace
+ * and errors as gla_chunk_bwd; there is no seg_dstate output.
+ */
+gla_status gla_chunk_bwd_from(const void* q, const void* k, const void* v, const float* g, const void* do_,
+                              const void* chunk_states, const float* seg_in, const float* seg_grad, void* dq,
+                              void* dk_, void* dv_, float* dg, int B, int H, int T, int dk, int dv, int chunk, int P,
+                              int dtype, void* workspace, size_t workspace_size, void* stream);
 
 #ifdef __cplusplus
 }

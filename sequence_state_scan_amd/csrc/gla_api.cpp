@@ -205,6 +205,101 @@ gla_status launched(const char* fn, hipError_t e) {
   return ok();
 }
 
+// The state passes of gla_chunk_state / gla_chunk_dstate: the kernels of `chunk`, or where there
+// are none (bf16 chunk 16 runs only the exact kernels) those of the longest chunk that divides the
+// segments (the state does not depend on the chunk length beyond rounding).  Returns the chunk
+// length used, 0 if none will do.
+int state_pass_chunk(int dtype, int dk, int dv, int chunk, int seg_len, gla::launch_fn* fwd_state,
+                     gla::launch_fn* bwd_state) {
+  for (int c : {chunk, 64, 32}) {
+    if (seg_len % c != 0) continue;
+    *fwd_state = gla::lookup_fwd_state(dtype, c, dk, dv);
+    *bwd_state = gla::lookup_bwd_state(dtype, c, dk, dv);
+    if (*fwd_state && *bwd_state) return c;
+  }
+  return 0;
+}
+
+// Sub-segments of a state pass: as many as the workspace holds, up to the count that fills the chip.
+int state_pass_split(int B, int H, int T, int dk, int dv, int chunk, int P, size_t bytes) {
+  const long long units = (long long)B * H * P;
+  const int nch = T / P / chunk;
+  int S = 1;
+  while (units * S < kFillUnits && nch % (2 * S) == 0 && nch / (2 * S) >= 2 &&
+         workspace_layout(B, H, P, dk, dv, 2 * S, 0).total <= bytes)
+    S *= 2;
+  return S;
+}
+
+// gla_chunk_state (which == GLA_FWD: seg_state, seg_logdecay from k, v, g) and gla_chunk_dstate
+// (GLA_BWD: seg_dstate from q, g, do).
+gla_status state_pass_run(int which, const void* q, const void* k, const void* v, const float* g, const void* do_,
+                          float* out_state, float* out_ld, int B, int H, int T, int dk, int dv, int chunk, int P,
+                          int dtype, void* workspace, size_t workspace_size, void* stream) {
+  const char* fn = which == GLA_FWD ? "gla_chunk_state" : "gla_chunk_dstate";
+  Kernels kern;
+  gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
+  if (st != GLA_OK) return st;
+  if (which == GLA_FWD ? (!k || !v || !g || !out_state || !out_ld) : (!q || !g || !do_ || !out_state))
+    return fail(GLA_ERR_INVALID_ARG, which == GLA_FWD ? "%s: k, v, g, seg_state and seg_logdecay must be non-null"
+                                                      : "%s: q, g, do and seg_dstate must be non-null", fn);
+  const void* ins[] = {q, k, v, g, do_};
+  for (const void* p : ins)
+    if (p && (p == out_state || p == out_ld || p == workspace))
+      return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
+  gla::launch_fn fwd_state = nullptr, bwd_state = nullptr;
+  const int cs = state_pass_chunk(dtype, dk, dv, chunk, T / P, &fwd_state, &bwd_state);
+  if (!cs)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: no state-pass kernel for dtype=%s dk=%d dv=%d and segments of %d tokens",
+                fn, dtype == GLA_BF16 ? "bf16" : "f32", dk, dv, T / P);
+  const int S = state_pass_split(B, H, T, dk, dv, cs, P, workspace ? workspace_size : 0);
+  const Workspace lay = workspace_layout(B, H, P, dk, dv, S, 0);
+  char* ws = static_cast<char*>(workspace);
+  float* sub_state = S > 1 ? reinterpret_cast<float*>(ws + lay.sub_state) : out_state;
+  float* sub_ld = S > 1 ? reinterpret_cast<float*>(ws + lay.sub_ld) : out_ld;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int units = B * H * P;
+  if (which == GLA_FWD) {
+    gla::FwdArgs a{};
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.BH = B * H;
+    a.T = T;
+    a.Dk = dk;
+    a.Dv = dv;
+    a.P = P;
+    a.chunk = cs;
+    a.S = S;
+    a.sub_state = sub_state;
+    a.sub_ld = sub_ld;
+    st = launched(fn, fwd_state(&a, s));
+  } else {
+    gla::BwdArgs a{};
+    a.q = q;
+    a.g = g;
+    a.dO = do_;
+    a.BH = B * H;
+    a.T = T;
+    a.Dk = dk;
+    a.Dv = dv;
+    a.P = P;
+    a.chunk = cs;
+    a.S = S;
+    a.sub_state = sub_state;
+    a.sub_ld = S > 1 ? sub_ld : nullptr;  // the segments' log decays come from gla_chunk_state
+    st = launched(fn, bwd_state(&a, s));
+  }
+  if (st != GLA_OK || S == 1) return st;
+  // the scan over each segment's sub-segments, from zero at its start (end): its end value is the
+  // segment's state (gradient)
+  float* carry = reinterpret_cast<float*>(ws + lay.carry);
+  st = launched(fn, gla::launch_segment_scan(sub_state, sub_ld, nullptr, carry, out_state, units, S, dk, dv, 1,
+                                             which == GLA_FWD ? 0 : 1, s));
+  if (st != GLA_OK || which != GLA_FWD) return st;
+  return launched(fn, gla::launch_sum_logdecay(sub_ld, out_ld, units, S, dk, s));
+}
+
 }  // namespace
 
 namespace gla {
@@ -252,25 +347,38 @@ gla_status gla_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
                          int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
                          void* stream) {
-  return gla::chunk_fwd_capped(q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P,
+  return gla::chunk_fwd_capped(q, k, v, g, nullptr, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk,
+                               P, dtype, workspace, workspace_size, 0, stream);
+}
+
+gla_status gla_chunk_fwd_from(const void* q, const void* k, const void* v, const float* g, const float* seg_in,
+                              void* o, void* chunk_states, int B, int H, int T, int dk, int dv, int chunk, int P,
+                              int dtype, void* workspace, size_t workspace_size, void* stream) {
+  if (!seg_in) return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_from: seg_in must be non-null");
+  return gla::chunk_fwd_capped(q, k, v, g, seg_in, o, chunk_states, nullptr, nullptr, B, H, T, dk, dv, chunk, P,
                                dtype, workspace, workspace_size, 0, stream);
 }
 
 }  // extern "C"
 
-gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, void* o,
-                                 void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T,
-                                 int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
-                                 int max_split, void* stream) {
-  const char* fn = "gla_chunk_fwd";
+gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, const float* seg_in,
+                                 void* o, void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H,
+                                 int T, int dk, int dv, int chunk, int P, int dtype, void* workspace,
+                                 size_t workspace_size, int max_split, void* stream) {
+  const bool from = seg_in != nullptr;
+  const char* fn = from ? "gla_chunk_fwd_from" : "gla_chunk_fwd";
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
   if (st != GLA_OK) return st;
-  if (!q || !k || !v || !g || !o || !seg_state || !seg_logdecay)  // chunk_states may be NULL (forward only)
+  if (from) {
+    if (!q || !k || !v || !g || !o)  // chunk_states may be NULL (forward only)
+      return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g, seg_in and o must be non-null", fn);
+  } else if (!q || !k || !v || !g || !o || !seg_state || !seg_logdecay) {  // chunk_states may be NULL
     return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g, o, seg_state and seg_logdecay must be non-null", fn);
-  const void* ins[] = {q, k, v, g};
+  }
+  const void* ins[] = {q, k, v, g, seg_in};
   for (const void* p : ins)
-    if (p == o || p == chunk_states || p == workspace)
+    if (p && (p == o || p == chunk_states || p == workspace))
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
   const Schedule sch = workspace ? fitting_schedule(B, H, T, dk, dv, chunk, P, kern, max_split, workspace_size)
                                  : Schedule{0, 0};
@@ -282,18 +390,20 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
   const Workspace lay = workspace_layout(B, H, P, dk, dv, S, sch.R);
   char* ws = static_cast<char*>(workspace);
   gla::FwdArgs a{q, k, v, g, o, chunk_states, seg_state, seg_logdecay, reinterpret_cast<int*>(ws + lay.flags),
-                 B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
+                 B * H, T, dk, dv, P, chunk, S, from ? seg_in : nullptr, nullptr, nullptr};
+  a.from_in = from ? 1 : 0;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (S > 1) {
     // state pass over the sub-segments, then the scan over them inside each segment: the state
-    // entering each sub-segment (zero at the segment's start) and, as its end value, the segment's
-    // local end state
+    // entering each sub-segment (from zero at the segment's start, or from seg_in[p]) and, as its
+    // end value, the segment's local end state
     a.sub_state = reinterpret_cast<float*>(ws + lay.sub_state);
     a.sub_ld = reinterpret_cast<float*>(ws + lay.sub_ld);
     float* carry = reinterpret_cast<float*>(ws + lay.carry);
+    a.init = nullptr;
     st = launched(fn, kern.fwd_state(&a, s));
     if (st != GLA_OK) return st;
-    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, nullptr, carry, seg_state, B * H * P, S, dk,
+    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, seg_in, carry, seg_state, B * H * P, S, dk,
                                                dv, 1, 0, s));
     if (st != GLA_OK) return st;
     a.init = carry;
@@ -315,7 +425,7 @@ gla_status gla::chunk_fwd_capped(const void* q, const void* k, const void* v, co
       st = launched(fn, kern.fwd_state(&a, s));
       if (st != GLA_OK) return st;
       st = launched(fn, gla::launch_resplit_scan(list, a.flags, a.r_state, a.r_ld, a.init, r_carry,
-                                                 S > 1 ? nullptr : seg_state, sch.R, dk, dv, 0, s));
+                                                 S > 1 || from ? nullptr : seg_state, sch.R, dk, dv, 0, s));
       if (st != GLA_OK) return st;
     }
   } else {
@@ -383,19 +493,26 @@ gla_status gla_segment_correct(int mode, const void* q, const void* k, const voi
   return launched(fn, kern.corr_bwd(&a, s));
 }
 
-gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* do_,
-                         const void* chunk_states, const float* seg_in, void* dq, void* dk_, void* dv_, float* dg,
-                         float* seg_dstate, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
-                         void* workspace, size_t workspace_size, void* stream) {
-  const char* fn = "gla_chunk_bwd";
+}  // extern "C"
+
+namespace {
+
+// gla_chunk_bwd, or with seg_grad non-null gla_chunk_bwd_from: every segment's backward starts from
+// seg_grad[p] at its end (seg_dstate unused).
+gla_status chunk_bwd_run(const void* q, const void* k, const void* v, const float* g, const void* do_,
+                         const void* chunk_states, const float* seg_in, const float* seg_grad, void* dq, void* dk_,
+                         void* dv_, float* dg, float* seg_dstate, int B, int H, int T, int dk, int dv, int chunk,
+                         int P, int dtype, void* workspace, size_t workspace_size, void* stream) {
+  const bool from = seg_grad != nullptr;
+  const char* fn = from ? "gla_chunk_bwd_from" : "gla_chunk_bwd";
   Kernels kern;
   gla_status st = check_shape(fn, B, H, T, dk, dv, chunk, P, dtype, &kern);
   if (st != GLA_OK) return st;
-  if (!q || !k || !v || !g || !do_ || !chunk_states || !seg_in || !dq || !dk_ || !dv_ || !dg || !seg_dstate)
+  if (!q || !k || !v || !g || !do_ || !chunk_states || !seg_in || !dq || !dk_ || !dv_ || !dg || (!from && !seg_dstate))
     return fail(GLA_ERR_INVALID_ARG, "%s: every pointer argument must be non-null", fn);
-  const void* ins[] = {q, k, v, g, do_, chunk_states, seg_in};
+  const void* ins[] = {q, k, v, g, do_, chunk_states, seg_in, seg_grad};
   for (const void* p : ins)
-    if (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace)
+    if (p && (p == dq || p == dk_ || p == dv_ || p == dg || p == seg_dstate || p == workspace))
       return fail(GLA_ERR_INVALID_ARG, "%s: outputs and the workspace must not alias inputs", fn);
   const Schedule sch = workspace ? fitting_schedule(B, H, T, dk, dv, chunk, P, kern, 0, workspace_size)
                                  : Schedule{0, 0};
@@ -406,20 +523,24 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
                 workspace_layout(B, H, P, dk, dv, 1, 0).total, workspace ? workspace_size : (size_t)0);
   const Workspace lay = workspace_layout(B, H, P, dk, dv, S, sch.R);
   char* ws = static_cast<char*>(workspace);
-  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, seg_dstate,
-                 reinterpret_cast<int*>(ws + lay.flags), B * H, T, dk, dv, P, chunk, S, nullptr, nullptr, nullptr};
+  gla::BwdArgs a{q, k, v, g, do_, chunk_states, seg_in, dq, dk_, dv_, dg, from ? nullptr : seg_dstate,
+                 reinterpret_cast<int*>(ws + lay.flags), B * H, T, dk, dv, P, chunk, S, from ? seg_grad : nullptr,
+                 nullptr, nullptr};
+  a.from_in = from ? 1 : 0;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (S > 1) {
     // state-gradient pass over the sub-segments, then the reverse scan over them inside each
     // segment: the gradient w.r.t. the state leaving each sub-segment from the rest of its segment
-    // and, as its end value, the segment's gradient w.r.t. its incoming state
+    // (and from the later segments, seg_grad[p], with from) and, as its end value, the segment's
+    // gradient w.r.t. its incoming state
     a.sub_state = reinterpret_cast<float*>(ws + lay.sub_state);
     a.sub_ld = reinterpret_cast<float*>(ws + lay.sub_ld);
     float* carry = reinterpret_cast<float*>(ws + lay.carry);
+    a.init = nullptr;
     st = launched(fn, kern.bwd_state(&a, s));
     if (st != GLA_OK) return st;
-    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, nullptr, carry, seg_dstate, B * H * P, S, dk,
-                                               dv, 1, 1, s));
+    st = launched(fn, gla::launch_segment_scan(a.sub_state, a.sub_ld, seg_grad, carry, from ? nullptr : seg_dstate,
+                                               B * H * P, S, dk, dv, 1, 1, s));
     if (st != GLA_OK) return st;
     a.init = carry;
   }
@@ -440,13 +561,48 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
       st = launched(fn, kern.bwd_state(&a, s));
       if (st != GLA_OK) return st;
       st = launched(fn, gla::launch_resplit_scan(list, a.flags, a.r_state, a.r_ld, a.init, r_carry,
-                                                 S > 1 ? nullptr : seg_dstate, sch.R, dk, dv, 1, s));
+                                                 S > 1 || from ? nullptr : seg_dstate, sch.R, dk, dv, 1, s));
       if (st != GLA_OK) return st;
     }
   } else {
     a.flags = nullptr;  // every unit
   }
   return launched(fn, kern.bwd_exact(&a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* do_,
+                         const void* chunk_states, const float* seg_in, void* dq, void* dk_, void* dv_, float* dg,
+                         float* seg_dstate, int B, int H, int T, int dk, int dv, int chunk, int P, int dtype,
+                         void* workspace, size_t workspace_size, void* stream) {
+  return chunk_bwd_run(q, k, v, g, do_, chunk_states, seg_in, nullptr, dq, dk_, dv_, dg, seg_dstate, B, H, T, dk, dv,
+                       chunk, P, dtype, workspace, workspace_size, stream);
+}
+
+gla_status gla_chunk_state(const void* k, const void* v, const float* g, float* seg_state, float* seg_logdecay, int B,
+                           int H, int T, int dk, int dv, int chunk, int P, int dtype, void* workspace,
+                           size_t workspace_size, void* stream) {
+  return state_pass_run(GLA_FWD, nullptr, k, v, g, nullptr, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P, dtype,
+                        workspace, workspace_size, stream);
+}
+
+gla_status gla_chunk_dstate(const void* q, const float* g, const void* do_, float* seg_dstate, int B, int H, int T,
+                            int dk, int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
+                            void* stream) {
+  return state_pass_run(GLA_BWD, q, nullptr, nullptr, g, do_, seg_dstate, nullptr, B, H, T, dk, dv, chunk, P, dtype,
+                        workspace, workspace_size, stream);
+}
+
+gla_status gla_chunk_bwd_from(const void* q, const void* k, const void* v, const float* g, const void* do_,
+                              const void* chunk_states, const float* seg_in, const float* seg_grad, void* dq,
+                              void* dk_, void* dv_, float* dg, int B, int H, int T, int dk, int dv, int chunk, int P,
+                              int dtype, void* workspace, size_t workspace_size, void* stream) {
+  if (!seg_grad) return fail(GLA_ERR_INVALID_ARG, "gla_chunk_bwd_from: seg_grad must be non-null");
+  return chunk_bwd_run(q, k, v, g, do_, chunk_states, seg_in, seg_grad, dq, dk_, dv_, dg, nullptr, B, H, T, dk, dv,
+                       chunk, P, dtype, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

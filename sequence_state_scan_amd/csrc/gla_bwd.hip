@@ -9,7 +9,11 @@
 //   dg_t     = sum_{t <= t' in chunk n} (q dq - k dk)_t' + rowsum(S_n * U_n)
 // The last line is exact: over the segment's tokens after chunk n the running sum of
 // q dq - k dk equals rowsum(S_n * U_n) (the closed form of dg applied to that suffix), so no sum
-// ever runs over more than one chunk.
+// ever runs over more than one chunk.  The carry is formed inside the chunk, as
+// rowsum(S_{n-1} * exp(lam) U_n) + sum_s (k dk|U_n)_s with dk|U_n the U_n part of dk (the two
+// pieces of S_n = exp(lam) S_{n-1} + Ktil^T V), not from the stored S_n: the suffix sum subtracts
+// the same U_n terms again, so where the decay is strong (S_n made of the chunk's own last tokens)
+// they cancel to float32 rounding rather than to the stored state's rounding.
 //
 // A chunk in which some channel decays by more than kFastMinChunkLogDecay stops the unit: its flag
 // is set and the exact sub-block kernel (gla_exact.hip) recomputes the whole unit.
@@ -110,22 +114,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
   };
 
   f32x4 U[NJB];  // U[jb][i] = U[16cb + n16][16jb + 4g4 + i]
-  // carry into the current chunk: rowsum(S_n * U_n) for c = 16cb + 4g4 + i (nothing after the last chunk)
-  float cin[4] = {0.f, 0.f, 0.f, 0.f};
-  if (a.init && sub < NS - 1 && urole) {
-    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment), and its
-    // carry rowsum(S * U) with S the global state after the sub-segment's last chunk
-    const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
-    float part = 0.f;
+  if (a.init && (sub < NS - 1 || a.from_in) && urole) {
+    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment, or the
+    // global one with from_in)
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
+    for (int jb = 0; jb < NJB; ++jb)
       U[jb] = load4(a.init + (long)unit * SS + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4);
-      part += piece_dot(load_state_piece<E, NJB>(cst + (chunk0 + nchunks - 1) * SS, cb, jb, state_lane_row(n16, g4)),
-                        U[jb]);
-    }
-    part = sum_over_g4(part);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
   } else {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
@@ -275,12 +270,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
           }
         }
       }
-      // the carry into chunk n-1, rowsum(S_{n-1} * U_{n-1}) with U_{n-1} = exp(lam) U_n + Qbar^T dO, is
-      // rowsum(S_{n-1} * exp(lam) U_n) + sum_t Qbar[t] * (dO_t S_{n-1}^T): the second term uses the
-      // inter-chunk part of dq^T before the intra-chunk part is added
-      f32x4 qs = zero4();
+      // the carry into this chunk from the later tokens, rowsum(S_n * U_n), formed as
+      // rowsum(S_{n-1} * exp(lam) U_n) + sum_s k_s * dk_s|U_n (S_n = exp(lam) S_{n-1} + Ktil^T V): the
+      // second term from the same U-part of dk^T that dg subtracts again below, so that where the
+      // decay is strong the two cancel to float32 rounding, not to the stored state's
+      f32x4 ku = zero4();
 #pragma unroll
-      for (int tT = 0; tT < NTT; ++tT) qs += load4(sQ + (tT * 16 + n16) * LDQ + cb * 16 + 4 * g4) * aq[tT];
+      for (int tT = 0; tT < NTT; ++tT) ku += load4(sK + (tT * 16 + n16) * LDK + cb * 16 + 4 * g4) * ak[tT];
       // + sum_s Kbar^T[c][s] dA[t][s] (s <= t);  + sum_t Qbar^T[c][t] dA^T[s][t] (t >= s): the Kbar^T and
       // Qbar^T fragments of this wave's rows are read once per k step for all row blocks
 #pragma unroll
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
       // each row block (one DPP row: the lanes n16 of one g4), then over the later row blocks
       f32x4 later;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) later[i] = cin[i];
+      for (int i = 0; i < 4; ++i) later[i] = __shfl(part, (l & ~15) | (4 * g4 + i)) + row_sum16(ku[i]);
 #pragma unroll
       for (int tT = NTT - 1; tT >= 0; --tT) {
         f32x4 d;
@@ -339,9 +335,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
         }
         store4(dg + (t0 + tT * 16 + n16) * DK + cb * 16 + 4 * g4, d);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i)) + seg_last<16>(seg_scan_incl<16>(qs[i]));
     }
     __syncthreads();  // V and exp(b) are dead: the U staging area takes their place
     // ---- (4) dv = A^T dO + Kbar (exp(lam) U), half of d_v at a time; (5) U_{n-1} once the last half
@@ -412,8 +405,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
     }
   }
   // D = gradient w.r.t. the state entering the segment (from this segment's outputs); with
-  // sub-segments the reverse scan over them gives it
-  if (urole && NS == 1) {
+  // sub-segments the reverse scan over them gives it, with from_in the state-gradient pass
+  if (urole && NS == 1 && !a.from_in) {
     float* dst = a.seg_dstate + (long)unit * SS;
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
@@ -529,7 +522,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
     for (int jb = 0; jb < NJB; ++jb) store4(dst + (long)(cb * 16 + n16) * DV + jb * 16 + 4 * g4, U[jb]);
   }
   const int tid = threadIdx.x;
-  if (GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
+  if (up.ld && GT::active(tid) && GT::set_of(tid) == 0 && (tid & 15) == 0)
     store8(up.ld + 8 * GT::group_of(tid), ldsum);
 }
 

@@ -493,6 +493,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_zero_fill(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+// Sum of x over the 16 lanes of the DPP row, on every lane of the row (rotations by 8, 4, 2, 1).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return x;
+}
 template <int D> __device__ __forceinline__ float row_shr(float x) { return dpp_zero_fill<0x110 + D>(x); }
 template <int D> __device__ __forceinline__ float row_shl(float x) { return dpp_zero_fill<0x100 + D>(x); }
 

@@ -19,7 +19,8 @@
 //   dv = A^T dO + Ktil U
 //   U <- exp(lam) U + Qbar^T dO
 //   dg_t = sum_{t' >= t in the sub-block} (q dq - k dk)_t' + rowsum(S_after * U_after)
-// (the last line is the exact carry of the fast backward, at sub-block granularity).
+// (the last line is the exact carry of the fast backward, at sub-block granularity, formed the
+// same way: rowsum(S_before * exp(lam) U) + sum_s (k dk|U)_s).
 //
 // One workgroup of 8 waves per unit (b, h, segment); with flags non-null only the units whose
 // flag is 1 (set by the fast kernel) run.  With a re-split list, further workgroups serve the
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if (up.init && sub > 0 && vrole)  // the state entering the sub-segment
+      if (up.init && (sub > 0 || a.from_in) && vrole)  // the state entering the sub-segment
         S[jj][kb] = quad_transpose(load4(up.init + (long)(kb * 16 + 4 * g4 + (n16 & 3)) * DV +
                                          (w * JPW + jj) * 16 + (n16 & ~3)));
       else
@@ -339,8 +340,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_exact_kernel(FwdArgs a, int n_uni
       }
     }
   }
-  // ---- segment results: local end state (float32) and log cumulative decay ----
-  if (NS == 1) {
+  // ---- segment results: local end state (float32) and log cumulative decay (with from_in the
+  // state pass has given them) ----
+  if (a.from_in) {
+  } else if (NS == 1) {
     if (vrole) {
       float* st = a.seg_state + (long)unit * DK * DV;
 #pragma unroll
@@ -414,21 +417,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
   const bool urole = w < NCB;  // holds U rows 16w .. and the gate rows 4w .. 4w + 3
 
   f32x4 U[NJB];  // U[jb][i] = U[16w + n16][16jb + 4g4 + i]
-  f32x4 cin = zero4();  // rowsum(S_after * U_after) for c = 16w + 4g4 + i
-  if (up.init && sub < NS - 1 && urole) {
-    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment), and the
-    // carry rowsum(S * U) with S the global state after the sub-segment's last chunk
-    const int l = lane_id(), n16 = l & 15, g4 = l >> 4;
+  if (up.init && (sub < NS - 1 || a.from_in) && urole) {
+    // the gradient w.r.t. the state leaving the sub-segment (from the rest of its segment, or the
+    // global one with from_in)
+    const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) U[jb] = load4(up.init + (long)(16 * w + n16) * DV + jb * 16 + 4 * g4);
-    f32x4 Se[NJB];
-    load_state_rows<E, NJB>(cst + (chunk0 + nchunks - 1) * SS, w, Se);
-    float part = 0.f;
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) part += piece_dot(Se[jb], U[jb]);
-    part = sum_over_g4(part);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
   } else {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
@@ -604,11 +598,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
             Sf[jb] = mma_k16<E, true, true>(Sf[jb] * le, sV + i * kSB * LDV + jb * 16, LDV,
                                             sKt + i * kSB * LDQ + 16 * w, LDQ);
         }
+        // the carry into the sub-block from the later tokens, rowsum(S_after * U), formed as
+        // rowsum(S_j * exp(lam) U) + sum_s k_s * dk_s|U (S_after = exp(lam) S_j + Ktil^T V): the
+        // second term from the same U-part of dk that dg subtracts again, so that where the decay is
+        // strong the two cancel to float32 rounding, not to the rounding of S
+        float ps = 0.f;
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
+          ps += piece_dot(Sf[jb], U[jb]);
           if constexpr (sizeof(E) == 2) Sj[jb] = to_bf16x4(Sf[jb]);
           else Sj[jb] = Sf[jb];
         }
+        ps = sum_over_g4(ps) * sLamE[j][16 * w + n16];
         f32x4 aq = zero4(), ak = zero4();
         if constexpr (sizeof(E) == 2) {
 #pragma unroll
@@ -629,10 +630,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
         f32x4 dqv, dkv, dgv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const float du = __expf(x.lam[i] - x.b[i]) * ak[i];  // dk's U part
+          dgv[i] = __shfl(ps, (l & ~15) | (4 * g4 + i)) + row_sum16(x.k[i] * du);  // the carry
           dqv[i] = __expf(x.b[i]) * aq[i] + dqd[i];
-          dkv[i] = __expf(x.lam[i] - x.b[i]) * ak[i] + dkd[i];
-          dgv[i] = seg_scan_rev_incl<16>(x.q[i] * dqv[i] - x.k[i] * dkv[i]) + cin[i];
+          dkv[i] = du + dkd[i];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dgv[i] += seg_scan_rev_incl<16>(x.q[i] * dqv[i] - x.k[i] * dkv[i]);
         const long go = (ts0 + n16) * DK + 16 * w + 4 * g4;
         store4(dq + go, dqv);
         store4(dk + go, dkv);
@@ -650,26 +654,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_exact_kernel(BwdArgs a, int n_uni
         acc = mma<E, true, false>(acc, sU + jb * 16, LDU, sKt + j * kSB * LDQ, LDQ, 0, DK);
         store4(dv + (ts0 + n16) * DV + jb * 16 + 4 * g4, acc);
       }
-      // ---- U before the sub-block, and the carry rowsum(S_j * U) for the sub-block before ----
+      // ---- U before the sub-block ----
       if (urole) {
         const float le = sLamE[j][16 * w + n16];
-        float part = 0.f;
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
+        for (int jb = 0; jb < NJB; ++jb)
           U[jb] = mma_k16<E, true, true>(U[jb] * le, sdO + jb * 16, LDV, sQb + j * kSB * LDQ + 16 * w, LDQ);
-          part += piece_dot(Sj[jb], U[jb]);
-        }
-        part = sum_over_g4(part);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cin[i] = __shfl(part, (l & ~15) | (4 * g4 + i));
       }
       if (more) post_moderate(xn);  // every wave has read sMod for this sub-block before its first barrier
       __syncthreads();
     }
   }
   // D = gradient w.r.t. the state entering the segment (from this segment's outputs); with
-  // sub-segments the reverse scan over them gives it
-  if (urole && NS == 1) {
+  // sub-segments the reverse scan over them gives it, with from_in the state-gradient pass
+  if (urole && NS == 1 && !a.from_in) {
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
     float* dst = a.seg_dstate + (long)unit * SS;
 #pragma unroll

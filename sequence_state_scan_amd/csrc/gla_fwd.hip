@@ -86,9 +86,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
   };
 
   f32x4 S[JPW][NKB];  // S[jj][kb][i] = S[16kb + 4g4 + i][16jb + n16]
-  if (a.init && sub > 0 && w * JPW < NJB) {
-    // the state entering the sub-segment (from its segment's start), row-major float32: each lane
-    // reads 4 consecutive columns of a row and the quad transpose turns them into its rows
+  if (a.init && (sub > 0 || a.from_in) && w * JPW < NJB) {
+    // the state entering the sub-segment (from its segment's start, or the global one with
+    // from_in), row-major float32: each lane reads 4 consecutive columns of a row and the quad
+    // transpose turns them into its rows
     const float* ci = a.init + (long)unit * DK * DV;
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll
@@ -249,9 +250,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
     __syncthreads();
   }
 
-  // ---- segment results: local end state (float32) and log cumulative decay ----
+  // ---- segment results: local end state (float32) and log cumulative decay (with from_in the
+  // state pass has given them) ----
   const int tid = threadIdx.x;
-  if (NS == 1) {
+  if (a.from_in) {
+  } else if (NS == 1) {
     float* st = a.seg_state + (long)unit * DK * DV;
     const int n16 = lane_id() & 15, g4 = lane_id() >> 4;
 #pragma unroll

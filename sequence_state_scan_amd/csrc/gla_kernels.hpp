@@ -33,6 +33,11 @@ struct FwdArgs {  // gla_chunk_fwd
   int R, xmax;
   const float* r_init;
   float *r_state, *r_ld;
+  // from_in = 1: the segments' incoming states are known (the ordering that runs the state pass
+  // and the scan before the local pass).  init is then the GLOBAL state entering every unit, its
+  // segment's first sub-segment included, so outputs and chunk states come out global, and the
+  // segment-level outputs (seg_state, seg_logdecay) are neither needed nor written.
+  int from_in;
 };
 
 struct BwdArgs {  // gla_chunk_bwd
@@ -58,13 +63,19 @@ struct BwdArgs {  // gla_chunk_bwd
   int R, xmax;
   const float* r_init;
   float *r_state, *r_ld;
+  // from_in = 1: init is the GLOBAL gradient w.r.t. the state leaving every unit, its segment's
+  // last sub-segment included (the later segments' share), so dk, dv and dg come out global;
+  // seg_dstate is neither needed nor written.
+  int from_in;
 };
 
 // gla_chunk_fwd with the sub-segment split capped at max_split (0: no cap), the workspace already
-// checked to hold workspace_size bytes for that cap.
-gla_status chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, void* o, void* chunk_states,
-                            float* seg_state, float* seg_logdecay, int B, int H, int T, int dk, int dv, int chunk,
-                            int P, int dtype, void* workspace, size_t workspace_size, int max_split, void* stream);
+// checked to hold workspace_size bytes for that cap.  With seg_in non-null it is
+// gla_chunk_fwd_from: every segment starts from seg_in[p] (seg_state, seg_logdecay unused).
+gla_status chunk_fwd_capped(const void* q, const void* k, const void* v, const float* g, const float* seg_in, void* o,
+                            void* chunk_states, float* seg_state, float* seg_logdecay, int B, int H, int T, int dk,
+                            int dv, int chunk, int P, int dtype, void* workspace, size_t workspace_size,
+                            int max_split, void* stream);
 
 struct CorrArgs {  // gla_segment_correct
   const void *q, *k, *v;
@@ -123,6 +134,10 @@ hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay
 // starting from hb[u] (null: zero) and writing the end value to hout[u] (null: not written).
 hipError_t launch_resplit_scan(const int* list, int* flags, const float* r_state, const float* r_ld, const float* hb,
                                float* r_carry, float* hout, int R, int dk, int dv, int reverse, hipStream_t stream);
+
+// seg_ld[u][c] = sum over s < S of sub_ld[u][s][c]: a segment's summed log-gates from its
+// sub-segments', for n_units segments of dk channels.
+hipError_t launch_sum_logdecay(const float* sub_ld, float* seg_ld, int n_units, int S, int dk, hipStream_t stream);
 
 hipError_t launch_segment_scan_allgather(const float* seg_state, const float* seg_logdecay, const float* h_boundary,
                                          float* seg_carry, float* h_out, int BH, int P, int dk, int dv, int reverse,

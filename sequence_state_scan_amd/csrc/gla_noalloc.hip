@@ -63,6 +63,6 @@ extern "C" gla_status gla_chunk_fwd_noalloc(const void* q, const void* k, const 
   // the scratch holds the per-unit flags only: offered as a workspace of just that size (one int
   // per unit, rounded up to 256 bytes), the call cuts no sub-segments and re-splits no units
   const size_t flags_bytes = ((size_t)B * H * P * sizeof(int) + 255) / 256 * 256;
-  return gla::chunk_fwd_capped(q, k, v, g, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk, P, dtype,
-                               ws, flags_bytes, 1, stream);
+  return gla::chunk_fwd_capped(q, k, v, g, nullptr, o, chunk_states, seg_state, seg_logdecay, B, H, T, dk, dv, chunk,
+                               P, dtype, ws, flags_bytes, 1, stream);
 }

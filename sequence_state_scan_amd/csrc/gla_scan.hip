@@ -120,4 +120,23 @@ hipError_t launch_segment_scan(const float* seg_state, const float* seg_logdecay
   return hipGetLastError();
 }
 
+// A segment's summed log-gates from its S sub-segments' (in sub-segment order, as the local
+// kernels sum them): one lane per (segment, channel).
+__global__ __launch_bounds__(kThreads) void sum_logdecay_kernel(const float* __restrict__ sub_ld,
+                                                                float* __restrict__ seg_ld, long n, int S, int dk) {
+  const long i = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const long u = i / dk, c = i - u * dk;
+  float sum = 0.f;
+  for (int s = 0; s < S; ++s) sum += sub_ld[(u * S + s) * dk + c];
+  seg_ld[i] = sum;
+}
+
+hipError_t launch_sum_logdecay(const float* sub_ld, float* seg_ld, int n_units, int S, int dk, hipStream_t stream) {
+  const long n = (long)n_units * dk;
+  hipLaunchKernelGGL(sum_logdecay_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     sub_ld, seg_ld, n, S, dk);
+  return hipGetLastError();
+}
+
 }  // namespace gla

@@ -5,8 +5,13 @@ device memory (tensors) and the stream (torch's current stream on the tensors' d
 There is no CPU fallback: without the built library every call raises.
 
 Low-level calls carry the C names (gla_chunk_fwd, gla_segment_scan, gla_segment_correct,
-gla_chunk_bwd).  ``zeco_forward`` / ``zeco_backward`` chain them in the order of the method:
+gla_chunk_bwd, and for the other order gla_chunk_state, gla_chunk_fwd_from, gla_chunk_dstate,
+gla_chunk_bwd_from).  ``zeco_forward`` / ``zeco_backward`` chain them in the order of the method:
 local pass -> segment scan -> correction, and the same for the backward.
+``states_first_forward`` / ``states_first_backward`` chain the same decomposition with the
+segments' incoming states first: state pass -> segment scan -> local pass from the true incoming
+state, with no correction pass (cheaper where the decay is weak and the corrections would reach
+every chunk).
 """
 from __future__ import annotations
 
@@ -65,6 +70,14 @@ def load_library(path: str = LIB_PATH):
         lib.gla_segment_correct.restype = i
         lib.gla_chunk_bwd.argtypes = [vp, vp, vp, fp, vp, vp, fp, vp, vp, vp, fp, fp] + [i] * 8 + [vp, sz, vp]
         lib.gla_chunk_bwd.restype = i
+        lib.gla_chunk_state.argtypes = [vp, vp, fp, fp, fp] + [i] * 8 + [vp, sz, vp]
+        lib.gla_chunk_state.restype = i
+        lib.gla_chunk_fwd_from.argtypes = [vp, vp, vp, fp, fp, vp, vp] + [i] * 8 + [vp, sz, vp]
+        lib.gla_chunk_fwd_from.restype = i
+        lib.gla_chunk_dstate.argtypes = [vp, fp, vp, fp] + [i] * 8 + [vp, sz, vp]
+        lib.gla_chunk_dstate.restype = i
+        lib.gla_chunk_bwd_from.argtypes = [vp, vp, vp, fp, vp, vp, fp, fp, vp, vp, vp, fp] + [i] * 8 + [vp, sz, vp]
+        lib.gla_chunk_bwd_from.restype = i
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -358,6 +371,103 @@ def gla_chunk_bwd(q, k, v, g, do, chunk_states, seg_in, chunk: int, P: int, dq=N
     return dq, dk, dv, dg, seg_dstate
 
 
+def _seg_args(name_a, a, v, g, extra=()):
+    """(B, H, T, dk, dv) for the state passes, whose inputs are a ([B,H,T,dk]: k or q), v or do
+    ([B,H,T,dv]) and g, after checking them and ``extra``'s (name, tensor, last dim, dtype)."""
+    if not isinstance(a, torch.Tensor) or not isinstance(v, torch.Tensor) or a.dim() != 4 or v.dim() != 4:
+        raise ValueError("%s and the value-side input must be [B, H, T, d] tensors" % name_a)
+    B, H, T, dk = a.shape
+    dv = v.shape[-1]
+    if not a.is_cuda:
+        raise ValueError("libgla works on device tensors only (got a %s tensor)" % a.device)
+    _dtype_code(a.dtype)
+    _expect(a, name_a, (B, H, T, dk), a.dtype, a.device)
+    _expect(g, "g", (B, H, T, dk), torch.float32, a.device)
+    for name, t, d, dt in extra:
+        _expect(t, name, (B, H, T, d), dt, a.device)
+    return B, H, T, dk, dv
+
+
+def gla_chunk_state(k, v, g, chunk: int, P: int, seg_state=None, seg_logdecay=None, workspace=None):
+    """State pass: each segment's local end state and summed log-gates from a zero start (reads k,
+    v, g only).  Returns (seg_state [B,H,P,dk,dv], seg_logdecay [B,H,P,dk]), the same quantities as
+    gla_chunk_fwd's.  ``workspace`` (GLA_FWD size) lets it cut segments into sub-segments."""
+    B, H, T, dk, dv = _seg_args("k", k, v, g, (("v", v, v.shape[-1], k.dtype),))
+    _, st_shape, ld_shape = _seg_shapes(B, H, T, dk, dv, chunk, P)
+    dev, f32 = k.device, torch.float32
+    seg_state = torch.empty(st_shape, device=dev, dtype=f32) if seg_state is None else seg_state
+    seg_logdecay = torch.empty(ld_shape, device=dev, dtype=f32) if seg_logdecay is None else seg_logdecay
+    _expect(seg_state, "seg_state", st_shape, f32, dev)
+    _expect(seg_logdecay, "seg_logdecay", ld_shape, f32, dev)
+    ws, nbytes = _workspace(workspace, GLA_FWD, B, H, T, dk, dv, chunk, P, k.dtype, dev)
+    _check(load_library().gla_chunk_state(_p(k), _p(v), _p(g), _p(seg_state), _p(seg_logdecay), B, H, T, dk, dv,
+                                          chunk, P, _dtype_code(k.dtype), _p(ws), nbytes, _stream(k)))
+    return seg_state, seg_logdecay
+
+
+def gla_chunk_fwd_from(q, k, v, g, seg_in, chunk: int, P: int, o=None, chunk_states=None, workspace=None,
+                       keep_chunk_states: bool = True):
+    """Local pass with every segment starting from its true incoming state seg_in [B,H,P,dk,dv]
+    (the forward scan's carry): returns (o, chunk_states), both GLOBAL; no correction follows.
+    chunk_states (tiled layout) is None with keep_chunk_states=False."""
+    B, H, T, dk, dv = _head_args(q, k, v, g)
+    cs_shape, st_shape, _ = _seg_shapes(B, H, T, dk, dv, chunk, P)
+    dev = q.device
+    o = torch.empty_like(v) if o is None else o
+    if not keep_chunk_states:
+        if chunk_states is not None:
+            raise ValueError("chunk_states given with keep_chunk_states=False")
+    elif chunk_states is None:
+        chunk_states = torch.empty(cs_shape, device=dev, dtype=q.dtype)
+    _expect(seg_in, "seg_in", st_shape, torch.float32, dev)
+    _expect(o, "o", (B, H, T, dv), q.dtype, dev)
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev, optional=not keep_chunk_states)
+    ws, nbytes = _workspace(workspace, GLA_FWD, B, H, T, dk, dv, chunk, P, q.dtype, dev)
+    _check(load_library().gla_chunk_fwd_from(_p(q), _p(k), _p(v), _p(g), _p(seg_in), _p(o), _p(chunk_states), B, H,
+                                             T, dk, dv, chunk, P, _dtype_code(q.dtype), _p(ws), nbytes, _stream(q)))
+    return o, chunk_states
+
+
+def gla_chunk_dstate(q, g, do, chunk: int, P: int, seg_dstate=None, workspace=None):
+    """State-gradient pass: each segment's gradient w.r.t. its incoming state from its own outputs
+    (reads q, g, do only).  Returns seg_dstate [B,H,P,dk,dv], the same quantity as gla_chunk_bwd's.
+    ``workspace`` (GLA_BWD size) lets it cut segments into sub-segments."""
+    B, H, T, dk, dv = _seg_args("q", q, do, g, (("do", do, do.shape[-1], q.dtype),))
+    _, st_shape, _ = _seg_shapes(B, H, T, dk, dv, chunk, P)
+    dev = q.device
+    seg_dstate = torch.empty(st_shape, device=dev, dtype=torch.float32) if seg_dstate is None else seg_dstate
+    _expect(seg_dstate, "seg_dstate", st_shape, torch.float32, dev)
+    ws, nbytes = _workspace(workspace, GLA_BWD, B, H, T, dk, dv, chunk, P, q.dtype, dev)
+    _check(load_library().gla_chunk_dstate(_p(q), _p(g), _p(do), _p(seg_dstate), B, H, T, dk, dv, chunk, P,
+                                           _dtype_code(q.dtype), _p(ws), nbytes, _stream(q)))
+    return seg_dstate
+
+
+def gla_chunk_bwd_from(q, k, v, g, do, chunk_states, seg_in, seg_grad, chunk: int, P: int, dq=None, dk=None,
+                       dv=None, dg=None, workspace=None):
+    """Backward of every segment starting from seg_grad [B,H,P,dk,dv] (the reverse scan's carry)
+    at its end, given the global chunk states and incoming states: returns (dq, dk, dv, dg), all
+    GLOBAL; no correction follows."""
+    B, H, T, d_k, d_v = _head_args(q, k, v, g, (("do", do, v.shape[-1], q.dtype),))
+    cs_shape, st_shape, _ = _seg_shapes(B, H, T, d_k, d_v, chunk, P)
+    dev, f32 = q.device, torch.float32
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dg = torch.empty_like(g) if dg is None else dg
+    _expect(chunk_states, "chunk_states", cs_shape, q.dtype, dev)
+    _expect(seg_in, "seg_in", st_shape, f32, dev)
+    _expect(seg_grad, "seg_grad", st_shape, f32, dev)
+    for name, t, d in (("dq", dq, d_k), ("dk", dk, d_k), ("dv", dv, d_v)):
+        _expect(t, name, (B, H, T, d), q.dtype, dev)
+    _expect(dg, "dg", (B, H, T, d_k), f32, dev)
+    ws, nbytes = _workspace(workspace, GLA_BWD, B, H, T, d_k, d_v, chunk, P, q.dtype, dev)
+    _check(load_library().gla_chunk_bwd_from(_p(q), _p(k), _p(v), _p(g), _p(do), _p(chunk_states), _p(seg_in),
+                                             _p(seg_grad), _p(dq), _p(dk), _p(dv), _p(dg), B, H, T, d_k, d_v, chunk,
+                                             P, _dtype_code(q.dtype), _p(ws), nbytes, _stream(q)))
+    return dq, dk, dv, dg
+
+
 # ------------------------------------------------------------------------------ method chains
 
 def zeco_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain",
@@ -382,6 +492,29 @@ def zeco_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=Non
     seg_grad, dh0 = _scan(scan, seg_dstate, fwd["seg_logdecay"], K, dhT, True)
     gla_segment_correct(GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=fwd["seg_in"], seg_grad=seg_grad,
                         chunk_states=fwd["chunk_states"], dk=dk, dv=dv, dg=dg)
+    return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dh0": dh0, "seg_dstate": seg_dstate, "seg_grad": seg_grad}
+
+
+def states_first_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain",
+                         keep_chunk_states: bool = True):
+    """The same forward with the incoming states first: state pass -> forward segment scan ->
+    local pass from each segment's true incoming state (no correction).  Returns the dict
+    zeco_forward returns (o, chunk_states, seg_in, h_final, seg_state, seg_logdecay)."""
+    seg_state, seg_logdecay = gla_chunk_state(k, v, g, chunk, P)
+    seg_in, h_final = _scan(scan, seg_state, seg_logdecay, K, h0, False)
+    o, chunk_states = gla_chunk_fwd_from(q, k, v, g, seg_in, chunk, P, keep_chunk_states=keep_chunk_states)
+    return {"o": o, "chunk_states": chunk_states, "seg_in": seg_in, "h_final": h_final, "seg_state": seg_state,
+            "seg_logdecay": seg_logdecay}
+
+
+def states_first_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=None, scan: str = "chain"):
+    """The same backward with the incoming gradients first: state-gradient pass -> reverse segment
+    scan -> local backward from each segment's true outgoing gradient (no correction).  ``fwd`` is
+    the dict states_first_forward (or zeco_forward) returned.  Returns the dict zeco_backward
+    returns."""
+    seg_dstate = gla_chunk_dstate(q, g, do, chunk, P)
+    seg_grad, dh0 = _scan(scan, seg_dstate, fwd["seg_logdecay"], K, dhT, True)
+    dq, dk, dv, dg = gla_chunk_bwd_from(q, k, v, g, do, fwd["chunk_states"], fwd["seg_in"], seg_grad, chunk, P)
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dh0": dh0, "seg_dstate": seg_dstate, "seg_grad": seg_grad}
 
 

@@ -136,6 +136,57 @@ def test_chunk_bwd_host_checks(lib):
     assert ws_call(ctypes.c_void_p(0x1480), 256) == E  # the workspace aliases chunk_states
 
 
+def test_states_first_calls_host_checks(lib):
+    # the calls of the order with the incoming states first reject bad arguments the same way
+    E, U = gla.GLA_ERR_INVALID_ARG, gla.GLA_ERR_UNSUPPORTED
+    A = [ctypes.c_void_p(0x1000 + 0x100 * i) for i in range(16)]  # distinct stand-in pointers
+
+    def state(k=A[1], st=A[5], ld=A[6], T=256, P=2, chunk=64, dk=64, dtype=gla.GLA_BF16, ws=NUL, wsb=0):
+        return lib.gla_chunk_state(k, A[2], A[3], st, ld, 1, 1, T, dk, 64, chunk, P, dtype, ws, wsb, NUL)
+
+    assert state(k=NUL) == E
+    assert state(st=NUL) == E
+    assert state(ld=NUL) == E
+    assert state(st=A[1]) == E                 # the output aliases k
+    assert state(T=250) == E
+    assert state(T=0) == E
+    assert state(dk=48) == U
+    assert state(ws=A[2], wsb=1 << 20) == E    # the workspace aliases v
+    # bf16 chunk 16 has no state kernel of its own: segments of 48 tokens are not whole 32- or
+    # 64-token chunks, so there is no state pass for them
+    assert state(T=96, P=2, chunk=16) == U
+    assert b"state-pass" in lib.gla_last_error()
+
+    def dstate(q=A[0], out=A[7], T=256, P=2):
+        return lib.gla_chunk_dstate(q, A[3], A[4], out, 1, 1, T, 64, 64, 64, P, gla.GLA_BF16, NUL, 0, NUL)
+
+    assert dstate(q=NUL) == E
+    assert dstate(out=NUL) == E
+    assert dstate(out=A[4]) == E               # the output aliases do
+    assert dstate(P=3) == E
+
+    def fwd_from(seg_in=A[8], o=A[9], ws=WS, wsb=1 << 20):
+        return lib.gla_chunk_fwd_from(A[0], A[1], A[2], A[3], seg_in, o, A[10], 1, 1, 256, 64, 64, 64, 2,
+                                      gla.GLA_BF16, ws, wsb, NUL)
+
+    assert fwd_from(seg_in=NUL) == E
+    assert b"seg_in" in lib.gla_last_error()
+    assert fwd_from(o=NUL) == E
+    assert fwd_from(o=A[8]) == E               # o aliases seg_in
+    assert fwd_from(ws=NUL) == E               # the workspace is required, as for gla_chunk_fwd
+    assert fwd_from(wsb=8) == E
+
+    def bwd_from(seg_grad=A[11], dq=A[12], ws=WS, wsb=1 << 20):
+        return lib.gla_chunk_bwd_from(A[0], A[1], A[2], A[3], A[4], A[10], A[8], seg_grad, dq, A[13], A[14], A[15],
+                                      1, 1, 256, 64, 64, 64, 2, gla.GLA_BF16, ws, wsb, NUL)
+
+    assert bwd_from(seg_grad=NUL) == E
+    assert b"seg_grad" in lib.gla_last_error()
+    assert bwd_from(dq=NUL) == E
+    assert bwd_from(dq=A[11]) == E             # dq aliases seg_grad
+    assert bwd_from(ws=NUL) == E
+
+
 def _expected_workspace(B, H, T, dk, dv, C, P, fast=True):
     """The workspace rule of include/gla.h, written out: with fewer than 256 units (b, h, segment)
     each segment is cut into S sub-segments (S a power of two, at least 2 chunks each) until

@@ -494,6 +494,87 @@ def test_flagged_units_are_re_split(case):
         assert maxrel(gpu[k_], plain[k_]) < TOL[dtype] / 2, k_
 
 
+# -------------------------------------------------------- the order with the incoming states first
+
+SF_FWD_KEYS = ("S_local", "logdecay", "S_in", "h_final", "o", "cs")
+SF_BWD_KEYS = ("D_local", "G", "dh0", "dq", "dk", "dv", "dg")
+
+
+def states_first_pipeline(d, chunk, P, K, h0=None, dhT=None, ws=None):
+    """State pass -> scan -> local pass from each segment's true incoming state, and the same for
+    the backward, through the C ABI, keeping the intermediates (float64 numpy arrays)."""
+    q, k, v, g = d["q"], d["k"], d["v"], d["g"]
+    S_loc, ld = gla.gla_chunk_state(k, v, g, chunk, P, workspace=ws)
+    S_in, h_final = gla.gla_segment_scan(S_loc, ld, K, h_boundary=h0)
+    o, cs = gla.gla_chunk_fwd_from(q, k, v, g, S_in, chunk, P, workspace=ws)
+    res = {"S_local": S_loc, "logdecay": ld, "S_in": S_in, "h_final": h_final, "o": o,
+           "cs": gla.chunk_states_dense(cs)}
+    D = gla.gla_chunk_dstate(q, g, d["do"], chunk, P, workspace=ws)
+    G, dh0 = gla.gla_segment_scan(D, ld, K, h_boundary=dhT, reverse=True)
+    dq, dk, dv, dg = gla.gla_chunk_bwd_from(q, k, v, g, d["do"], cs, S_in, G, chunk, P, workspace=ws)
+    res.update(D_local=D, G=G, dh0=dh0, dq=dq, dk=dk, dv=dv, dg=dg)
+    torch.cuda.synchronize()
+    return {n: as_f64(t) for n, t in res.items()}
+
+
+SF_CASES = [
+    # dtype, B, H, T, dk, dv, chunk, P, K, gate
+    ("bf16", 1, 4, 16384, 64, 64, 64, 64, 8, "logsigmoid16"),   # 256 units, no sub-segments
+    ("bf16", 1, 2, 4096, 128, 256, 64, 4, 2, "logsigmoid16"),   # 8 units, each cut into 8 sub-segments
+    ("bf16", 2, 1, 8192, 64, 128, 32, 4, 4, "zero"),
+    ("bf16", 1, 2, 4096, 64, 128, 64, 4, 2, "strong5"),         # every unit on the exact kernels
+    ("bf16", 1, 2, 4096, 64, 128, 64, 4, 2, "mixed"),
+    ("bf16", 1, 2, 2048, 64, 128, 16, 4, 2, "logsigmoid16"),    # chunk 16: the state passes run in 64-token chunks
+    ("bf16", 1, 1, 960, 32, 32, 64, 3, 1, "weak"),              # 5 chunks a segment: no sub-segments
+    ("f32", 1, 2, 1024, 32, 32, 16, 4, 2, "strong"),
+    ("f32", 1, 1, 256, 16, 16, 16, 4, 2, "logsigmoid16"),       # the tiny configuration
+]
+
+
+@pytest.mark.parametrize("case", SF_CASES, ids=lambda c: "%s-T%d-dk%d-dv%d-C%d-P%d-%s" % (c[0], c[3], c[4], c[5],
+                                                                                          c[6], c[7], c[9]))
+def test_states_first_order_matches_oracle(case):
+    """gla_chunk_state -> gla_segment_scan -> gla_chunk_fwd_from and gla_chunk_dstate -> reverse scan
+    -> gla_chunk_bwd_from, with boundary states h0 and dL/dS_T: every intermediate and result
+    against the oracle's segmented form, and against the correction order on the same inputs."""
+    dtype, B, H, T, dk, dv, chunk, P, K, gate = case
+    d = inputs.generate(B, H, T, dk, dv, dtype, 41, True, gate)
+    rng = np.random.default_rng(141)
+    h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    x = dev(d)
+    gpu = states_first_pipeline(x, chunk, P, K, h0.cuda(), dhT.cuda())
+    ref = oracle_pipeline(d, chunk, P, True, h0.numpy(), dhT.numpy())
+    label = "states first %s B%d H%d T%d dk%d dv%d C%d P%d %s" % (dtype, B, H, T, dk, dv, chunk, P, gate)
+    check(gpu, ref, SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype], label)
+    zc = gpu_pipeline(x, chunk, P, K, True, h0.cuda(), dhT.cuda())
+    check(gpu, zc, SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype], label + " vs the correction order")
+
+
+def test_states_first_order_re_splits_flagged_units():
+    """Strong stretches in two of 256 units: the fast kernels flag them and the re-split redoes
+    them in pieces, each from its true incoming state, the segment's first piece from seg_in."""
+    B, H, T, dk, dv, chunk, P = 1, 4, 65536, 64, 64, 64, 64
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 29, True, "logsigmoid16")
+    g = d["g"].clone()
+    L = T // P
+    for u in (3, 200):
+        h, p = divmod(u, P)
+        t0 = p * L + L // 2 - 24
+        g[0, h, t0:t0 + 48, ::2] = -3.0
+    d["g"] = g
+    x = dev(d)
+    full = gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, chunk, P, x["q"].dtype)
+    list_at, total = _layout(B * H * P, dk, dv, 1, 256)
+    assert full == total
+    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    gpu = states_first_pipeline(x, chunk, P, 2, ws=ws)
+    lst = ws[list_at:list_at + 16].view(torch.int32).cpu().numpy()  # the backward's list
+    assert lst[0] == 2 and lst[1] == 8 and list(lst[2:]) == [3, 200], lst
+    ref = oracle_pipeline(d, chunk, P, True)
+    check(gpu, ref, SF_FWD_KEYS + SF_BWD_KEYS, TOL["bf16"], "states first, re-split")
+
+
 def test_state_carry_across_calls():
     # running the second half with h0 = the first half's final state equals one call
     d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 8, False, "weak")
