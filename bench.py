@@ -259,11 +259,13 @@ def compare_orderings(torch, gla, w, x, buf, stream, ms_chain, pc_chain):
     return res
 
 
-def path_buffers(torch, gla, w, dev, edt, bwd=True):
+def path_buffers(torch, gla, w, dev, edt, bwd=True, P=None):
     """Every output and intermediate of one fwd+bwd step, and the two calls' workspaces, allocated
     before anything is timed.  A forward-only workload keeps no per-chunk states (they exist for
-    the backward only)."""
-    B, H, T, dk, dv, C, P = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P
+    the backward only).  P: the segment count the per-segment buffers are sized for (default: the
+    workload's)."""
+    B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
+    P = w.P if P is None else P
     f32 = torch.float32
     st = (B, H, P, dk, dv)
     ws = max(gla.workspace_size(gla.GLA_FWD, B, H, T, dk, dv, C, P, edt),
@@ -277,7 +279,7 @@ def path_buffers(torch, gla, w, dev, edt, bwd=True):
         "dv": torch.empty((B, H, T, dv), device=dev, dtype=edt), "dg": torch.empty((B, H, T, dk), device=dev, dtype=f32),
         "D": torch.empty(st, device=dev, dtype=f32), "G": torch.empty(st, device=dev, dtype=f32),
         "dh0": torch.empty((B, H, dk, dv), device=dev, dtype=f32),
-        "ws": torch.empty(ws, device=dev, dtype=torch.uint8),
+        "ws": torch.empty(ws, device=dev, dtype=torch.uint8), "P": P,
     }
 
 
@@ -310,18 +312,39 @@ def path_calls(gla, w, x, buf, bwd=True):
     return calls
 
 
-def path_calls_states_first(gla, w, x, buf):
+def states_first_buffers(torch, gla, w, buf):
+    """buf with its per-segment buffers sized for the segment count of the order with the incoming
+    states first (gla.states_first_segments: the workload's segments cut to fill the chip)."""
+    P = gla.states_first_segments(w.B, w.H, w.T, w.chunk, w.P)
+    if P == buf["P"]:
+        return buf
+    out = dict(buf, P=P)
+    for n in ("S_loc", "S_in", "D", "G"):
+        out[n] = torch.empty((w.B, w.H, P, w.dk, w.dv), device=buf["o"].device, dtype=torch.float32)
+    out["ld"] = torch.empty((w.B, w.H, P, w.dk), device=buf["o"].device, dtype=torch.float32)
+    return out
+
+
+def path_calls_states_first(gla, w, x, buf, bwd=True):
     """The same step with the segments' incoming states first: state pass, scan, local pass from the
-    true incoming state (no correction), and the same for the backward."""
-    C, P, K = w.chunk, w.P, w.K
-    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
-    return [
+    true incoming state (no correction), and with bwd the same for the backward, over the
+    buffers' segment count (path_buffers with P = gla.states_first_segments(...): the segments cut
+    to fill the chip)."""
+    C, P, K = w.chunk, buf["P"], w.K
+    q, k, v, g = x["q"], x["k"], x["v"], x["g"]
+    calls = [
         ("gla_chunk_state", lambda: gla.gla_chunk_state(k, v, g, C, P, seg_state=buf["S_loc"], seg_logdecay=buf["ld"],
                                                          workspace=buf["ws"])),
         ("gla_segment_scan", lambda: gla.gla_segment_scan(buf["S_loc"], buf["ld"], K, seg_carry=buf["S_in"],
                                                            h_out=buf["h_fin"])),
         ("gla_chunk_fwd_from", lambda: gla.gla_chunk_fwd_from(q, k, v, g, buf["S_in"], C, P, o=buf["o"],
-                                                               chunk_states=buf["cs"], workspace=buf["ws"])),
+                                                               chunk_states=buf["cs"], workspace=buf["ws"],
+                                                               keep_chunk_states=buf["cs"] is not None)),
+    ]
+    if not bwd:
+        return calls
+    do = x["do"]
+    return calls + [
         ("gla_chunk_dstate", lambda: gla.gla_chunk_dstate(q, g, do, C, P, seg_dstate=buf["D"], workspace=buf["ws"])),
         ("gla_segment_scan(reverse)", lambda: gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True,
                                                                     seg_carry=buf["G"], h_out=buf["dh0"])),
@@ -378,7 +401,18 @@ def other_workloads(torch, gla, inputs, dev, stream, names, iters=50, warmup=5):
             "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},
         }
         log("%s: %.4f ms mean (%.4f median), %.3f of HBM peak" % (name, mean, med, out[name]["hbm_frac"]))
-        del x, buf, calls
+        # the same step with the incoming states first (no correction pass)
+        sbuf = states_first_buffers(torch, gla, w, buf)
+        mean, med, per_call = time_scrubbed(torch, path_calls_states_first(gla, w, x, sbuf, bwd=w.bwd), iters, warmup,
+                                            stream, scrub)
+        out[name]["states_first"] = {
+            "segments": sbuf["P"],
+            "tokens_per_s": round(w.B * w.T / (mean / 1e3), 1), "ms_mean": round(mean, 4), "ms_median": round(med, 4),
+            "hbm_frac": round(ab / (mean / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_call_ms": {k_: round(v_, 4) for k_, v_ in per_call.items()},
+        }
+        log("%s, states first: %.4f ms mean, %.3f of HBM peak" % (name, mean, out[name]["states_first"]["hbm_frac"]))
+        del x, buf, sbuf, calls
         torch.cuda.empty_cache()
     return out
 
@@ -434,7 +468,8 @@ def main():
 
     B, H, T, dk, dv, C, P, K = w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.P, w.K
     buf = path_buffers(torch, gla, w, dev, x["q"].dtype)
-    calls = path_calls(gla, w, x, buf) if args.order == "correction" else path_calls_states_first(gla, w, x, buf)
+    calls = (path_calls(gla, w, x, buf) if args.order == "correction" else
+             path_calls_states_first(gla, w, x, states_first_buffers(torch, gla, w, buf)))
     if args.streams > 1:
         sbuf = gla.zeco_step_streams(x["q"], x["k"], x["v"], x["g"], x["do"], C, P, K, args.streams)
         calls = [("zeco_step_streams(%d)" % args.streams,
@@ -489,7 +524,8 @@ def main():
         ms0, pc0, _ = time_steps(torch, path_calls(gla, w, x0, buf), 10, 3, stream)
         log("g = 0: %.4f ms per step" % ms0)
         # and in the order with the incoming states first, which has no correction pass to grow
-        ms0s, pc0s, _ = time_steps(torch, path_calls_states_first(gla, w, x0, buf), 10, 3, stream)
+        ms0s, pc0s, _ = time_steps(torch, path_calls_states_first(gla, w, x0, states_first_buffers(torch, gla, w, buf)),
+                                   10, 3, stream)
         del x0
         log("g = 0, states first: %.4f ms per step" % ms0s)
         extras = {"no_decay_step": {
@@ -500,7 +536,8 @@ def main():
                              "hbm_frac": round(step_bytes / (ms0s / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                              "per_call_ms": {k_: round(v_, 4) for k_, v_ in pc0s.items()}}}}
         # the headline step itself in that order (default gates)
-        mss, pcs, _ = time_steps(torch, path_calls_states_first(gla, w, x, buf), 10, 3, stream)
+        mss, pcs, _ = time_steps(torch, path_calls_states_first(gla, w, x, states_first_buffers(torch, gla, w, buf)),
+                                 10, 3, stream)
         log("states first: %.4f ms per step" % mss)
         extras["states_first_step"] = {"gate": args.gate, "ms_per_step": round(mss, 4),
                                        "tokens_per_s": round(tokens / (mss / 1e3), 1),

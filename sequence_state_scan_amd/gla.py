@@ -495,23 +495,42 @@ def zeco_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=Non
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dh0": dh0, "seg_dstate": seg_dstate, "seg_grad": seg_grad}
 
 
+def states_first_segments(B: int, H: int, T: int, chunk: int, P: int) -> int:
+    """The segment count the order with the incoming states first runs at: P, each segment cut in
+    two while the B*H*P' units leave CUs idle (fewer than 256) and the halves keep at least 2
+    chunks.  In this order nothing depends on the segmentation beyond rounding (there is no
+    correction whose work grows with it), and with P' segments no call cuts sub-segments of its
+    own, whose state pass would repeat gla_chunk_state's."""
+    if P < 1 or chunk < 1 or T % P or (T // P) % chunk:
+        raise ValueError("T=%d must split into P=%d segments of whole chunks of %d tokens" % (T, P, chunk))
+    n = T // P // chunk
+    while B * H * P < 256 and n % 2 == 0 and n // 2 >= 2:
+        P, n = 2 * P, n // 2
+    return P
+
+
 def states_first_forward(q, k, v, g, chunk: int, P: int, K: int, h0=None, scan: str = "chain",
-                         keep_chunk_states: bool = True):
+                         keep_chunk_states: bool = True, fill: bool = True):
     """The same forward with the incoming states first: state pass -> forward segment scan ->
-    local pass from each segment's true incoming state (no correction).  Returns the dict
-    zeco_forward returns (o, chunk_states, seg_in, h_final, seg_state, seg_logdecay)."""
+    local pass from each segment's true incoming state (no correction).  With fill, the segments
+    are first cut to fill the chip (states_first_segments); the per-segment results then count
+    those segments, whose number the dict holds as "P".  Returns the dict zeco_forward returns
+    (o, chunk_states, seg_in, h_final, seg_state, seg_logdecay) plus "P"."""
+    if fill:
+        P = states_first_segments(q.shape[0], q.shape[1], q.shape[2], chunk, P)
     seg_state, seg_logdecay = gla_chunk_state(k, v, g, chunk, P)
     seg_in, h_final = _scan(scan, seg_state, seg_logdecay, K, h0, False)
     o, chunk_states = gla_chunk_fwd_from(q, k, v, g, seg_in, chunk, P, keep_chunk_states=keep_chunk_states)
     return {"o": o, "chunk_states": chunk_states, "seg_in": seg_in, "h_final": h_final, "seg_state": seg_state,
-            "seg_logdecay": seg_logdecay}
+            "seg_logdecay": seg_logdecay, "P": P}
 
 
-def states_first_backward(q, k, v, g, do, fwd: dict, chunk: int, P: int, K: int, dhT=None, scan: str = "chain"):
+def states_first_backward(q, k, v, g, do, fwd: dict, chunk: int, K: int, dhT=None, scan: str = "chain"):
     """The same backward with the incoming gradients first: state-gradient pass -> reverse segment
-    scan -> local backward from each segment's true outgoing gradient (no correction).  ``fwd`` is
-    the dict states_first_forward (or zeco_forward) returned.  Returns the dict zeco_backward
+    scan -> local backward from each segment's true outgoing gradient (no correction), over the
+    segments of ``fwd``, the dict states_first_forward returned.  Returns the dict zeco_backward
     returns."""
+    P = fwd["P"]
     seg_dstate = gla_chunk_dstate(q, g, do, chunk, P)
     seg_grad, dh0 = _scan(scan, seg_dstate, fwd["seg_logdecay"], K, dhT, True)
     dq, dk, dv, dg = gla_chunk_bwd_from(q, k, v, g, do, fwd["chunk_states"], fwd["seg_in"], seg_grad, chunk, P)

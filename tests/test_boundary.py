@@ -187,6 +187,26 @@ def test_states_first_calls_host_checks(lib):
     assert bwd_from(ws=NUL) == E
 
 
+def test_states_first_segments():
+    # the order with the incoming states first cuts the segments in two until B*H*P' fills the chip
+    # (256 units) or a half would drop below 2 chunks
+    f = gla.states_first_segments
+    assert f(1, 4, 1 << 20, 64, 64) == 64          # 256 units already
+    assert f(1, 16, 16384, 64, 4) == 16            # 64 units -> 256
+    assert f(2, 4, 16384, 64, 1) == 32             # 8 units -> 256
+    assert f(1, 4, 32768, 64, 8) == 64             # 32 units -> 256
+    assert f(1, 1, 256, 16, 4) == 8                # stops at 2 chunks a segment
+    assert f(1, 1, 960, 64, 3) == 3                # 5 chunks a segment: no halving
+    assert f(4, 64, 4096, 64, 1) == 1
+    for B, H, T, C, P in [(1, 2, 4096, 64, 4), (1, 3, 6144, 32, 3), (2, 1, 8192, 16, 2), (1, 1, 64, 16, 1)]:
+        Pp = f(B, H, T, C, P)
+        assert Pp % P == 0 and (Pp // P) & (Pp // P - 1) == 0 and T % Pp == 0 and (T // Pp) % C == 0
+        n = T // Pp // C
+        assert B * H * Pp >= 256 or n % 2 == 1 or n // 2 < 2, (B, H, T, C, P, Pp)
+    with pytest.raises(ValueError):
+        f(1, 1, 250, 16, 4)
+
+
 def _expected_workspace(B, H, T, dk, dv, C, P, fast=True):
     """The workspace rule of include/gla.h, written out: with fewer than 256 units (b, h, segment)
     each segment is cut into S sub-segments (S a power of two, at least 2 chunks each) until

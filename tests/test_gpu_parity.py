@@ -575,6 +575,30 @@ def test_states_first_order_re_splits_flagged_units():
     check(gpu, ref, SF_FWD_KEYS + SF_BWD_KEYS, TOL["bf16"], "states first, re-split")
 
 
+def test_states_first_chain_fills_the_chip():
+    """gla.states_first_forward / states_first_backward cut the 8 units (2 segments of 4 heads) into
+    256 segments of 2 chunks, so that no call cuts sub-segments of its own: the results against the
+    plain recurrence, with boundary states."""
+    B, H, T, dk, dv, chunk, P = 1, 4, 32768, 64, 128, 64, 2
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 43, True, "logsigmoid16")
+    rng = np.random.default_rng(143)
+    h0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3
+    dhT = rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3
+    x = dev(d)
+    f = gla.states_first_forward(x["q"], x["k"], x["v"], x["g"], chunk, P, 4, h0=torch.from_numpy(h0).cuda())
+    assert f["P"] == 64 and f["seg_state"].shape[2] == 64
+    b = gla.states_first_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, chunk, 4,
+                                  dhT=torch.from_numpy(dhT).cuda())
+    torch.cuda.synchronize()
+    gpu = {"o": as_f64(f["o"]), "h_final": as_f64(f["h_final"])}
+    gpu.update({n: as_f64(b[n]) for n in ("dq", "dk", "dv", "dg", "dh0")})
+    a = {n: as_f64(t) for n, t in d.items()}
+    o, hT = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"], h0)
+    ref = {"o": o, "h_final": hT}
+    ref.update(oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"], h0, dhT))
+    check(gpu, ref, ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL["bf16"], "states-first chain, P' = 64")
+
+
 def test_state_carry_across_calls():
     # running the second half with h0 = the first half's final state equals one call
     d = inputs.generate(1, 2, 2048, 64, 64, "bf16", 8, False, "weak")
