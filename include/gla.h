@@ -273,16 +273,26 @@ gla_status gla_chunk_bwd(const void* q, const void* k, const void* v, const floa
  *   gla_chunk_state -> gla_segment_scan -> gla_chunk_fwd_from                        (forward)
  *   gla_chunk_dstate -> gla_segment_scan(reverse) -> gla_chunk_bwd_from             (backward)
  *
- * A state pass reads k, v, g (forward) or q, g, do (backward) once more, a fixed cost; the
- * corrections cost the chunks the incoming states reach, which depends on the decay.  The results
- * equal those of the correction order up to rounding; seg_state, seg_logdecay and seg_dstate
- * are the same quantities (local, from a zero state).
+ * A state pass reads k, v, g (forward) or q, g, do (backward) of the chunks whose share of the
+ * segment's end state (or of the gradient entering it) is not an exact float32 zero: it walks
+ * from the segment's far end and stops once every channel's summed log-gates are below -112
+ * (e^-112 underflows to 0.0f).  The corrections cost the chunks the incoming states reach; both
+ * depend on the decay in the same way.  The results equal those of the correction order up to
+ * rounding; seg_state, seg_logdecay and seg_dstate are the same quantities (local, from a zero
+ * state), except that a segment whose walk stopped early reports, for seg_logdecay, the sum over
+ * the chunks walked: every channel below -112, so its exponential is 0.0f like the full sum's.
  */
 
 /*
  * gla_chunk_state -- each segment's local end state and summed log-gates, computed from a zero
- * start (seg_state, seg_logdecay exactly as gla_chunk_fwd returns them, up to rounding), reading only
- * k, v and g: S <- diag(exp(lam)) S + Ktil^T V per chunk, the state update of the chunkwise form.
+ * start (seg_state as gla_chunk_fwd returns it, up to rounding), reading only k, v and g: the end
+ * state unrolled, S = sum_t exp(x_t) k_t v_t^T with x_t the log-gates after token t, summed chunk by
+ * chunk from the segment's end (the state update of the chunkwise form, S <- diag(exp(lam)) S +
+ * Ktil^T V, with the decays folded into the keys).  The walk stops once every channel's x is
+ * below -112: the earlier tokens' weights are then exact zeros.  seg_logdecay is the segment's
+ * summed log-gates where the walk reached the segment's start; where it stopped early it is the
+ * sum over the chunks walked, below -112 in every channel (the full sum is lower still, and both
+ * exponentials are 0.0f, which is all gla_segment_scan takes from it).
  * Inputs k, v (dtype), g (float32), [B][H][T][d]; outputs seg_state [B][H][P][dk][dv] and
  * seg_logdecay [B][H][P][dk], float32, fully overwritten.
  * workspace: optional (NULL, or gla_workspace_size(GLA_FWD, ...) bytes): with room, segments are cut
@@ -308,8 +318,10 @@ gla_status gla_chunk_fwd_from(const void* q, const void* k, const void* v, const
 
 /*
  * gla_chunk_dstate -- each segment's local state gradient D_p (seg_dstate exactly as gla_chunk_bwd
- * returns it, up to rounding): U <- diag(exp(lam)) U + Qbar^T dO walking the chunks back from a zero
- * gradient at the segment's end, reading only q, g and do.  Output seg_dstate float32
+ * returns it, up to rounding), reading only q, g and do: the gradient recursion U <- diag(exp(lam))
+ * U + Qbar^T dO unrolled, D = sum_t exp(a_t) q_t do_t^T with a_t the log-gates from the segment's
+ * start through token t, summed chunk by chunk from the segment's start; the walk stops once every
+ * channel's a is below -112 (the later tokens' weights are exact zeros).  Output seg_dstate float32
  * [B][H][P][dk][dv], fully overwritten.  The reverse scan takes it with gla_chunk_state's
  * seg_logdecay.  workspace and the bf16 chunk-16 rule as gla_chunk_state (GLA_BWD size).
  */

@@ -273,6 +273,7 @@ gla_status state_pass_run(int which, const void* q, const void* k, const void* v
     a.S = S;
     a.sub_state = sub_state;
     a.sub_ld = sub_ld;
+    a.reach = 1;  // from each sub-segment's end, as far as its decay reaches
     st = launched(fn, fwd_state(&a, s));
   } else {
     gla::BwdArgs a{};
@@ -288,6 +289,7 @@ gla_status state_pass_run(int which, const void* q, const void* k, const void* v
     a.S = S;
     a.sub_state = sub_state;
     a.sub_ld = S > 1 ? sub_ld : nullptr;  // the segments' log decays come from gla_chunk_state
+    a.reach = 1;                          // from each sub-segment's start, as far as its decay reaches
     st = launched(fn, bwd_state(&a, s));
   }
   if (st != GLA_OK || S == 1) return st;

@@ -419,6 +419,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a, int n_units) {
 // its chunks back, U_{n-1} = diag(exp(lam)) U_n + Qbar^T dO (Qbar = q exp(b)); the result is the
 // gradient w.r.t. the state entering the sub-segment from its own outputs.  Every factor is
 // exp(<= 0).  Wave w holds rows 16w .. of U, in bwd_kernel's lane layout.
+// With a.reach the same gradient is summed from the other side: the chunks from the first one on,
+// U += Qhat^T dO with Qhat_t = q_t exp(a_t), a_t the log-gates from the sub-segment's start
+// through token t (b_t plus the earlier chunks' totals), and no decay of U.  Once every channel's
+// running total is below kReachCut the later chunks' Qhat are exact zeros and the walk stops.
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
@@ -435,6 +439,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
 
   __shared__ int sList[NT / 64];
+  __shared__ int sLive[2 * NW];  // the reach walk's stop vote
   UnitPlace up;
   if (a.list) {  // the re-split: list the flagged units (workgroup 0 writes the list), then this piece
     int n, X;
@@ -459,10 +464,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
   f32x4 U[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
-  float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // the sub-segment's summed log-gates
+  // the summed log-gates of the chunks walked so far (every active lane, for its 8 channels)
+  float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // reach: walk from the first chunk, token t weighted by exp(log-gates from the start through t),
+  // no decay of U; stop once every channel is past kReachCut
+  const bool reach = a.reach && !a.list;
 
-  prefetch(nchunks - 1, threadIdx.x);
-  for (int n = nchunks - 1; n >= 0; --n) {
+  prefetch(reach ? 0 : nchunks - 1, threadIdx.x);
+  for (int it = 0; it < nchunks; ++it) {
+    const int n = reach ? it : nchunks - 1 - it;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15;
     Vec8<E> pd[VPT];
 #pragma unroll
@@ -475,22 +485,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
       pgt.prefix(tid, sTot, b, lam);
       if (GT::active(tid)) {
         const int x = GT::group_of(tid);
+        float before[8];  // log-gates before the chunk (reach), else 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e) before[e] = reach ? ldsum[e] : 0.f;
 #pragma unroll
         for (int r = 0; r < GT::RI; ++r) {
           float xq[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xq[e] = pgt.q[r].at(e) * __expf(b[r][e]);
+          for (int e = 0; e < 8; ++e) xq[e] = pgt.q[r].at(e) * __expf(b[r][e] + before[e]);
           store8(sQ + GT::row(tid, r) * LDQ + 8 * x, xq);
         }
-        if (GT::set_of(tid) == 0 && n16 == 0) {
+        if (!reach && GT::set_of(tid) == 0 && n16 == 0) {
           float el[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            el[e] = __expf(lam[e]);
-            ldsum[e] += lam[e];
-          }
+          for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
           store8(sLamE + 8 * x, el);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ldsum[e] += lam[e];
       }
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
@@ -499,13 +511,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (n > 0) prefetch(n - 1, tid);
+    if (it + 1 < nchunks) prefetch(reach ? n + 1 : n - 1, tid);
     __syncthreads();
     if (urole) {
-      // U^T[j][c] = exp(lam_c) U^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]
-      const float le = sLamE[cb * 16 + n16];
+      // U^T[j][c] = exp(lam_c) U^T[j][c] + sum_t dO^T[j][t] Qbar^T[c][t]  (reach: no decay, the
+      // weights are in Qbar)
+      if (!reach) {
+        const float le = sLamE[cb * 16 + n16];
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) U[jb] *= le;
+        for (int jb = 0; jb < NJB; ++jb) U[jb] *= le;
+      }
 #pragma unroll
       for (int ks = 0; ks < C / KS; ++ks) {
         const typename Mma<E>::frag fq = frag_ld<E, true>(sQ + cb * 16, LDQ, ks * KS);
@@ -513,7 +528,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
         for (int jb = 0; jb < NJB; ++jb) U[jb] = Mma<E>::mma(frag_ld<E, true>(sdO + jb * 16, LDV, ks * KS), fq, U[jb]);
       }
     }
-    __syncthreads();
+    if (reach) {
+      bool live = false;  // some channel of this lane's item still above the cut
+      if (GT::active(tid))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) live |= ldsum[e] >= kReachCut;
+      if (!barrier_any<NW>(sLive, it & 1, live)) break;
+    } else {
+      __syncthreads();
+    }
   }
   if (urole) {
     float* dst = up.st;

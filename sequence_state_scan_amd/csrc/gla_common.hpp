@@ -706,6 +706,29 @@ __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / 
 // --------------------------------------------------------------------------------------------
 constexpr float kFastMinChunkLogDecay = -40.f;
 
+// The reach of a segment's decay.  A token's share of a segment's end state (or of the gradient
+// entering it) carries the factor exp(x), x the summed log-gates between the token and the
+// segment's far end.  Below x = kReachCut both exp and __expf give exactly 0.0f in float32
+// (e^-112 ~ 2e-49, under the smallest subnormal), and with g <= 0 x only falls further along the
+// walk, so a state pass that walks from the far end may stop once every channel is past it: the
+// chunks it leaves out contribute exact zeros.
+constexpr float kReachCut = -112.f;
+
+// A workgroup-uniform OR of pred at a barrier: every wave writes its ballot to its slot of sLive
+// ([2][NW] ints, the half picked by parity), the barrier follows, and every lane reads the NW
+// slots.  Loops calling it once per iteration alternate parity: a slot is written again only two
+// barriers after it was read.
+template <int NW>
+__device__ __forceinline__ bool barrier_any(int* sLive, int parity, bool pred) {
+  const int wave = __ballot(pred) != 0;
+  if (lane_id() == 0) sLive[parity * NW + wave_id()] = wave;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) any |= sLive[parity * NW + i];
+  return any != 0;
+}
+
 // Broadcast lane S of each 16-lane row to the whole row (DPP row_newbcast).
 template <int S>
 __device__ __forceinline__ float row_bcast(float x) {

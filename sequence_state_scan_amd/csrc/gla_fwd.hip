@@ -283,6 +283,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_local_kernel(FwdArgs a, int n_uni
 // S = diag(exp(lam)) S + Ktil^T V per chunk (no outputs), and the sub-segment's summed log-gates.
 // Every factor is exp(<= 0), so no chunk needs the exact kernels here.  Layout and per-chunk
 // staging as in fwd_local_kernel; only k, g and v are read.
+// With a.reach the same end state is summed from the other side: the chunks from the last one
+// back, S += Khat^T V with Khat_t = k_t exp(x_t), x_t the log-gates after token t up to the
+// sub-segment's end (lam - b_t plus the later chunks' totals), and no decay of S.  Once every
+// channel's running total is below kReachCut the earlier chunks' Khat are exact zeros and the
+// walk stops; the log-gate output is then the total of the chunks walked, itself below the cut,
+// so that its exponential is the same 0.0f.
 template <typename E, int C, int DK, int DV, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_units) {
   constexpr int NT = NW * 64;
@@ -300,6 +306,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
   __shared__ __attribute__((aligned(16))) float sTot[GT::NSET * DK];
 
   __shared__ int sList[NT / 64];
+  __shared__ int sLive[2 * NW];  // the reach walk's stop vote
   UnitPlace up;
   if (a.list) {  // the re-split: list the flagged units (workgroup 0 writes the list), then this piece
     int n, X;
@@ -336,32 +343,39 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
   for (int jj = 0; jj < JPW; ++jj)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) S_[jj][kb] = zero4();
+  // the summed log-gates of the chunks walked so far (every active lane, for its 8 channels)
   float ldsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // reach: walk from the last chunk, token t weighted by exp(log-gates after t), no decay of S;
+  // stop once every channel is past kReachCut
+  const bool reach = a.reach && !a.list;
 
-  prefetch(0, threadIdx.x);
-  for (int n = 0; n < nchunks; ++n) {
+  prefetch(reach ? nchunks - 1 : 0, threadIdx.x);
+  for (int it = 0; it < nchunks; ++it) {
+    const int n = reach ? nchunks - 1 - it : it;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15, g4 = l >> 4;
     {
       float b[GT::RI][8], lam[8];
       pgt.prefix(tid, sTot, b, lam);
       if (GT::active(tid)) {
         const int x = GT::group_of(tid);
+        float after[8];  // log-gates after the chunk (reach), else 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e) after[e] = reach ? ldsum[e] : 0.f;
 #pragma unroll
         for (int r = 0; r < GT::RI; ++r) {
           float xkt[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xkt[e] = pgt.k[r].at(e) * __expf(lam[e] - b[r][e]);
+          for (int e = 0; e < 8; ++e) xkt[e] = pgt.k[r].at(e) * __expf(lam[e] - b[r][e] + after[e]);
           store8(sKt + GT::row(tid, r) * LDKT + 8 * x, xkt);
         }
-        if (GT::set_of(tid) == 0 && n16 == 0) {
+        if (!reach && GT::set_of(tid) == 0 && n16 == 0) {
           float el[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            el[e] = __expf(lam[e]);
-            ldsum[e] += lam[e];
-          }
+          for (int e = 0; e < 8; ++e) el[e] = __expf(lam[e]);
           store8(sLamE + 8 * x, el);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ldsum[e] += lam[e];
       }
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
@@ -370,25 +384,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_state_kernel(FwdArgs a, int n_uni
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (n + 1 < nchunks) prefetch(n + 1, tid);
+    if (it + 1 < nchunks) prefetch(reach ? n - 1 : n + 1, tid);
     __syncthreads();
     if (w * JPW < NJB) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 lamE = load4(sLamE + kb * 16 + 4 * g4);
         frag fk[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) fk[ks] = frag_ld<E, true>(sKt + kb * 16, LDKT, ks * KS);
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
-          S_[jj][kb] *= lamE;
+          if (!reach) S_[jj][kb] *= load4(sLamE + kb * 16 + 4 * g4);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
             S_[jj][kb] = Mma<E>::mma(fk[ks], frag_ld<E, true>(sV + (w * JPW + jj) * 16, LDV, ks * KS), S_[jj][kb]);
         }
       }
     }
-    __syncthreads();
+    if (reach) {
+      bool live = false;  // some channel of this lane's item still above the cut
+      if (GT::active(tid))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) live |= ldsum[e] >= kReachCut;
+      if (!barrier_any<NW>(sLive, it & 1, live)) break;
+    } else {
+      __syncthreads();
+    }
   }
   float* st = up.st;
   const int n16 = lane_id() & 15, g4 = lane_id() >> 4;

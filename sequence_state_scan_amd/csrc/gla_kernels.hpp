@@ -38,6 +38,10 @@ struct FwdArgs {  // gla_chunk_fwd
   // segment's first sub-segment included, so outputs and chunk states come out global, and the
   // segment-level outputs (seg_state, seg_logdecay) are neither needed nor written.
   int from_in;
+  // reach = 1 (the state pass only, not with list): walk each sub-segment from its last chunk,
+  // weighting token t by exp(summed log-gates after t), and stop once every channel's summed
+  // log-gates are below kReachCut; sub_ld then holds the sum over the chunks walked.
+  int reach;
 };
 
 struct BwdArgs {  // gla_chunk_bwd
@@ -67,6 +71,11 @@ struct BwdArgs {  // gla_chunk_bwd
   // last sub-segment included (the later segments' share), so dk, dv and dg come out global;
   // seg_dstate is neither needed nor written.
   int from_in;
+  // reach = 1 (the state-gradient pass only, not with list): walk each sub-segment from its first
+  // chunk, weighting token t by exp(summed log-gates from the sub-segment's start through t), and
+  // stop once every channel's sum is below kReachCut; sub_ld then holds the sum over the chunks
+  // walked.
+  int reach;
 };
 
 // gla_chunk_fwd with the sub-segment split capped at max_split (0: no cap), the workspace already

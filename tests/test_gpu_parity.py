@@ -498,6 +498,16 @@ def test_flagged_units_are_re_split(case):
 
 SF_FWD_KEYS = ("S_local", "logdecay", "S_in", "h_final", "o", "cs")
 SF_BWD_KEYS = ("D_local", "G", "dh0", "dq", "dk", "dv", "dg")
+REACH_CUT = -112.0  # below it exp gives 0.0f: the state passes stop once every channel is past it
+
+
+def reach_clamped(res):
+    """The states-first state pass stops once every channel's summed log-gates are below the cut
+    and then reports the sum over the chunks it walked; past the cut only the (zero) exponential
+    is defined, so log-decays are compared clamped at the cut."""
+    out = dict(res)
+    out["logdecay"] = np.maximum(res["logdecay"], REACH_CUT)
+    return out
 
 
 def states_first_pipeline(d, chunk, P, K, h0=None, dhT=None, ws=None):
@@ -546,9 +556,37 @@ def test_states_first_order_matches_oracle(case):
     gpu = states_first_pipeline(x, chunk, P, K, h0.cuda(), dhT.cuda())
     ref = oracle_pipeline(d, chunk, P, True, h0.numpy(), dhT.numpy())
     label = "states first %s B%d H%d T%d dk%d dv%d C%d P%d %s" % (dtype, B, H, T, dk, dv, chunk, P, gate)
-    check(gpu, ref, SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype], label)
+    check(reach_clamped(gpu), reach_clamped(ref), SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype], label)
     zc = gpu_pipeline(x, chunk, P, K, True, h0.cuda(), dhT.cuda())
-    check(gpu, zc, SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype], label + " vs the correction order")
+    check(reach_clamped(gpu), reach_clamped(zc), SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype],
+          label + " vs the correction order")
+
+
+@pytest.mark.parametrize("gate", ["logsigmoid16", "mixed", "strong5", "weak"])
+def test_state_passes_stop_where_the_decay_ends(gate):
+    """Segments of 128 chunks with only the flags as workspace (no sub-segments): the state passes
+    walk from the far end and stop once every channel is past the cut.  The states and gradients
+    must still match the oracle; where the oracle's log-decay is far below the cut the reported
+    one is the partial sum, between the cut and the full sum (so the walk did stop early); where
+    the walk reached the segment's start it is the full sum."""
+    B, H, T, dk, dv, chunk, P = 1, 2, 16384, 64, 128, 64, 2
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 47, True, gate)
+    rng = np.random.default_rng(147)
+    h0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3
+    dhT = rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3
+    x = dev(d)
+    ws = torch.zeros(gla.flags_workspace_size(B, H, P), dtype=torch.uint8, device="cuda")
+    gpu = states_first_pipeline(x, chunk, P, 2, torch.from_numpy(h0).cuda(), torch.from_numpy(dhT).cuda(), ws=ws)
+    ref = oracle_pipeline(d, chunk, P, True, h0, dhT)
+    check(reach_clamped(gpu), reach_clamped(ref), SF_FWD_KEYS + SF_BWD_KEYS, TOL["bf16"], "reach %s" % gate)
+    ld, ld_ref = gpu["logdecay"], ref["logdecay"]
+    full = (ld >= REACH_CUT).any(axis=-1)  # segments whose walk reached the start: every sum complete
+    assert np.allclose(ld[full], ld_ref[full], rtol=1e-5, atol=1e-3)
+    if gate in ("logsigmoid16", "strong5"):  # every channel decays past the cut (mixed: only half)
+        far = ld_ref < 2 * REACH_CUT
+        assert far.all(axis=-1).any(), "this gate should decay past the cut within a segment"
+        assert (ld[~full] < REACH_CUT).all() and (ld[~full] >= ld_ref[~full] - 1e-3).all()
+        assert (ld[far & ~full[..., None]] > ld_ref[far & ~full[..., None]] + 1.0).any(), "the walk never stopped"
 
 
 def test_states_first_order_re_splits_flagged_units():
@@ -572,7 +610,7 @@ def test_states_first_order_re_splits_flagged_units():
     lst = ws[list_at:list_at + 16].view(torch.int32).cpu().numpy()  # the backward's list
     assert lst[0] == 2 and lst[1] == 8 and list(lst[2:]) == [3, 200], lst
     ref = oracle_pipeline(d, chunk, P, True)
-    check(gpu, ref, SF_FWD_KEYS + SF_BWD_KEYS, TOL["bf16"], "states first, re-split")
+    check(reach_clamped(gpu), reach_clamped(ref), SF_FWD_KEYS + SF_BWD_KEYS, TOL["bf16"], "states first, re-split")
 
 
 def test_states_first_chain_fills_the_chip():
