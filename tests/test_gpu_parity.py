@@ -672,10 +672,12 @@ def test_gradient_carry_across_calls():
 
 def test_headline_workload_at_full_size():
     """64 segments of 16384 tokens, 4 heads, fwd+bwd, in the launch configuration the benchmark
-    times.  The oracle runs head 0 in full, forward and backward over all 1M tokens, and every
-    output and gradient of that head is compared element by element on every segment; G[61] is
-    checked against the oracle's backward over the last two segments.  The homogeneity identity
-    sum<dq,q> = sum<dk,k> = sum<dv,v> = sum<do,o> is checked on every head."""
+    times, in both orders (the correction order, and the incoming states first with its state
+    passes stopping where the decay ends).  The oracle runs head 0 in full, forward and backward
+    over all 1M tokens, and every output and gradient of that head is compared element by element
+    on every segment, for both orders; G[61] is checked against the oracle's backward over the last
+    two segments.  The homogeneity identity sum<dq,q> = sum<dk,k> = sum<dv,v> = sum<do,o> is
+    checked on every head, and the two orders agree on every head."""
     w = inputs.WORKLOADS[inputs.HEADLINE]
     t = time.time()
     d = inputs.generate_workload(w)
@@ -684,8 +686,19 @@ def test_headline_workload_at_full_size():
     del d
     f = gla.zeco_forward(x["q"], x["k"], x["v"], x["g"], w.chunk, w.P, w.K)
     b = gla.zeco_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, w.chunk, w.P, w.K)
+    sf = gla.states_first_forward(x["q"], x["k"], x["v"], x["g"], w.chunk, w.P, w.K)
+    sb = gla.states_first_backward(x["q"], x["k"], x["v"], x["g"], x["do"], sf, w.chunk, w.K)
     torch.cuda.synchronize()
-    say("gpu fwd+bwd done")
+    assert sf["P"] == w.P
+    say("gpu fwd+bwd done, both orders")
+    both = {}
+    for n, a_, b_ in (("o", sf["o"], f["o"]), ("h_final", sf["h_final"], f["h_final"]),
+                      ("S_in", sf["seg_in"], f["seg_in"]), ("G", sb["seg_grad"], b["seg_grad"]),
+                      ("dh0", sb["dh0"], b["dh0"]), ("dq", sb["dq"], b["dq"]), ("dk", sb["dk"], b["dk"]),
+                      ("dv", sb["dv"], b["dv"]), ("dg", sb["dg"], b["dg"])):
+        both[n] = float((a_.float() - b_.float()).abs().max() / b_.float().abs().max())
+    say("states first against the correction order, every head: " + " ".join("%s=%.2e" % kv for kv in both.items()))
+    assert max(both.values()) <= TOL["bf16"], both
     # homogeneity on every (b, h)
     ref = (x["do"].double() * f["o"].double()).sum(dim=(2, 3))
     for xn, dn in (("q", "dq"), ("k", "dk"), ("v", "dv")):
@@ -710,24 +723,29 @@ def test_headline_workload_at_full_size():
         el[name] = elemrel(got, r)
 
     cmp("o", as_f64(f["o"][:1, :1]), o_ref)
+    cmp("o (states first)", as_f64(sf["o"][:1, :1]), o_ref)
     del o_ref
     cmp("h_final", as_f64(f["h_final"][:1, :1]), hT)
     cmp("S_in[62]", as_f64(f["seg_in"][:1, :1, w.P - 2]), S62)
+    cmp("S_in[62] (states first)", as_f64(sf["seg_in"][:1, :1, w.P - 2]), S62)
     t = time.time()
     gb = oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"])
     say("oracle backward over %d tokens: %.1fs" % (w.T, time.time() - t))
     for n in ("dq", "dk", "dv", "dg"):
-        got = as_f64(b[n][:1, :1])
-        cmp(n, got, gb[n])
-        # and segment by segment, so that no segment's error hides behind a larger one elsewhere
-        seg = max(maxrel(got[:, :, p * L:(p + 1) * L], gb[n][:, :, p * L:(p + 1) * L]) for p in range(w.P))
-        errs[n + "[worst segment]"] = seg
-        del got
+        for tag, res in (("", b), (" (states first)", sb)):
+            got = as_f64(res[n][:1, :1])
+            cmp(n + tag, got, gb[n])
+            # and segment by segment, so that no segment's error hides behind a larger one elsewhere
+            seg = max(maxrel(got[:, :, p * L:(p + 1) * L], gb[n][:, :, p * L:(p + 1) * L]) for p in range(w.P))
+            errs[n + tag + "[worst segment]"] = seg
+            del got
     cmp("dh0", as_f64(b["dh0"][:1, :1]), gb["dh0"])
+    cmp("dh0 (states first)", as_f64(sb["dh0"][:1, :1]), gb["dh0"])
     del gb
     gb2 = oracle.gla_bwd(a["q"][:, :, t62:], a["k"][:, :, t62:], a["v"][:, :, t62:], a["g"][:, :, t62:],
                          a["do"][:, :, t62:], S62)
     cmp("G[61]", as_f64(b["seg_grad"][:1, :1, w.P - 3]), gb2["dh0"])
+    cmp("G[61] (states first)", as_f64(sb["seg_grad"][:1, :1, w.P - 3]), gb2["dh0"])
     say("headline workload, head 0, every token: " +
         " ".join("%s=%.2e" % kv for kv in errs.items()) + " | element-wise: " +
         " ".join("%s=%.1e" % kv for kv in el.items()))
