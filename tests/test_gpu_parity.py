@@ -788,6 +788,15 @@ def test_the_whole_path_replays_in_a_hip_graph(strong):
         gla.gla_segment_correct(gla.GLA_BWD, chunk, P, k=k, v=v, g=g, seg_in=buf["S_in"], seg_grad=buf["G"],
                                 chunk_states=buf["cs"], dk=buf["dk"], dv=buf["dv"], dg=buf["dg"])
 
+    _replays_bit_for_bit(path, buf)
+    check({n: as_f64(buf[n]) for n in ("o", "dq", "dk", "dv", "dg")},
+          oracle_pipeline(d, chunk, P, True), ("o", "dq", "dk", "dv", "dg"), TOL["bf16"], "graph replay")
+
+
+def _replays_bit_for_bit(path, buf):
+    """Run path eagerly, record it into a HIP graph (after a warm-up on the capture's stream) and
+    replay it three times with eager work and synchronisations in between: every replay must
+    reproduce the eager run's buffers bit for bit."""
     path()
     torch.cuda.synchronize()
     ref = {n: t.clone() for n, t in buf.items()}
@@ -809,8 +818,43 @@ def test_the_whole_path_replays_in_a_hip_graph(strong):
         torch.cuda.synchronize()
         for n, t in ref.items():
             assert torch.equal(buf[n], t), (r, n)
-    check({n: as_f64(buf[n]) for n in ("o", "dq", "dk", "dv", "dg")},
-          oracle_pipeline(d, chunk, P, True), ("o", "dq", "dk", "dv", "dg"), TOL["bf16"], "graph replay")
+
+
+def test_the_states_first_path_replays_in_a_hip_graph():
+    """The order with the incoming states first recorded into one HIP graph: its state passes (cut
+    into sub-segments here, each walking from its far end and stopping where the decay ends), the
+    scans and the two local passes from the true incoming states; every replay equals the eager run
+    bit for bit, and the results match the oracle."""
+    B, H, T, dk, dv, chunk, P, K = 1, 16, 65536, 64, 64, 64, 8, 2
+    d = inputs.generate(B, H, T, dk, dv, "bf16", 37, True, "logsigmoid16")
+    x = dev(d)
+    ws = torch.empty(gla.workspace_size(gla.GLA_BWD, B, H, T, dk, dv, chunk, P, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    f32 = dict(device="cuda", dtype=torch.float32)
+    buf = {"o": torch.empty_like(x["v"]), "cs": torch.empty((B, H, T // chunk, dk, dv), device="cuda",
+                                                             dtype=torch.bfloat16),
+           "S": torch.empty((B, H, P, dk, dv), **f32), "ld": torch.empty((B, H, P, dk), **f32),
+           "S_in": torch.empty((B, H, P, dk, dv), **f32), "h": torch.empty((B, H, dk, dv), **f32),
+           "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+           "dg": torch.empty_like(x["g"]), "D": torch.empty((B, H, P, dk, dv), **f32),
+           "G": torch.empty((B, H, P, dk, dv), **f32), "dh0": torch.empty((B, H, dk, dv), **f32)}
+    q, k, v, g, do = x["q"], x["k"], x["v"], x["g"], x["do"]
+
+    def path():
+        gla.gla_chunk_state(k, v, g, chunk, P, seg_state=buf["S"], seg_logdecay=buf["ld"], workspace=ws)
+        gla.gla_segment_scan(buf["S"], buf["ld"], K, seg_carry=buf["S_in"], h_out=buf["h"])
+        gla.gla_chunk_fwd_from(q, k, v, g, buf["S_in"], chunk, P, o=buf["o"], chunk_states=buf["cs"], workspace=ws)
+        gla.gla_chunk_dstate(q, g, do, chunk, P, seg_dstate=buf["D"], workspace=ws)
+        gla.gla_segment_scan(buf["D"], buf["ld"], K, reverse=True, seg_carry=buf["G"], h_out=buf["dh0"])
+        gla.gla_chunk_bwd_from(q, k, v, g, do, buf["cs"], buf["S_in"], buf["G"], chunk, P, dq=buf["dq"],
+                               dk=buf["dk"], dv=buf["dv"], dg=buf["dg"], workspace=ws)
+
+    _replays_bit_for_bit(path, buf)
+    keys = ("o", "h", "dq", "dk", "dv", "dg", "dh0")
+    gpu = {n: as_f64(buf[n]) for n in keys}
+    ref = oracle_pipeline(d, chunk, P, True)
+    ref["h"] = ref["h_final"]
+    check(gpu, ref, keys, TOL["bf16"], "states-first graph replay")
 
 
 def test_element_offsets_beyond_two_to_the_31():

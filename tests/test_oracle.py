@@ -280,3 +280,38 @@ def test_chunk_states_local_and_corrected(P, C):
         p0 = (t1 - 1) // L * L  # first token of this chunk's segment
         _, loc = oracle.gla_fwd(c["q"][:, :, p0:t1], c["k"][:, :, p0:t1], c["v"][:, :, p0:t1], c["g"][:, :, p0:t1])
         assert _rel(z["chunk_states_local"][:, :, n], loc) < 1e-12
+
+
+# ------------------------------------------------------- the state passes' unrolled weighted sums
+
+@pytest.mark.parametrize("gscale", [0.05, 3.0])
+def test_segment_state_and_gradient_are_unrolled_weighted_sums(gscale):
+    """The oracle's per-segment local state and state gradient against the recurrence unrolled:
+    from S_t = diag(e^{g_t}) S_{t-1} + k_t v_t^T and a zero start, a segment's end state is
+    sum_t exp(x_t) k_t v_t^T with x_t the log-gates after t in the segment, and the gradient
+    w.r.t. the state entering it from its own outputs (o_t = S_t^T q_t) is sum_t exp(a_t) q_t do_t^T
+    with a_t the log-gates from the segment's start through t.  These are the sums the state
+    passes add chunk by chunk from the far end.  With strong decay (gscale 3: about -2.4 per token)
+    the tokens whose weight is below e^-112 in every channel, which the passes leave out, move
+    neither sum by more than 1e-40 of its size."""
+    P, T = 2, 256
+    c = _case(1, 2, T, 4, 3, seed=77, gscale=gscale, with_do=True)
+    z = oracle.zeco_fwd(c["q"], c["k"], c["v"], c["g"], P)
+    b = oracle.zeco_bwd(c["q"], c["k"], c["v"], c["g"], c["do"], P, z["S_in"], z["logdecay"])
+    L = T // P
+    for p in range(P):
+        q, k, v, g, do = (c[n][:, :, p * L:(p + 1) * L] for n in ("q", "k", "v", "g", "do"))
+        after = np.cumsum(g[:, :, ::-1], axis=2)[:, :, ::-1] - g  # sum over tau > t
+        through = np.cumsum(g, axis=2)                              # sum over tau <= t
+        S = np.einsum("bhtc,bhtj->bhcj", k * np.exp(after), v)
+        D = np.einsum("bhtc,bhtj->bhcj", q * np.exp(through), do)
+        assert _rel(z["S_local"][:, :, p], S) < 1e-12
+        assert _rel(b["D_local"][:, :, p], D) < 1e-12
+        assert np.allclose(z["logdecay"][:, :, p], g.sum(axis=2), rtol=1e-12, atol=1e-12)
+        keep_s = (after >= -112).any(axis=3, keepdims=True)   # [B, H, L, 1]: some channel above the cut
+        keep_d = (through >= -112).any(axis=3, keepdims=True)
+        S_cut = np.einsum("bhtc,bhtj->bhcj", k * np.exp(after) * keep_s, v)
+        D_cut = np.einsum("bhtc,bhtj->bhcj", q * np.exp(through) * keep_d, do)
+        assert _rel(S_cut, S) <= 1e-40 and _rel(D_cut, D) <= 1e-40
+        if gscale > 1:  # the cut is reached inside the segment, from both ends
+            assert not keep_s.all() and not keep_d.all()
