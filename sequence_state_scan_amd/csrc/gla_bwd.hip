@@ -460,7 +460,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
   const bool urole = cb < NCB;
 
   GT pgt;
-  auto prefetch = [&](int n, int tid) { pgt.load(a.g, q, nullptr, (tok0 + (long)n * C) * DK, tid); };
+  Vec8<E> pd[VPT];  // dO of the next chunk, requested with its gate tile
+  auto prefetch = [&](int n, int tid) {
+    pgt.load(a.g, q, nullptr, (tok0 + (long)n * C) * DK, tid);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + NT * i;
+      if (NVP % NT == 0 || pc < NVP) pd[i].load(dO + (tok0 + (long)n * C + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
+    }
+  };
   f32x4 U[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) U[jb] = zero4();
@@ -474,12 +482,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_state_kernel(BwdArgs a, int n_uni
   for (int it = 0; it < nchunks; ++it) {
     const int n = reach ? it : nchunks - 1 - it;
     const int tid = fresh_tid(), l = tid & 63, n16 = l & 15;
-    Vec8<E> pd[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int pc = tid + NT * i;
-      if (NVP % NT == 0 || pc < NVP) pd[i].load(dO + (tok0 + (long)n * C + pc / (DV / 8)) * DV + (pc % (DV / 8)) * 8);
-    }
     {
       float b[GT::RI][8], lam[8];
       pgt.prefix(tid, sTot, b, lam);
