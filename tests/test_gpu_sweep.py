@@ -12,6 +12,10 @@ on one MI355X), and GLA_SWEEP_SEED to draw another sample.
 A second sweep (test_random_strong_windows, GLA_SWEEP_WINDOWS cases, 10 by default) puts strongly
 decaying stretches at random places into shapes with at least 256 units of 4 or more chunks, where
 the flagged units are cut into pieces (the re-split) or, beyond the slots, run whole.
+
+A third (test_random_configuration_states_first, GLA_SWEEP_SF cases, 24 by default) draws from the
+same distribution and runs the order with the incoming states first: state passes that stop where
+the decay ends, the scans, and the local passes from the true incoming states.
 """
 import os
 
@@ -20,7 +24,8 @@ import pytest
 import torch
 
 from sequence_state_scan_amd import gla, inputs
-from test_gpu_parity import SUPPORTED, TOL, FWD_KEYS, BWD_KEYS, check, dev, gpu_pipeline, oracle_pipeline, run_case
+from test_gpu_parity import (SF_BWD_KEYS, SF_FWD_KEYS, SUPPORTED, TOL, FWD_KEYS, BWD_KEYS, check, dev, gpu_pipeline,
+                             oracle_pipeline, reach_clamped, run_case, states_first_pipeline)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +101,27 @@ def test_random_strong_windows(case):
     ref = oracle_pipeline(d, chunk, P, True, None if h0 is None else h0.numpy(), None if dhT is None else dhT.numpy())
     check(gpu, ref, FWD_KEYS + BWD_KEYS, TOL[dtype], "windows %s B%d H%d T%d dk%d dv%d C%d P%d" %
           (dtype, B, H, T, dk, dv, chunk, P))
+
+
+def _sf_runs(case):
+    """bf16 chunk 16 has no state-pass kernel of its own: its state passes run in 32- or 64-token
+    chunks, so the segments must hold whole ones."""
+    B, H, T, dk, dv, chunk, P, K, dtype, gate, seed, carry = case
+    return not (dtype == "bf16" and chunk == 16 and (T // P) % 32)
+
+
+@pytest.mark.parametrize("case", [c for c in _cases(int(os.environ.get("GLA_SWEEP_SF", "24")), SEED + 2)
+                                  if _sf_runs(c)])
+def test_random_configuration_states_first(case):
+    B, H, T, dk, dv, chunk, P, K, dtype, gate, seed, carry = case
+    d = inputs.generate(B, H, T, dk, dv, dtype, seed, True, gate)
+    h0 = dhT = None
+    if carry:
+        rng = np.random.default_rng(seed + 100)
+        h0 = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+        dhT = torch.from_numpy(rng.standard_normal((B, H, dk, dv)).astype(np.float32) * 0.3)
+    gpu = states_first_pipeline(dev(d), chunk, P, K, None if h0 is None else h0.cuda(),
+                                None if dhT is None else dhT.cuda())
+    ref = oracle_pipeline(d, chunk, P, True, None if h0 is None else h0.numpy(), None if dhT is None else dhT.numpy())
+    check(reach_clamped(gpu), reach_clamped(ref), SF_FWD_KEYS + SF_BWD_KEYS, TOL[dtype],
+          "states first B%d H%d T%d dk%d dv%d C%d P%d K%d %s %s" % (B, H, T, dk, dv, chunk, P, K, dtype, gate))
