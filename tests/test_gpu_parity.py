@@ -157,6 +157,29 @@ def test_fwdbwd_workload_h16():
     say("%s: %.1fs" % (w.name, time.time() - t))
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32_t256_p4", "fwd_b2h4_t16k_p1", "fwd_h4_t32k_p8", "fwdbwd_h16_t16k_p4"])
+def test_workloads_in_the_states_first_order(name):
+    """The smaller workloads at full size through the states-first chain the benchmark times
+    (gla.states_first_forward / _backward, segments cut to fill the chip), against the oracle's
+    plain recurrence over every token: o and h_final, and with the backward dq, dk, dv, dg and dh0
+    (the backward runs on every workload, the forward-only ones included)."""
+    w = inputs.WORKLOADS[name]
+    d = inputs.generate_workload(w, bwd=True)
+    x = dev(d)
+    t = time.time()
+    f = gla.states_first_forward(x["q"], x["k"], x["v"], x["g"], w.chunk, w.P, w.K)
+    b = gla.states_first_backward(x["q"], x["k"], x["v"], x["g"], x["do"], f, w.chunk, w.K)
+    torch.cuda.synchronize()
+    say("%s states first: P' = %d, %.1fs" % (name, f["P"], time.time() - t))
+    gpu = {"o": as_f64(f["o"]), "h_final": as_f64(f["h_final"])}
+    gpu.update({n: as_f64(b[n]) for n in ("dq", "dk", "dv", "dg", "dh0")})
+    a = {n: as_f64(v) for n, v in d.items()}
+    o, hT = oracle.gla_fwd(a["q"], a["k"], a["v"], a["g"])
+    ref = {"o": o, "h_final": hT}
+    ref.update(oracle.gla_bwd(a["q"], a["k"], a["v"], a["g"], a["do"]))
+    check(gpu, ref, ("o", "h_final", "dq", "dk", "dv", "dg", "dh0"), TOL[w.dtype], "%s, states first" % name)
+
+
 # ------------------------------------------------------------------------- stress and edge cases
 
 @pytest.mark.parametrize("gate", ["weak", "zero", "strong", "strong5", "mixed", "scalar"])
