@@ -443,7 +443,7 @@ def main():
                          % COPY_CALIBRATION_BYTES)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs every segment on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs every segment on a single MI355X and has no "
               "multi-GPU path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
